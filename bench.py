@@ -1,0 +1,266 @@
+"""Benchmark of the Hybrid HiSparse sparse-MLA decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the indexer sweep + top-K select
+(hisparse_index_topk), the fused resolver with its host-to-device miss copies
+(hisparse_resolve), and sparse MLA decode attention for every layer sharing the top-K
+(sparse_mla_decode).  Inputs are synthetic and seeded; every per-step input (queries, context
+lengths) is staged in HBM before the timed region; the KV pool, indexer keys, block tables
+and the pinned host pool are filled up front.
+
+Default workload: 64 requests at 131,072-token context, MTP3 verification (4 query tokens per
+request resolved together), FP8 rows and keys, newest 10 % of pages resident, the rest in the
+pinned host pool, hot buffer (3 + 2) x 2,048 rows per request.
+
+Prints one JSON line.  `value` is layer-steps/s (one layer-step = one sparse-MLA layer's decode
+for the whole batch, including its share of index + resolve).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-MLA decode layer-steps/s + achieved HBM GB/s (indexer+gather) at 128K ctx"
+HBM_PEAK_GBPS = 8000.0
+BF16_DENSE_TFLOPS = 2500.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=16)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload index (3 = the 128K metric config)")
+    ap.add_argument("--scale", type=int, default=1, help="divide context lengths (development only)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-requests", type=int, default=4)
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(see DESIGN.md, 'More than one GPU'); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    from sparse_mla_attention_score_amd import accounting as acc
+    from sparse_mla_attention_score_amd import hisparse as hsb
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    total_steps = args.warmup + args.steps
+    wl = synth.config(args.config, scale=args.scale, steps=total_steps)
+    lay = synth.make_layout(wl)
+    B, S, K, NL = wl.batch, wl.queries, wl.topk, wl.n_layers
+    log(f"workload {wl.name}: B={B} S={S} ctx={wl.ctx[0]} layers={NL} gpu_blocks={lay.num_gpu_blocks} "
+        f"host_blocks={lay.num_host_blocks} idx_blocks={lay.num_idx_blocks}")
+
+    t0 = time.time()
+    cfg = hsb.make_config(topk=K, kv_dtype=wl.kv_dtype, idx_dtype=wl.idx_dtype, n_layers=NL,
+                          max_batch=B, max_queries=S, max_pages_per_req=wl.max_pages,
+                          hot_rows_per_req=wl.hot_rows, num_gpu_blocks=lay.num_gpu_blocks,
+                          num_idx_blocks=lay.num_idx_blocks, num_host_blocks=lay.num_host_blocks)
+    ctx = hsb.Context(cfg, dev)
+    stage = np.zeros(lay.num_idx_blocks * wl.idx_block_bytes, np.uint8)
+    synth.fill_idx_pool(wl, lay, stage)
+    ctx.idx_pool.copy_(torch.from_numpy(stage))
+    del stage
+    stage = np.zeros(NL * lay.num_gpu_blocks * 64 * wl.row_bytes, np.uint8)
+    synth.fill_kv(wl, lay, stage, ctx.host_pool)
+    ctx.kv_pool.copy_(torch.from_numpy(stage))
+    del stage
+    for name in ("idx_block_table", "block_table", "host_block_table", "hot_blocks"):
+        getattr(ctx, name).copy_(torch.from_numpy(np.ascontiguousarray(getattr(lay, name))))
+    chains = [synth.qidx(wl, b, total_steps * S) for b in range(B)]
+    w = torch.from_numpy(synth.head_weights(wl)).to(dev)
+    qidx_d, q_d, lens_d = [], [], []
+    for step in range(total_steps):
+        qidx_d.append(torch.from_numpy(synth.qidx_step(wl, step, chains).view(np.int16)).to(dev))
+        q_d.append(torch.from_numpy(synth.mla_q(wl, step).view(np.int16)).to(dev))
+        lens_d.append(torch.from_numpy(wl.ctx_at(step).astype(np.int32)).to(dev))
+    topk = torch.empty((B, S, K), dtype=torch.int32, device=dev)
+    rows = torch.empty_like(topk)
+    stats = torch.empty((B, 4), dtype=torch.int32, device=dev)
+    out = torch.empty((B, S, 64, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, S, 64), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(576.0)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t0:.1f} s")
+
+    stream = torch.cuda.current_stream()
+
+    def run_step(step, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ctx.index_topk(qidx_d[step].view(torch.bfloat16), w, lens_d[step], topk)
+        if ev is not None:
+            ev[1].record(stream)
+        ctx.resolve(topk, lens_d[step], rows, stats)
+        if ev is not None:
+            ev[2].record(stream)
+        for layer in range(NL):
+            ctx.decode(layer, q_d[step].view(torch.bfloat16), rows, lens_d[step], scale, out, lse)
+        if ev is not None:
+            ev[3].record(stream)
+
+    misses_warm = []
+    for step in range(args.warmup):
+        run_step(step)
+        torch.cuda.synchronize()
+        misses_warm.append(int(stats[:, 2].sum()))
+    err = ctx.device_error()
+    if err:
+        log(f"device error word after warmup: {err:#x}")
+        return 1
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    misses = []
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_host = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        run_step(args.warmup + i, events[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host
+    elapsed_ms = start.elapsed_time(end)
+    err = ctx.device_error()
+    if err:
+        log(f"device error word after timed steps: {err:#x}")
+        return 1
+    # per-call durations (ms), averaged over the timed steps
+    t_idx = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    t_res = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    t_dec = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    # misses of the timed steps (stats of the last step only are resident; rerun is not needed:
+    # count misses per step with a second identical pass is avoided, report the last step)
+    last_miss = int(stats[:, 2].sum())
+
+    ms_per_step = elapsed_ms / args.steps
+    layer_steps_per_s = args.steps * NL / (elapsed_ms / 1e3)
+    # algorithmic work of the timed steps
+    idx_b = gat_b = att_f = 0
+    for i in range(args.steps):
+        wk = acc.step_work(wl.ctx_at(args.warmup + i), S, K, NL, wl.kv_dtype, wl.idx_dtype)
+        idx_b += wk["indexer_bytes"]
+        gat_b += wk["gather_bytes"]
+        att_f += wk["attention_flops"]
+    idx_b /= args.steps
+    gat_b /= args.steps
+    att_f /= args.steps
+    idx_gbps = idx_b / (t_idx * 1e-3) / 1e9
+    gat_gbps = gat_b / (t_dec * 1e-3) / 1e9
+    both_gbps = (idx_b + gat_b) / ((t_idx + t_dec) * 1e-3) / 1e9
+    mfma_util = att_f / (t_dec * 1e-3) / (BF16_DENSE_TFLOPS * 1e12)
+    host_gbps = last_miss * NL * wl.row_bytes / (t_res * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, chains, args.cpu_sample_requests)
+
+    splits = hsb.hs_decode_splits(ctx.ctx, B, S)
+    line = {
+        "metric": METRIC,
+        "value": round(layer_steps_per_s, 3),
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; FP8 E4M3 rows and keys, bf16 queries)",
+        "config": {"workload": wl.name, "batch": B, "queries_per_request": S,
+                   "ctx": int(wl.ctx[0]), "topk": K, "layers": NL, "hot_rows": wl.hot_rows,
+                   "resident_fraction": wl.residency[0][1], "scale": args.scale,
+                   "decode_splits": splits},
+        "hbm_gbps_indexer_gather": round(both_gbps, 1),
+        "stages_ms": {"index_topk": round(t_idx, 4), "resolve": round(t_res, 4),
+                      "sparse_mla_decode": round(t_dec, 4)},
+        "indexer": {"algorithmic_bytes": int(idx_b), "gbps": round(idx_gbps, 1),
+                    "frac_hbm_peak": round(idx_gbps / HBM_PEAK_GBPS, 4)},
+        "gather": {"algorithmic_bytes": int(gat_b), "gbps": round(gat_gbps, 1),
+                   "frac_hbm_peak": round(gat_gbps / HBM_PEAK_GBPS, 4)},
+        "attention": {"algorithmic_flops": int(att_f), "tflops": round(att_f / (t_dec * 1e-3) / 1e12, 2),
+                      "mfma_util_bf16_dense": round(mfma_util, 4)},
+        "host_link": {"misses_last_step": last_miss, "misses_warmup_steps": misses_warm,
+                      "gbps": round(host_gbps, 2)},
+        "roofline": {"kernel": "hisparse_index_topk (score sweep + top-K select)",
+                     "bound": "hbm", "achieved": round(idx_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(idx_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "host_wall_s": round(t_host, 4),
+    }
+    print(json.dumps(line), flush=True)
+    ctx.close()
+    return 0
+
+
+def cpu_baseline(wl, chains, n_req: int):
+    """The oracle, as it stands, on a bounded sample of the same workload: the first
+    `n_req` requests of the first decode step (cold hot buffer), all stages.  Scaled to
+    layer-steps/s of the full batch."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    import synth
+
+    S, K = wl.queries, wl.topk
+    w = synth.head_weights(wl)
+    q = synth.mla_q(wl, 0, batches=range(n_req))
+    lay = synth.make_layout(wl)
+    lens = wl.ctx_at(0)
+    scale = 1.0 / math.sqrt(576.0)
+    t_total = 0.0
+    for b in range(n_req):
+        L = int(lens[b])
+        codes, sc = synth.idx_tokens(wl, b, 0, L)
+        qidx = np.stack(chains[b][:S])
+        t = time.perf_counter()
+        keys = oracle.dequant_idx_keys(codes, sc)
+        scores = oracle.indexer_scores(qidx, w[b], keys)
+        tk = np.stack([oracle.topk_select(s, K) for s in scores])
+        st = oracle.HotState.cold(wl.hot_rows, wl.max_pages * 64)
+        oracle.resolve(tk, lay.block_table[b], lay.host_block_table[b], lay.hot_blocks[b], st)
+        t_total += time.perf_counter() - t
+        for layer in range(wl.n_layers):
+            for j in range(S):
+                toks = tk[j][tk[j] >= 0]
+                rows = synth.latent_tokens(wl, b, layer, toks)      # input fetch, not timed
+                t = time.perf_counter()
+                lat = oracle.decode_latent_rows(rows, wl.kv_dtype)
+                oracle.attention(q[b, j], lat, scale)
+                t_total += time.perf_counter() - t
+    per_step_s = t_total / n_req * wl.batch
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": round(wl.n_layers / per_step_s, 6), "unit": "layer-steps/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n_req} of {wl.batch} requests, decode step 0 (cold hot buffer), all stages; "
+                      f"{t_total:.1f} s of oracle time scaled by {wl.batch}/{n_req}"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,227 @@
+/*
+ * hisparse.h -- C ABI of the Hybrid HiSparse sparse-MLA decode step on MI355X (gfx950).
+ *
+ * One decode step of sparse MLA with the KV of old pages offloaded to pinned host memory:
+ *
+ *   hisparse_index_topk  the indexer scores every earlier token of each request and keeps
+ *                        the top-K (2,048) of them.  GLM-5.3 part-2 page, "Why not TP or
+ *                        DP?" (the indexer scores every earlier token and picks the 2,048
+ *                        that sparse MLA attends to); Hybrid HiSparse part-1 page, "Using
+ *                        sparsity when it is needed" (the indexer picks the top-K tokens,
+ *                        indexer keys stay on the GPU).
+ *   hisparse_resolve     the fused top-K resolver: each selected token is read in place
+ *                        when its page is GPU-resident, read from the hot buffer (and its
+ *                        LRU entry refreshed) when it is hot, or copied as a single row from
+ *                        pinned host memory into an LRU victim slot when it is a miss.  It
+ *                        emits row ids into one shared paged KV tensor, gathered with one
+ *                        stride.  Part-1 page, "How it works" (hybrid residency bullet; the
+ *                        paragraph on hot-buffer pages leased from the shared pool).
+ *   sparse_mla_decode    sparse MLA decode attention (MQA form): all 64 heads share one
+ *                        576-dim latent row (512 "nope" + 64 rope) as key, and its first 512
+ *                        dims as value.  Part-2 page, "Try it" (the sparse-MLA MQA kernel)
+ *                        and footnote 1 (656-byte FP8 rows, QK over 576 dims, PV over 512).
+ *
+ * Conventions shared by every call:
+ *   - Status codes are returned; nothing throws across the ABI.  hs_last_error() gives a
+ *     human-readable reason for the last failing call on the calling thread.
+ *   - Arguments are checked on the host without synchronising.  Faults only the device can
+ *     see (a placeholder page without a host copy, a block or row id out of range, a
+ *     context shorter than its query count) set a sticky device error word, read with
+ *     hs_read_device_error() outside the hot loop; the offending item is skipped.
+ *   - Device buffers are borrowed: the caller allocates them (e.g. with PyTorch) and keeps
+ *     them alive while bound.  The library owns only the context and the pinned host pool.
+ *   - The three step calls allocate nothing, never synchronise and take every per-step
+ *     value from device memory or by value, so a sequence of them can be captured into a
+ *     HIP graph and replayed (part-1 page, "How it works": nothing on the decode path waits
+ *     for a CPU decision).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  All work of a call is enqueued
+ *     on it, in order.
+ *   - Block size is 64 tokens; row id = block * 64 + offset.  Shapes of the kernels are fixed:
+ *     32 indexer heads x 128 dims, 64 MLA heads, d_qk = 576, d_v = 512, 1 <= S <= 4 queries.
+ */
+#ifndef HISPARSE_H
+#define HISPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HS_OK = 0,
+  HS_ERR_INVALID_ARG = -1,  /* a null pointer, a size out of range, an unbound context */
+  HS_ERR_UNSUPPORTED = -2,  /* a shape the kernels are not built for */
+  HS_ERR_OUT_OF_MEMORY = -3,/* pinned host pool allocation failed */
+  HS_ERR_HIP = -4,          /* a HIP runtime call failed (launch, device query) */
+  HS_ERR_STATE = -5         /* call order violated (e.g. bind before host pool) */
+} hs_status;
+
+typedef enum { HS_BF16 = 0, HS_FP8_E4M3 = 1 } hs_dtype;
+
+/* Device error word bits (hs_read_device_error). */
+#define HS_DEVERR_NO_HOST_COPY   0x1  /* selected token on a placeholder page with no host block */
+#define HS_DEVERR_BAD_BLOCK      0x2  /* block id outside its pool */
+#define HS_DEVERR_BAD_ROW        0x4  /* row id outside the KV pool, or a token >= context */
+#define HS_DEVERR_SHORT_CONTEXT  0x8  /* context < number of queries, or > max pages */
+#define HS_DEVERR_TOPK_COUNT     0x10 /* internal: selection did not produce min(K, L) tokens */
+#define HS_DEVERR_HOT_FULL       0x20 /* more misses than untouched hot slots */
+
+/*
+ * Static configuration.  Fixed kernel shapes must be given as listed; the rest size the
+ * pools.  FP8 rows are 656 bytes: bytes [0,512) OCP E4M3 "nope" codes, [512,640) 64 bf16
+ * rope values, [640,644) the fp32 scale of the nope codes, [644,656) zero (the pages give
+ * only the 656-byte size).  bf16 rows are 576 bf16 values (1,152 bytes).  FP8 indexer
+ * blocks hold 64 x 128 E4M3 codes then 64 fp32 scales (8,448 bytes, i.e. 132 bytes per
+ * token); bf16 indexer blocks hold 64 x 128 bf16 (16,384 bytes).
+ */
+typedef struct hs_config {
+  int32_t block_size;        /* must be 64 */
+  int32_t topk;              /* K, 1..2048 (2,048 on the pages) */
+  int32_t n_idx_heads;       /* must be 32 */
+  int32_t idx_dim;           /* must be 128 */
+  int32_t n_heads;           /* must be 64 */
+  int32_t d_qk;              /* must be 576 */
+  int32_t d_v;               /* must be 512 */
+  int32_t kv_dtype;          /* hs_dtype of latent rows */
+  int32_t idx_dtype;         /* hs_dtype of indexer keys */
+  int32_t n_layers;          /* sparse-MLA layers sharing one top-K (IndexShare), 1..16 */
+  int32_t max_batch;         /* B upper bound, >= 1 */
+  int32_t max_queries;       /* S upper bound, 1..4 (S = 1 + speculative tokens) */
+  int32_t max_pages_per_req; /* block-table width; context <= 64 * this */
+  int32_t hot_rows_per_req;  /* 0 => (max_queries + 1) * topk rounded up to 64, i.e.
+                                2 x top-K without MTP and (spec + 2) x top-K with MTP
+                                (part-1 page: default hot buffer, and the MTP note under the
+                                concurrency calculator).  Must be a multiple of 64, at least
+                                max_queries * topk and at most 16384. */
+  int32_t topk_lds_candidates; /* 0 => default; otherwise caps the on-chip candidate list of
+                                  the top-K select (a smaller cap exercises the multi-pass
+                                  path; results are identical) */
+  int32_t reserved;
+  int64_t num_gpu_blocks;    /* blocks of the shared KV pool (resident pages + hot pages) */
+  int64_t num_idx_blocks;    /* blocks of the indexer key pool */
+  int64_t num_host_blocks;   /* blocks of the pinned host pool */
+} hs_config;
+
+/* Device buffers, all borrowed, all on the context's device. */
+typedef struct hs_buffers {
+  void* kv_pool;                   /* [n_layers][num_gpu_blocks][64][row bytes] */
+  const void* idx_pool;            /* [num_idx_blocks][indexer block bytes] */
+  const int32_t* idx_block_table;  /* [max_batch][max_pages_per_req] indexer block per page */
+  const int32_t* block_table;      /* [max_batch][max_pages_per_req] GPU block, or -1 for a
+                                      placeholder whose rows live only in host memory */
+  const int32_t* host_block_table; /* [max_batch][max_pages_per_req] host block or -1 */
+  const int32_t* hot_blocks;       /* [max_batch][hot_rows/64] GPU blocks leased as hot pages */
+  void* workspace;                 /* hs_workspace_bytes() bytes, 256-byte aligned */
+} hs_buffers;
+
+typedef struct hs_ctx hs_ctx;
+
+/* Validate `cfg` and create a context on the current HIP device.  No device work. */
+hs_status hs_create(const hs_config* cfg, hs_ctx** out);
+
+/* Free the pinned host pool and the context.  Bound buffers are not touched. */
+hs_status hs_destroy(hs_ctx* ctx);
+
+/* Device workspace needed by a context with this configuration: hot-buffer state
+ * (slot tokens, LRU stamps and order, token-to-slot map, per-request step counters),
+ * top-K scratch, split-K partials and the device error word. */
+hs_status hs_workspace_bytes(const hs_config* cfg, size_t* dev_bytes);
+
+/* Bytes of the pinned host pool: n_layers * num_host_blocks * 64 * row bytes. */
+hs_status hs_host_pool_bytes(const hs_config* cfg, size_t* host_bytes);
+
+/* Allocate the pinned, device-mapped host pool (library-owned; freed by hs_destroy) and
+ * return its host address.  Layout [n_layers][num_host_blocks][64][row bytes].  The caller
+ * writes host copies of placeholder pages through it.  The pool is sized in whole host
+ * blocks (part-1 page, reproduction appendix: the host pool is rounded up to whole host
+ * blocks).  Calling it twice returns HS_ERR_STATE. */
+hs_status hs_host_pool_alloc(hs_ctx* ctx, void** host_base);
+
+/* Bind borrowed device buffers.  Requires the host pool when num_host_blocks > 0.
+ * Re-binding replaces the previous set (the hot state must then be reset). */
+hs_status hs_bind(hs_ctx* ctx, const hs_buffers* bufs);
+
+/* Reset the hot buffer of every request to cold (all slots empty, LRU clock 0), clear
+ * the top-K scratch and the device error word.  Enqueued on `stream`. */
+hs_status hs_hot_reset(hs_ctx* ctx, void* stream);
+
+/*
+ * Indexer sweep + top-K select for B requests of S query tokens each.
+ *   q_idx     device [B][S][32][128] bf16 indexer queries
+ *   w         device [B][S][32] fp32 non-negative head weights
+ *   ctx_lens  device [B] int32: rows present per request, including the S query tokens'
+ *             own rows (the last S).  Query j of request b sees rows t < L_b - S + 1 + j.
+ *   topk_out  device [B][S][topk] int32: for each query the min(K, L) tokens with the
+ *             largest score s(t) = sum_h w_h * max(0, q_h . k_t), ties to the lower token
+ *             index, written in ascending token order and padded with -1.
+ * The score formula is not printed on the pages; this is the reading the library takes.
+ */
+hs_status hisparse_index_topk(hs_ctx* ctx, const void* q_idx, const float* w,
+                              const int32_t* ctx_lens, int32_t B, int32_t S, int32_t* topk_out,
+                              void* stream);
+
+/*
+ * Fused top-K resolver for B requests (one call per decode step; the S lists of a request
+ * are resolved together, as MTP verification needs).  Per request, over the sorted union U
+ * of its S top-K lists:
+ *   - a token whose page is GPU-resident (block_table >= 0) gets row block*64 + offset and
+ *     does not touch the LRU;
+ *   - a token already in the hot buffer gets its slot's row, and the slot's LRU stamp is
+ *     set to the request's step counter;
+ *   - the remaining tokens (misses), in ascending token order, take the slots not touched
+ *     in this call in least-recently-used order (empty slots first, ties to the lower slot);
+ *     each copies its single row, for all n_layers layers, from the pinned host pool (host
+ *     block from host_block_table) into that slot's row of the shared KV pool.  The copy is
+ *     issued by the GPU; no CPU is involved.
+ *   row_ids_out  device [B][S][topk] int32 rows into the shared KV pool, -1 where topk is -1
+ *   stats_out    device [B][4] int32 (resident, hit, miss, hot pages in use) or NULL
+ * The request's step counter then advances by one.  row_ids stays valid for
+ * sparse_mla_decode until the next resolve of that request.
+ */
+hs_status hisparse_resolve(hs_ctx* ctx, const int32_t* topk, const int32_t* ctx_lens, int32_t B,
+                           int32_t S, int32_t* row_ids_out, int32_t* stats_out, void* stream);
+
+/*
+ * Sparse MLA decode attention of layer `layer` for B x S queries:
+ *   out[b][j][h] = sum_k softmax_k(sm_scale * q[b][j][h] . latent(row_k)) * latent(row_k)[0:512]
+ * over the rows row_ids[b][j][0 .. min(K, L_bj)).
+ *   q        device [B][S][64][576] bf16
+ *   row_ids  device [B][S][topk] int32 (from hisparse_resolve)
+ *   ctx_lens device [B] int32 (as above)
+ *   out      device [B][S][64][512] bf16
+ *   lse      device [B][S][64] fp32 natural-log sum-exp of the scaled logits, or NULL
+ */
+hs_status sparse_mla_decode(hs_ctx* ctx, int32_t layer, const void* q, const int32_t* row_ids,
+                            const int32_t* ctx_lens, int32_t B, int32_t S, float sm_scale,
+                            void* out, float* lse, void* stream);
+
+/* Synchronise the context's device and read (then clear) the device error word. */
+hs_status hs_read_device_error(hs_ctx* ctx, int32_t* code);
+
+/* Device addresses of the hot-buffer state inside the bound workspace, for inspection (the
+ * LRU state is part of what a resolve call produces).  Read-only for callers. */
+typedef struct hs_hot_state_ptrs {
+  const int32_t* slot_token;  /* [max_batch][hot_rows] token in each hot slot, -1 empty */
+  const int32_t* slot_stamp;  /* [max_batch][hot_rows] LRU stamp, -1 never used */
+  const int32_t* tok2slot;    /* [max_batch][tokens_per_req] hot slot of each token, -1 absent */
+  const int32_t* req_step;    /* [max_batch] resolve calls made */
+  int32_t hot_rows;
+  int32_t reserved;
+  int64_t tokens_per_req;     /* max_pages_per_req * 64 */
+} hs_hot_state_ptrs;
+
+hs_status hs_hot_state(const hs_ctx* ctx, hs_hot_state_ptrs* out);
+
+/* Number of split-K partitions sparse_mla_decode uses for a (B, S) batch. */
+hs_status hs_decode_splits(const hs_ctx* ctx, int32_t B, int32_t S, int32_t* splits);
+
+const char* hs_status_string(hs_status status);
+const char* hs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HISPARSE_H */

@@ -1,0 +1,389 @@
+// Indexer score sweep and top-K select (gfx950).
+//
+// What is computed (GLM-5.3 part-2 page, "Why not TP or DP?": the indexer scores every
+// earlier token and keeps the 2,048 that sparse MLA attends to; part-1 page, "Using sparsity
+// when it is needed": indexer keys stay GPU-resident).  The score formula is not printed on
+// the pages; the reading taken is
+//     s_j(t) = sum_h w[j][h] * max(0, q[j][h] . k[t]),   32 heads x 128 dims,
+// and the selection is the min(K, L_j) tokens ranked by (score desc, token asc), emitted in
+// ascending token order.
+//
+// Sweep: one workgroup scores 32 pages (2,048 tokens) of one request for all S queries.  The
+// contraction [S*32 heads x 128] x [128 x tokens] runs on bf16 MFMA (32x32x16): FP8 keys are
+// converted to bf16 exactly, the per-token fp32 scale is applied after the ReLU (positive
+// scales commute with it).  Each wave streams a page: lane l reads 64 contiguous key bytes
+// of token l%32 (dims 64*(l/32) .. +64); the 128 dims are assigned to MFMA k-slots in that
+// order, and the queries held in registers use the same assignment.  Scores go to a
+// per-(request, query) scratch row; their first radix digit (bits [30:19]) is counted in LDS
+// and added to a global histogram.
+//
+// Select: one workgroup per (request, query).  The histogram gives the threshold bin; one
+// pass over the scores marks the tokens above it in a bitmap (wave ballots) and collects the
+// bin's tokens on chip, where a bitonic sort by (score desc, token asc) picks the rest.  If
+// the bin is too large for the chip, a general radix refinement over the remaining bits and
+// an index-ordered pass for exact ties does the same.  The bitmap is then emitted in order.
+#include "hs_device.h"
+#include "hs_internal.h"
+
+namespace hs {
+namespace {
+
+template <int S, bool kFp8>
+__global__ __launch_bounds__(256) void index_score_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const int32_t* __restrict__ ctx_lens, const uint8_t* __restrict__ idx_pool,
+    const int32_t* __restrict__ idx_block_table, int max_pages, int64_t num_idx_blocks, int B,
+    float* __restrict__ scores, int64_t lmax, uint32_t* __restrict__ hist,
+    int32_t* __restrict__ err) {
+  constexpr int kBlkBytes = kFp8 ? kIdxFp8Block : kIdxBf16Block;
+  // 16-bit LDS counters, two bins per word: one workgroup sees at most 2,048 tokens.
+  __shared__ uint32_t lhist[S][kHistBins / 2];
+
+  const int b = blockIdx.x % B;
+  const int item = blockIdx.x / B;
+  const int L = ctx_lens[b];
+  if (L < S || L > max_pages * kBlock) {
+    if (item == 0 && threadIdx.x == 0) raise_error(err, HS_DEVERR_SHORT_CONTEXT);
+    return;
+  }
+  const int n_pages = (L + kBlock - 1) / kBlock;
+  const int p_begin = item * kPagesPerItem;
+  if (p_begin >= n_pages) return;
+  const int p_end = min(n_pages, p_begin + kPagesPerItem);
+
+  for (int i = threadIdx.x; i < S * kHistBins / 2; i += 256) (&lhist[0][0])[i] = 0;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, col = lane & 31;
+
+  // A operand: Q[j][head = col][dims 64*half + 8*s .. +8] for k-step s.
+  bf16x8 qa[S][8];
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    const uint16_t* qp = q_idx + ((int64_t)(b * S + j) * kIdxHeads + col) * kIdxDim + 64 * half;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qa[j][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 8 * s));
+  }
+  // Weights of the 16 head rows this lane's accumulator holds.
+  float wr[S][16];
+#pragma unroll
+  for (int j = 0; j < S; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wr[j][i] = w[(b * S + j) * kIdxHeads + 8 * (i / 4) + 4 * half + (i % 4)];
+  __syncthreads();
+
+  for (int p = p_begin + wave; p < p_end; p += 4) {
+    const int blk = idx_block_table[(int64_t)b * max_pages + p];
+    if (blk < 0 || blk >= num_idx_blocks) {
+      if (lane == 0) raise_error(err, HS_DEVERR_BAD_BLOCK);
+      continue;
+    }
+    const uint8_t* base = idx_pool + (int64_t)blk * kBlkBytes;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int o = tt * 32 + col;
+      const int t = p * kBlock + o;
+      bf16x8 kb[8];
+      float scale = 1.0f;
+      if constexpr (kFp8) {
+        const u32x4* kp = reinterpret_cast<const u32x4*>(base + o * 128 + 64 * half);
+        u32x4 raw[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) raw[v] = kp[v];
+        scale = *reinterpret_cast<const float*>(base + 8192 + o * 4);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          kb[s] = e4m3x8_to_bf16(raw[s / 2][(s % 2) * 2], raw[s / 2][(s % 2) * 2 + 1]);
+      } else {
+        const u32x4* kp = reinterpret_cast<const u32x4*>(base + o * 256 + 128 * half);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) kb[s] = as_bf16x8(kp[s]);
+      }
+#pragma unroll
+      for (int j = 0; j < S; ++j) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) acc = mfma32x32x16(qa[j][s], kb[s], acc);
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) part += wr[j][i] * fmaxf(acc[i], 0.0f);
+        // add the other half's 16 heads of the same token (lane l ^ 32)
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
+                                                   false, false);
+        const float total = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * scale;
+        // scores are >= 0: clearing the sign bit maps -0 to +0
+        const uint32_t bits = __float_as_uint(total) & 0x7fffffffu;
+        if (half == 0 && t < L - S + 1 + j) {
+          scores[(int64_t)(b * S + j) * lmax + t] = __uint_as_float(bits);
+          const uint32_t bin = bits >> kHistShift;
+          atomicAdd(&lhist[j][bin >> 1], 1u << (16 * (bin & 1)));
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < S * kHistBins / 2; i += 256) {
+    const uint32_t v = (&lhist[0][0])[i];
+    if (v == 0) continue;
+    const int j = i / (kHistBins / 2), pair = i % (kHistBins / 2);
+    uint32_t* g = hist + (int64_t)(b * S + j) * kHistBins + 2 * pair;
+    if (v & 0xffffu) atomicAdd(g, v & 0xffffu);
+    if (v >> 16) atomicAdd(g + 1, v >> 16);
+  }
+}
+
+constexpr int kSelThreads = 1024;
+
+struct SelectShared {
+  uint32_t hist[kHistBins];
+  int scan[kSelThreads / 64 + 1];
+  int misc[8];
+};
+
+// Bin (of `nbins`) holding the K-th largest element given per-bin counts in sh.hist, counted
+// from the top.  Returns the bin; *above = number of elements in higher bins.
+__device__ int find_threshold_bin(SelectShared& sh, int nbins, int need, int* above) {
+  const int per = nbins / kSelThreads > 0 ? nbins / kSelThreads : 1;
+  const int tid = threadIdx.x;
+  // thread tid owns bins [nbins - per*(tid+1), nbins - per*tid) (highest bins first)
+  int local = 0;
+  const int hi = nbins - per * tid, lo = hi - per;
+  if (lo >= 0)
+    for (int bin = lo; bin < hi; ++bin) local += sh.hist[bin];
+  int total;
+  const int before = block_exclusive_scan<kSelThreads>(local, sh.scan, &total);  // count above `hi`
+  if (threadIdx.x == 0) {
+    sh.misc[0] = -1;
+    sh.misc[1] = 0;
+  }
+  __syncthreads();
+  if (lo >= 0 && before < need && before + local >= need) {
+    int acc = before;
+    for (int bin = hi - 1; bin >= lo; --bin) {
+      if (acc + (int)sh.hist[bin] >= need) {
+        sh.misc[0] = bin;
+        sh.misc[1] = acc;
+        break;
+      }
+      acc += sh.hist[bin];
+    }
+  }
+  __syncthreads();
+  const int bin = sh.misc[0];
+  *above = sh.misc[1];
+  __syncthreads();
+  return bin;
+}
+
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
+    const int32_t* __restrict__ ctx_lens, int B, int S, int K, int max_ctx,
+    const float* __restrict__ scores, int64_t lmax, uint32_t* __restrict__ hist,
+    uint32_t* __restrict__ bitmap, int64_t bm_words, int32_t* __restrict__ topk_out,
+    int cand_cap, int32_t* __restrict__ err) {
+  extern __shared__ __align__(16) unsigned char dyn[];
+  __shared__ SelectShared sh;
+  uint64_t* cand = reinterpret_cast<uint64_t*>(dyn);  // (key << 32) | ~token
+
+  const int bj = blockIdx.x;
+  const int b = bj / S, j = bj % S;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Lb = ctx_lens[b];
+  int32_t* out = topk_out + (int64_t)bj * K;
+  uint32_t* gh = hist + (int64_t)bj * kHistBins;
+  if (Lb < S || Lb > max_ctx) {
+    for (int i = tid; i < kHistBins; i += kSelThreads) gh[i] = 0;
+    for (int i = tid; i < K; i += kSelThreads) out[i] = -1;
+    return;
+  }
+  const int Lj = Lb - S + 1 + j;
+  if (Lj <= K) {  // everything is selected; keep the histogram zero for the next call
+    for (int i = tid; i < kHistBins; i += kSelThreads) gh[i] = 0;
+    for (int i = tid; i < K; i += kSelThreads) out[i] = i < Lj ? i : -1;
+    return;
+  }
+
+  for (int i = tid; i < kHistBins; i += kSelThreads) {
+    sh.hist[i] = gh[i];
+    gh[i] = 0;
+  }
+  __syncthreads();
+  int above;
+  const int beta = find_threshold_bin(sh, kHistBins, K, &above);
+  const int cnt_beta = beta >= 0 ? (int)sh.hist[beta] : 0;
+  const int need = K - above;  // tokens to take from bin beta
+  const float* sc = scores + (int64_t)bj * lmax;
+  // bm_words covers whole 1,024-token chunks, so the last chunk's ballot words stay inside
+  uint32_t* bm = bitmap + (int64_t)bj * bm_words;
+  const int n_chunks = (Lj + kSelThreads - 1) / kSelThreads;
+
+  if (beta >= 0 && cnt_beta <= cand_cap) {
+    // ---- fast path: one pass, bin beta collected on chip
+    if (tid == 0) sh.misc[2] = 0;
+    __syncthreads();
+    for (int c = 0; c < n_chunks; ++c) {
+      const int t = c * kSelThreads + tid;
+      uint32_t key = 0;
+      if (t < Lj) key = __float_as_uint(sc[t]);
+      const int bin = t < Lj ? (int)(key >> kHistShift) : -1;
+      const uint64_t m = __ballot(bin > beta);
+      if (lane == 0) {
+        const int word = (c * kSelThreads + wave * 64) / 32;
+        bm[word] = (uint32_t)m;
+        bm[word + 1] = (uint32_t)(m >> 32);
+      }
+      if (bin == beta) {
+        const int pos = atomicAdd(&sh.misc[2], 1);
+        if (pos < cand_cap) cand[pos] = ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)t);
+      }
+    }
+    __threadfence();  // bitmap words are complete in L2 before the atomics below
+    __syncthreads();
+    const int n = min(sh.misc[2], cand_cap);
+    if (tid == 0 && n != cnt_beta) raise_error(err, HS_DEVERR_TOPK_COUNT);
+    int n2 = 1;
+    while (n2 < n) n2 <<= 1;
+    for (int i = n + tid; i < n2; i += kSelThreads) cand[i] = 0;
+    __syncthreads();
+    // bitonic sort, descending
+    for (int k = 2; k <= n2; k <<= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        for (int i = tid; i < n2; i += kSelThreads) {
+          const int ixj = i ^ jj;
+          if (ixj > i) {
+            const uint64_t a = cand[i], c2 = cand[ixj];
+            const bool desc = (i & k) == 0;
+            if (desc ? (a < c2) : (a > c2)) {
+              cand[i] = c2;
+              cand[ixj] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < need && i < n; i += kSelThreads) {
+      const uint32_t t = ~(uint32_t)(cand[i] & 0xffffffffu);
+      atomicOr(&bm[t >> 5], 1u << (t & 31));
+    }
+  } else {
+    // ---- general path: refine the threshold over the remaining 19 bits, then an ordered
+    // pass that takes the lowest-index ties.
+    uint32_t prefix = (uint32_t)max(beta, 0);
+    int prefix_shift = kHistShift;  // bits above this are fixed by `prefix`
+    int need_left = need;
+    const int digit_bits[2] = {12, 7};
+    for (int d = 0; d < 2; ++d) {
+      const int shift = prefix_shift - digit_bits[d];
+      const int nb = 1 << digit_bits[d];
+      for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
+      __syncthreads();
+      for (int c = 0; c < n_chunks; ++c) {
+        const int t = c * kSelThreads + tid;
+        if (t < Lj) {
+          const uint32_t key = __float_as_uint(sc[t]);
+          if ((key >> prefix_shift) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
+        }
+      }
+      __syncthreads();
+      int ab;
+      const int dig = find_threshold_bin(sh, nb, need_left, &ab);
+      need_left -= ab;
+      prefix = (prefix << digit_bits[d]) | (uint32_t)max(dig, 0);
+      prefix_shift = shift;
+    }
+    const uint32_t T = prefix;  // the K-th largest key; take need_left of the keys equal to it
+    int eq_carry = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+      const int t = c * kSelThreads + tid;
+      uint32_t key = 0;
+      if (t < Lj) key = __float_as_uint(sc[t]);
+      const bool eq = t < Lj && key == T;
+      int eq_total;
+      const int eq_rank = eq_carry + block_exclusive_scan<kSelThreads>(eq ? 1 : 0, sh.scan, &eq_total);
+      eq_carry += eq_total;
+      const bool sel = t < Lj && (key > T || (eq && eq_rank < need_left));
+      const uint64_t m = __ballot(sel);
+      if (lane == 0) {
+        const int word = (c * kSelThreads + wave * 64) / 32;
+        bm[word] = (uint32_t)m;
+        bm[word + 1] = (uint32_t)(m >> 32);
+      }
+    }
+  }
+  __threadfence();
+  __syncthreads();
+
+  // ---- emission in ascending token order
+  const int n_words = (Lj + 31) / 32;
+  const int per = (n_words + kSelThreads - 1) / kSelThreads;
+  const int w0 = tid * per, w1 = min(n_words, w0 + per);
+  int cnt = 0;
+  for (int wd = w0; wd < w1; ++wd) cnt += __popc(load_agent(&bm[wd]));
+  int total;
+  int pos = block_exclusive_scan<kSelThreads>(cnt, sh.scan, &total);
+  for (int wd = w0; wd < w1; ++wd) {
+    uint32_t v = load_agent(&bm[wd]);
+    while (v) {
+      const int bit = __ffs(v) - 1;
+      v &= v - 1;
+      if (pos < K) out[pos] = wd * 32 + bit;
+      ++pos;
+    }
+  }
+  for (int i = total + tid; i < K; i += kSelThreads) out[i] = -1;
+  if (tid == 0 && total != K) raise_error(err, HS_DEVERR_TOPK_COUNT);
+}
+
+template <int S, bool kFp8>
+hipError_t launch_scores(const hs_ctx* ctx, const void* q_idx, const float* w,
+                         const int32_t* ctx_lens, int B, hipStream_t stream) {
+  const hs_config& c = ctx->cfg;
+  const int items = (c.max_pages_per_req + kPagesPerItem - 1) / kPagesPerItem;
+  dim3 grid((unsigned)(B * items)), block(256);
+  hipLaunchKernelGGL((index_score_kernel<S, kFp8>), grid, block, 0, stream,
+                     static_cast<const uint16_t*>(q_idx), w, ctx_lens,
+                     static_cast<const uint8_t*>(ctx->buf.idx_pool), ctx->buf.idx_block_table,
+                     c.max_pages_per_req, (int64_t)c.num_idx_blocks, B, ctx->ws.scores,
+                     ctx->lay.lmax, ctx->ws.hist, ctx->ws.err);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace hs
+
+using namespace hs;
+
+// On-chip candidate capacity of the select: a power of two (the bitonic sort's size).
+int hs_select_cand_cap(const hs_config& c) {
+  int want = c.topk_lds_candidates > 0 ? c.topk_lds_candidates : kDefaultCandCap;
+  if (want > kDefaultCandCap) want = kDefaultCandCap;
+  int cap = 1;
+  while (cap * 2 <= want) cap *= 2;
+  return cap;
+}
+
+hipError_t hs_launch_index_topk(const hs_ctx* ctx, const void* q_idx, const float* w,
+                                const int32_t* ctx_lens, int B, int S, int32_t* topk_out,
+                                hipStream_t stream) {
+  const bool fp8 = ctx->cfg.idx_dtype == HS_FP8_E4M3;
+  hipError_t e;
+  switch (S * 2 + (fp8 ? 1 : 0)) {
+    case 2: e = launch_scores<1, false>(ctx, q_idx, w, ctx_lens, B, stream); break;
+    case 3: e = launch_scores<1, true>(ctx, q_idx, w, ctx_lens, B, stream); break;
+    case 4: e = launch_scores<2, false>(ctx, q_idx, w, ctx_lens, B, stream); break;
+    case 5: e = launch_scores<2, true>(ctx, q_idx, w, ctx_lens, B, stream); break;
+    case 6: e = launch_scores<3, false>(ctx, q_idx, w, ctx_lens, B, stream); break;
+    case 7: e = launch_scores<3, true>(ctx, q_idx, w, ctx_lens, B, stream); break;
+    case 8: e = launch_scores<4, false>(ctx, q_idx, w, ctx_lens, B, stream); break;
+    case 9: e = launch_scores<4, true>(ctx, q_idx, w, ctx_lens, B, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  const int cap = hs_select_cand_cap(ctx->cfg);
+  const size_t dyn = (size_t)cap * sizeof(uint64_t);
+  hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)(B * S)), dim3(kSelThreads), dyn, stream,
+                     ctx_lens, B, S, ctx->cfg.topk, ctx->cfg.max_pages_per_req * kBlock,
+                     ctx->ws.scores, ctx->lay.lmax, ctx->ws.hist, ctx->ws.bitmap,
+                     (int64_t)ctx->lay.bm_words, topk_out, cap, ctx->ws.err);
+  return hipGetLastError();
+}

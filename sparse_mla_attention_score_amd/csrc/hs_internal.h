@@ -1,0 +1,93 @@
+// Internal declarations of the HiSparse decode-step library (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hisparse.h"
+
+namespace hs {
+
+// Fixed shapes of the kernels.
+constexpr int kBlock = 64;             // tokens per page
+constexpr int kIdxHeads = 32;          // indexer heads
+constexpr int kIdxDim = 128;           // indexer head dim
+constexpr int kHeads = 64;             // MLA query heads sharing one latent row
+constexpr int kDqk = 576;              // latent: 512 "nope" + 64 rope
+constexpr int kDv = 512;               // value = first 512 latent dims
+constexpr int kFp8Row = 656;           // FP8 latent row bytes
+constexpr int kBf16Row = 1152;         // bf16 latent row bytes
+constexpr int kIdxFp8Block = 8448;     // 64 x 128 e4m3 + 64 fp32 scales
+constexpr int kIdxBf16Block = 16384;   // 64 x 128 bf16
+constexpr int kMaxTopk = 2048;
+constexpr int kMaxQueries = 4;
+constexpr int kMaxUnion = kMaxTopk * kMaxQueries;
+constexpr int kMaxHot = 16384;
+
+// Top-K radix select: the first digit is score bits [30:19] (8 exponent + 4 mantissa bits of
+// a non-negative fp32), histogrammed by the score sweep itself.
+constexpr int kHistBins = 4096;
+constexpr int kHistShift = 19;
+constexpr int kPagesPerItem = 32;      // pages scored by one sweep workgroup (2,048 tokens)
+constexpr int kDefaultCandCap = 4096;  // on-chip candidates of the threshold bin
+
+// Decode split-K.
+constexpr int kTileRows = 64;
+constexpr int kMaxSplits = 32;
+
+// Pointers into the borrowed device workspace.
+struct Workspace {
+  int32_t* slot_token;   // [Bmax][H]          token held by each hot slot, -1 empty
+  int32_t* slot_stamp;   // [Bmax][H]          LRU stamp (resolve call counter), -1 never
+  int32_t* lru_order;    // [2][Bmax][H]       slots in (stamp, slot) order, double-buffered by
+                         //                    the parity of the request's call counter
+  int32_t* tok2slot;     // [Bmax][Lmax]       hot slot of each token, -1 absent
+  int32_t* req_step;     // [Bmax]             resolve calls made per request
+  int32_t* req_used;     // [Bmax]             hot slots ever filled per request
+  int32_t* err;          // [1]                sticky device error word (HS_DEVERR_*)
+  float* scores;         // [Bmax][Smax][Lmax] indexer scores of one call
+  uint32_t* hist;        // [Bmax][Smax][kHistBins] first-digit histogram (kept zero between calls)
+  uint32_t* bitmap;      // [Bmax][Smax][bm_words] selected-token bitmap
+  float* part_o;         // [Bmax*Smax*splits_cap][64][512] split-K partial outputs
+  float* part_ml;        // [Bmax*Smax*splits_cap][64][2] split-K (max, sum) in log2 units
+};
+
+struct Layout {
+  size_t off_slot_token, off_slot_stamp, off_lru_order, off_tok2slot, off_req_step, off_req_used,
+      off_err, off_scores, off_hist, off_bitmap, off_part_o, off_part_ml, total;
+  int32_t hot_rows;
+  int64_t lmax;       // max_pages_per_req * 64
+  int64_t bm_words;   // bitmap words per (request, query): lmax rounded up to 1,024, / 32
+  int32_t splits_cap;
+};
+
+hs_status compute_layout(const hs_config& c, Layout* out);
+
+}  // namespace hs
+
+struct hs_ctx {
+  hs_config cfg;
+  hs::Layout lay;
+  int device;
+  int row_bytes;
+  int idx_block_bytes;
+  void* host_pool;          // host address (pinned, mapped)
+  void* host_pool_dev;      // device address of the same memory
+  size_t host_pool_bytes;
+  bool bound;
+  hs_buffers buf;
+  hs::Workspace ws;
+};
+
+// Kernel launchers (each enqueues on `stream`, returns hipSuccess or the launch error).
+hipError_t hs_launch_hot_reset(const hs_ctx* ctx, hipStream_t stream);
+hipError_t hs_launch_index_topk(const hs_ctx* ctx, const void* q_idx, const float* w,
+                                const int32_t* ctx_lens, int B, int S, int32_t* topk_out,
+                                hipStream_t stream);
+hipError_t hs_launch_resolve(const hs_ctx* ctx, const int32_t* topk, const int32_t* ctx_lens, int B,
+                             int S, int32_t* row_ids, int32_t* stats, hipStream_t stream);
+hipError_t hs_launch_decode(const hs_ctx* ctx, int layer, const void* q, const int32_t* row_ids,
+                            const int32_t* ctx_lens, int B, int S, float sm_scale, void* out,
+                            float* lse, int splits, hipStream_t stream);
+int hs_choose_splits(const hs_ctx* ctx, int B, int S);
+int hs_select_cand_cap(const hs_config& c);

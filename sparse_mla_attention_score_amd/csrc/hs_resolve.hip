@@ -1,0 +1,402 @@
+// Fused top-K resolver and hot-buffer state (gfx950).
+//
+// What is computed (Hybrid HiSparse part-1 page, "How it works", hybrid residency bullet and
+// the paragraph that follows it): each token selected by the indexer is read where it lives.
+// A token on a GPU-resident page is read in place.  A token in the token-indexed hot buffer
+// is read there and its LRU entry is refreshed.  Any other token is a miss: its single row
+// is copied from pinned host memory into an LRU slot of the hot buffer.  The hot buffer's
+// pages are ordinary blocks of the shared KV pool, so every selected row is named by one row
+// id into one tensor with one stride.  Nothing waits on the CPU.
+//
+// Readings where the pages are silent (the same ones the oracle takes): the LRU clock is the
+// request's resolve-call counter; a hit and a fill both stamp it; resident pages win and do
+// not touch the LRU; victims are the slots untouched in this call in (stamp, slot) order,
+// empty slots first; the i-th miss in ascending token order takes the i-th victim.
+//
+// Implementation: one 1,024-thread workgroup per request.  The S top-K lists are merged into
+// their sorted union on chip (bitonic sort + compaction).  The (stamp, slot) order is kept as
+// an explicit recency list of slots, double-buffered by the parity of the call counter: the
+// victims are the first untouched entries of the old list, and the new list is the untouched
+// entries in old order followed by the touched slots in ascending slot order, which is the
+// (stamp, slot) order after this call.  Every choice is a prefix sum, so the result does not
+// depend on thread timing.  Miss rows are then copied from the mapped host pool by the GPU,
+// 16 bytes per thread, all layers sharing the request's top-K.
+#include "hs_device.h"
+#include "hs_internal.h"
+
+namespace hs {
+namespace {
+
+constexpr int kResThreads = 1024;
+
+__global__ __launch_bounds__(kResThreads) void resolve_kernel(
+    const int32_t* __restrict__ topk, const int32_t* __restrict__ ctx_lens, int S, int K,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ host_block_table,
+    const int32_t* __restrict__ hot_blocks, int max_pages, int H, int64_t num_gpu_blocks,
+    int64_t num_host_blocks, int max_batch, int32_t* __restrict__ slot_token,
+    int32_t* __restrict__ slot_stamp, int32_t* __restrict__ lru_order,
+    int32_t* __restrict__ tok2slot, int64_t lmax, int32_t* __restrict__ req_step,
+    int32_t* __restrict__ req_used, const uint8_t* __restrict__ host_pool,
+    uint8_t* __restrict__ kv_pool, int n_layers, int row_bytes, int union_cap,
+    int32_t* __restrict__ row_ids, int32_t* __restrict__ stats, int32_t* __restrict__ err) {
+  extern __shared__ __align__(16) unsigned char dyn[];
+  // union_cap (power of two >= S*K) entries each: sorted union, per-token row (or miss code),
+  // miss source row, miss destination (victim slot, then its row); then H slot flags.
+  int32_t* U = reinterpret_cast<int32_t*>(dyn);
+  int32_t* cls = U + union_cap;
+  int32_t* msrc = cls + union_cap;
+  int32_t* mdst = msrc + union_cap;
+  uint8_t* flag = reinterpret_cast<uint8_t*>(mdst + union_cap);
+  __shared__ int scan[kResThreads / 64 + 1];
+  __shared__ int cnt[8];
+
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int Lb = ctx_lens[b];
+  const int step = req_step[b];
+  const int32_t* tk = topk + (int64_t)b * S * K;
+  int32_t* out = row_ids + (int64_t)b * S * K;
+  const int32_t* bt = block_table + (int64_t)b * max_pages;
+  const int32_t* hbt = host_block_table + (int64_t)b * max_pages;
+  const int32_t* hot = hot_blocks + (int64_t)b * (H / kBlock);
+  int32_t* st_tok = slot_token + (int64_t)b * H;
+  int32_t* st_stamp = slot_stamp + (int64_t)b * H;
+  int32_t* t2s = tok2slot + (int64_t)b * lmax;
+  const int32_t* order_cur = lru_order + ((int64_t)(step & 1) * max_batch + b) * H;
+  int32_t* order_next = lru_order + ((int64_t)((step + 1) & 1) * max_batch + b) * H;
+
+  if (Lb < S || Lb > max_pages * kBlock) {
+    if (tid == 0) raise_error(err, HS_DEVERR_SHORT_CONTEXT);
+    for (int i = tid; i < S * K; i += kResThreads) out[i] = -1;
+    return;
+  }
+
+  // ---- 1. sorted union of the S lists (tokens outside [0, Lb) are dropped and flagged)
+  const int n_in = S * K;
+  for (int i = tid; i < union_cap; i += kResThreads) {
+    int32_t t = i < n_in ? tk[i] : -1;
+    if (t >= Lb) {
+      raise_error(err, HS_DEVERR_BAD_ROW);
+      t = -1;
+    }
+    U[i] = t < 0 ? INT32_MAX : t;
+  }
+  for (int i = tid; i < H; i += kResThreads) flag[i] = 0;
+  if (tid == 0) cnt[1] = S > 1 ? 1 : 0;
+  __syncthreads();
+  if (S == 1) {  // one list is ascending by contract; sort it anyway if it is not
+    for (int i = tid + 1; i < union_cap; i += kResThreads)
+      if (U[i - 1] > U[i]) cnt[1] = 1;
+    __syncthreads();
+  }
+  if (cnt[1]) {
+    for (int k = 2; k <= union_cap; k <<= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        for (int i = tid; i < union_cap; i += kResThreads) {
+          const int ixj = i ^ jj;
+          if (ixj > i) {
+            const int32_t a = U[i], c = U[ixj];
+            const bool asc = (i & k) == 0;
+            if (asc ? (a > c) : (a < c)) {
+              U[i] = c;
+              U[ixj] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  // compaction of distinct valid entries (a single list is already sorted and distinct)
+  int nU = 0;
+  {
+    int carry = 0;
+    for (int base = 0; base < union_cap; base += kResThreads) {
+      const int i = base + tid;
+      const int32_t v = U[i];
+      const bool keep = v != INT32_MAX && (i == 0 || U[i - 1] != v);
+      int tot;
+      const int pos = carry + block_exclusive_scan<kResThreads>(keep ? 1 : 0, scan, &tot);
+      if (keep) cls[pos] = v;
+      carry += tot;
+    }
+    nU = carry;
+    __syncthreads();
+    for (int i = tid; i < nU; i += kResThreads) U[i] = cls[i];
+    __syncthreads();
+  }
+
+  // ---- 2. classify: resident / hot hit (stamp) / miss
+  int n_res = 0, n_hit = 0, n_miss = 0;
+  {
+    int carry = 0, res_c = 0, hit_c = 0;
+    for (int base = 0; base < nU; base += kResThreads) {
+      const int i = base + tid;
+      int is_miss = 0, is_res = 0, is_hit = 0;
+      if (i < nU) {
+        const int32_t u = U[i];
+        const int page = u >> 6;
+        const int32_t blk = bt[page];
+        int32_t c = -1;
+        if (blk >= 0) {
+          if (blk < num_gpu_blocks) c = blk * kBlock + (u & 63);
+          else raise_error(err, HS_DEVERR_BAD_BLOCK);
+          is_res = 1;
+        } else {
+          const int32_t s = t2s[u];
+          if (s >= 0 && s < H) {
+            flag[s] = 1;
+            st_stamp[s] = step;
+            const int32_t hb = hot[s >> 6];
+            if (hb >= 0 && hb < num_gpu_blocks) c = hb * kBlock + (s & 63);
+            else raise_error(err, HS_DEVERR_BAD_BLOCK);
+            is_hit = 1;
+          } else {
+            const int32_t hb = hbt[page];
+            if (hb < 0) raise_error(err, HS_DEVERR_NO_HOST_COPY);
+            else if (hb >= num_host_blocks) raise_error(err, HS_DEVERR_BAD_BLOCK);
+            else is_miss = 1;
+          }
+        }
+        cls[i] = c;
+      }
+      int tot;
+      const int rank = carry + block_exclusive_scan<kResThreads>(is_miss, scan, &tot);
+      if (is_miss) {
+        cls[i] = -2 - rank;                           // miss code carries its rank
+        msrc[rank] = hbt[U[i] >> 6] * kBlock + (U[i] & 63);
+      }
+      carry += tot;
+      int t2;
+      block_exclusive_scan<kResThreads>(is_res, scan, &t2);
+      res_c += t2;
+      block_exclusive_scan<kResThreads>(is_hit, scan, &t2);
+      hit_c += t2;
+    }
+    n_miss = carry;
+    n_res = res_c;
+    n_hit = hit_c;
+  }
+  __syncthreads();
+
+  // ---- 3. victims: the first n_miss untouched slots of the recency list
+  int n_assign = 0;
+  {
+    int carry = 0;
+    for (int base = 0; base < H; base += kResThreads) {
+      const int i = base + tid;
+      int32_t s = -1;
+      int cand = 0;
+      if (i < H) {
+        s = order_cur[i];
+        cand = (s >= 0 && s < H && !flag[s]) ? 1 : 0;
+      }
+      int tot;
+      const int r = carry + block_exclusive_scan<kResThreads>(cand, scan, &tot);
+      if (cand && r < n_miss) mdst[r] = s;
+      carry += tot;
+    }
+    n_assign = min(n_miss, carry);
+    if (tid == 0 && n_assign < n_miss) raise_error(err, HS_DEVERR_HOT_FULL);
+  }
+  __syncthreads();
+  for (int r = tid; r < n_assign; r += kResThreads) flag[mdst[r]] = 1;
+  __syncthreads();
+  // new recency list: untouched in old order, then touched in ascending slot order
+  {
+    int carry = 0;
+    for (int base = 0; base < H; base += kResThreads) {
+      const int i = base + tid;
+      int32_t s = -1;
+      int keep = 0;
+      if (i < H) {
+        s = order_cur[i];
+        keep = (s >= 0 && s < H && !flag[s]) ? 1 : 0;
+      }
+      int tot;
+      const int r = carry + block_exclusive_scan<kResThreads>(keep, scan, &tot);
+      if (keep) order_next[r] = s;
+      carry += tot;
+    }
+    const int n_untouched = carry;
+    carry = 0;
+    for (int base = 0; base < H; base += kResThreads) {
+      const int s = base + tid;
+      const int touched = (s < H && flag[s]) ? 1 : 0;
+      int tot;
+      const int r = carry + block_exclusive_scan<kResThreads>(touched, scan, &tot);
+      if (touched) order_next[n_untouched + r] = s;
+      carry += tot;
+    }
+  }
+
+  // ---- 4. assign victims to misses (ascending token order = rank order)
+  int new_fills = 0;
+  {
+    int fills = 0;
+    for (int i = tid; i < nU; i += kResThreads) {
+      const int32_t c = cls[i];
+      if (c > -2) continue;
+      const int r = -2 - c;
+      if (r >= n_assign) {
+        cls[i] = -1;
+        continue;
+      }
+      const int32_t u = U[i];
+      const int32_t v = mdst[r];
+      const int32_t old = st_tok[v];
+      if (old >= 0 && old < lmax) t2s[old] = -1;
+      else ++fills;
+      st_tok[v] = u;
+      st_stamp[v] = step;
+      t2s[u] = v;
+      const int32_t hb = hot[v >> 6];
+      int32_t row = -1;
+      if (hb >= 0 && hb < num_gpu_blocks) row = hb * kBlock + (v & 63);
+      else raise_error(err, HS_DEVERR_BAD_BLOCK);
+      cls[i] = row;
+      mdst[r] = row;
+    }
+    if (tid == 0) cnt[0] = 0;
+    __syncthreads();
+    atomicAdd(&cnt[0], fills);
+    __syncthreads();
+    new_fills = cnt[0];
+  }
+
+  // ---- 5. single-row copies from the pinned host pool, all layers
+  {
+    const int chunks = row_bytes / 16;
+    const int64_t gpu_layer = num_gpu_blocks * kBlock * (int64_t)row_bytes;
+    const int64_t host_layer = num_host_blocks * kBlock * (int64_t)row_bytes;
+    const int64_t total = (int64_t)n_assign * n_layers * chunks;
+    constexpr int kBatch = 4;
+    for (int64_t base = tid; base < total; base += (int64_t)kResThreads * kBatch) {
+      u32x4 v[kBatch];
+      int64_t dst[kBatch];
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        const int64_t idx = base + (int64_t)e * kResThreads;
+        dst[e] = -1;
+        if (idx < total) {
+          const int r = (int)(idx / (n_layers * chunks));
+          const int rem = (int)(idx % (n_layers * chunks));
+          const int layer = rem / chunks, q = rem % chunks;
+          if (mdst[r] >= 0) {
+            const int64_t so = layer * host_layer + (int64_t)msrc[r] * row_bytes + q * 16;
+            v[e] = *reinterpret_cast<const u32x4*>(host_pool + so);
+            dst[e] = layer * gpu_layer + (int64_t)mdst[r] * row_bytes + q * 16;
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e)
+        if (dst[e] >= 0) *reinterpret_cast<u32x4*>(kv_pool + dst[e]) = v[e];
+    }
+  }
+  __syncthreads();
+
+  // ---- 6. row ids, positionally
+  for (int i = tid; i < S * K; i += kResThreads) {
+    const int32_t t = tk[i];
+    int32_t r = -1;
+    if (t >= 0 && t < Lb) {
+      int lo = 0, hi = nU - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (U[mid] < t) lo = mid + 1;
+        else hi = mid;
+      }
+      r = cls[lo];
+    }
+    out[i] = r;
+  }
+  if (tid == 0) {
+    const int used = min(H, req_used[b] + new_fills);
+    req_used[b] = used;
+    req_step[b] = step + 1;
+    if (stats) {
+      stats[b * 4 + 0] = n_res;
+      stats[b * 4 + 1] = n_hit;
+      stats[b * 4 + 2] = n_miss;
+      stats[b * 4 + 3] = (used + kBlock - 1) / kBlock;
+    }
+  }
+}
+
+__global__ void hot_reset_kernel(int32_t* slot_token, int32_t* slot_stamp, int32_t* lru_order,
+                                 int64_t n_slots, int H, int32_t* tok2slot, int64_t n_tok,
+                                 int32_t* req_step, int32_t* req_used, int max_batch,
+                                 uint32_t* hist, int64_t n_hist, int64_t n_all, int32_t* err) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_all; i += stride) {
+    if (i < n_tok) tok2slot[i] = -1;
+    if (i < n_slots) {
+      slot_token[i] = -1;
+      slot_stamp[i] = -1;
+      lru_order[i] = (int32_t)(i % H);
+      lru_order[n_slots + i] = (int32_t)(i % H);
+    }
+    if (i < n_hist) hist[i] = 0;
+    if (i < max_batch) {
+      req_step[i] = 0;
+      req_used[i] = 0;
+    }
+    if (i == 0) *err = 0;
+  }
+}
+
+}  // namespace
+}  // namespace hs
+
+using namespace hs;
+
+static int union_cap_for(int S, int K) {
+  int n = 1;
+  while (n < S * K) n <<= 1;
+  return n < 1024 ? 1024 : n;
+}
+
+size_t hs_resolve_lds_bytes(int S, int K, int H) {
+  return (size_t)union_cap_for(S, K) * 16 + (size_t)((H + 15) / 16) * 16;
+}
+
+hipError_t hs_launch_resolve(const hs_ctx* ctx, const int32_t* topk, const int32_t* ctx_lens, int B,
+                             int S, int32_t* row_ids, int32_t* stats, hipStream_t stream) {
+  const hs_config& c = ctx->cfg;
+  const int H = ctx->lay.hot_rows;
+  const int cap = union_cap_for(S, c.topk);
+  const size_t lds = hs_resolve_lds_bytes(S, c.topk, H);
+  hipLaunchKernelGGL(resolve_kernel, dim3((unsigned)B), dim3(kResThreads), lds, stream, topk,
+                     ctx_lens, S, c.topk, ctx->buf.block_table, ctx->buf.host_block_table,
+                     ctx->buf.hot_blocks, c.max_pages_per_req, H, (int64_t)c.num_gpu_blocks,
+                     (int64_t)c.num_host_blocks, c.max_batch, ctx->ws.slot_token,
+                     ctx->ws.slot_stamp, ctx->ws.lru_order, ctx->ws.tok2slot, ctx->lay.lmax,
+                     ctx->ws.req_step, ctx->ws.req_used,
+                     static_cast<const uint8_t*>(ctx->host_pool_dev),
+                     static_cast<uint8_t*>(ctx->buf.kv_pool), c.n_layers, ctx->row_bytes, cap,
+                     row_ids, stats, ctx->ws.err);
+  return hipGetLastError();
+}
+
+hipError_t hs_launch_hot_reset(const hs_ctx* ctx, hipStream_t stream) {
+  const hs_config& c = ctx->cfg;
+  const int64_t n_slots = (int64_t)c.max_batch * ctx->lay.hot_rows;
+  const int64_t n_tok = (int64_t)c.max_batch * ctx->lay.lmax;
+  const int64_t n_hist = (int64_t)c.max_batch * c.max_queries * kHistBins;
+  int64_t n = n_tok;
+  if (n_slots > n) n = n_slots;
+  if (n_hist > n) n = n_hist;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(hot_reset_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     ctx->ws.slot_token, ctx->ws.slot_stamp, ctx->ws.lru_order, n_slots,
+                     ctx->lay.hot_rows, ctx->ws.tok2slot, n_tok, ctx->ws.req_step, ctx->ws.req_used,
+                     c.max_batch, ctx->ws.hist, n_hist, n, ctx->ws.err);
+  return hipGetLastError();
+}
+
+hipError_t hs_resolve_set_attributes(size_t lds_bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&resolve_kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+}

@@ -1,0 +1,301 @@
+"""ctypes binding of libhisparse.so (the C ABI in include/hisparse.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP library.
+PyTorch is used for device memory and streams.  The library must be built
+(``python -m sparse_mla_attention_score_amd.build``); importing this module
+without it raises, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhisparse.so")
+
+HS_OK, HS_ERR_INVALID_ARG, HS_ERR_UNSUPPORTED, HS_ERR_OUT_OF_MEMORY, HS_ERR_HIP, HS_ERR_STATE = \
+    0, -1, -2, -3, -4, -5
+HS_BF16, HS_FP8_E4M3 = 0, 1
+HS_DEVERR_NO_HOST_COPY = 0x1
+HS_DEVERR_BAD_BLOCK = 0x2
+HS_DEVERR_BAD_ROW = 0x4
+HS_DEVERR_SHORT_CONTEXT = 0x8
+HS_DEVERR_TOPK_COUNT = 0x10
+HS_DEVERR_HOT_FULL = 0x20
+
+EXPORTED = ["hs_create", "hs_destroy", "hs_workspace_bytes", "hs_host_pool_bytes",
+            "hs_host_pool_alloc", "hs_bind", "hs_hot_reset", "hisparse_index_topk",
+            "hisparse_resolve", "sparse_mla_decode", "hs_read_device_error", "hs_decode_splits",
+            "hs_hot_state", "hs_status_string", "hs_last_error"]
+
+
+class hs_config(ctypes.Structure):
+    _fields_ = [("block_size", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("n_idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("idx_dtype", ctypes.c_int32),
+                ("n_layers", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+                ("max_queries", ctypes.c_int32), ("max_pages_per_req", ctypes.c_int32),
+                ("hot_rows_per_req", ctypes.c_int32), ("topk_lds_candidates", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("num_gpu_blocks", ctypes.c_int64),
+                ("num_idx_blocks", ctypes.c_int64), ("num_host_blocks", ctypes.c_int64)]
+
+
+class hs_buffers(ctypes.Structure):
+    _fields_ = [("kv_pool", ctypes.c_void_p), ("idx_pool", ctypes.c_void_p),
+                ("idx_block_table", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("host_block_table", ctypes.c_void_p), ("hot_blocks", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p)]
+
+
+class hs_hot_state_ptrs(ctypes.Structure):
+    _fields_ = [("slot_token", ctypes.c_void_p), ("slot_stamp", ctypes.c_void_p),
+                ("tok2slot", ctypes.c_void_p), ("req_step", ctypes.c_void_p),
+                ("hot_rows", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("tokens_per_req", ctypes.c_int64)]
+
+
+class HiSparseError(RuntimeError):
+    def __init__(self, what: str, status: int):
+        self.status = status
+        super().__init__(f"{what}: {hs_status_string(status)}: {hs_last_error()}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_mla_attention_score_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+        sig = {
+            "hs_create": [ctypes.POINTER(hs_config), ctypes.POINTER(P)],
+            "hs_destroy": [P],
+            "hs_workspace_bytes": [ctypes.POINTER(hs_config), ctypes.POINTER(ctypes.c_size_t)],
+            "hs_host_pool_bytes": [ctypes.POINTER(hs_config), ctypes.POINTER(ctypes.c_size_t)],
+            "hs_host_pool_alloc": [P, ctypes.POINTER(P)],
+            "hs_bind": [P, ctypes.POINTER(hs_buffers)],
+            "hs_hot_reset": [P, P],
+            "hisparse_index_topk": [P, P, P, P, i32, i32, P, P],
+            "hisparse_resolve": [P, P, P, i32, i32, P, P, P],
+            "sparse_mla_decode": [P, i32, P, P, P, i32, i32, f32, P, P, P],
+            "hs_read_device_error": [P, ctypes.POINTER(i32)],
+            "hs_decode_splits": [P, i32, i32, ctypes.POINTER(i32)],
+            "hs_hot_state": [P, ctypes.POINTER(hs_hot_state_ptrs)],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.hs_status_string.argtypes = [ctypes.c_int]
+        L.hs_status_string.restype = ctypes.c_char_p
+        L.hs_last_error.argtypes = []
+        L.hs_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def hs_status_string(status: int) -> str:
+    return lib().hs_status_string(status).decode()
+
+
+def hs_last_error() -> str:
+    return lib().hs_last_error().decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != HS_OK:
+        raise HiSparseError(what, status)
+
+
+# ---------------------------------------------------------------- thin wrappers (same names)
+
+def hs_workspace_bytes(cfg: hs_config) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().hs_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)), "hs_workspace_bytes")
+    return n.value
+
+
+def hs_host_pool_bytes(cfg: hs_config) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().hs_host_pool_bytes(ctypes.byref(cfg), ctypes.byref(n)), "hs_host_pool_bytes")
+    return n.value
+
+
+def hs_create(cfg: hs_config) -> int:
+    ctx = ctypes.c_void_p()
+    _check(lib().hs_create(ctypes.byref(cfg), ctypes.byref(ctx)), "hs_create")
+    return ctx.value
+
+
+def hs_destroy(ctx: int) -> None:
+    _check(lib().hs_destroy(ctx), "hs_destroy")
+
+
+def hs_host_pool_alloc(ctx: int) -> int:
+    p = ctypes.c_void_p()
+    _check(lib().hs_host_pool_alloc(ctx, ctypes.byref(p)), "hs_host_pool_alloc")
+    return p.value or 0
+
+
+def hs_bind(ctx: int, bufs: hs_buffers) -> None:
+    _check(lib().hs_bind(ctx, ctypes.byref(bufs)), "hs_bind")
+
+
+def hs_hot_reset(ctx: int, stream: int) -> None:
+    _check(lib().hs_hot_reset(ctx, stream), "hs_hot_reset")
+
+
+def hisparse_index_topk(ctx: int, q_idx: int, w: int, ctx_lens: int, B: int, S: int, topk_out: int,
+                        stream: int) -> None:
+    _check(lib().hisparse_index_topk(ctx, q_idx, w, ctx_lens, B, S, topk_out, stream),
+           "hisparse_index_topk")
+
+
+def hisparse_resolve(ctx: int, topk: int, ctx_lens: int, B: int, S: int, row_ids_out: int,
+                     stats_out: int, stream: int) -> None:
+    _check(lib().hisparse_resolve(ctx, topk, ctx_lens, B, S, row_ids_out, stats_out or None, stream),
+           "hisparse_resolve")
+
+
+def sparse_mla_decode(ctx: int, layer: int, q: int, row_ids: int, ctx_lens: int, B: int, S: int,
+                      sm_scale: float, out: int, lse: int, stream: int) -> None:
+    _check(lib().sparse_mla_decode(ctx, layer, q, row_ids, ctx_lens, B, S, sm_scale, out,
+                                   lse or None, stream), "sparse_mla_decode")
+
+
+def hs_read_device_error(ctx: int) -> int:
+    code = ctypes.c_int32()
+    _check(lib().hs_read_device_error(ctx, ctypes.byref(code)), "hs_read_device_error")
+    return code.value
+
+
+def hs_decode_splits(ctx: int, B: int, S: int) -> int:
+    n = ctypes.c_int32()
+    _check(lib().hs_decode_splits(ctx, B, S, ctypes.byref(n)), "hs_decode_splits")
+    return n.value
+
+
+def hs_hot_state(ctx: int) -> hs_hot_state_ptrs:
+    out = hs_hot_state_ptrs()
+    _check(lib().hs_hot_state(ctx, ctypes.byref(out)), "hs_hot_state")
+    return out
+
+
+def make_config(*, topk: int = 2048, kv_dtype: int = HS_FP8_E4M3, idx_dtype: int = HS_FP8_E4M3,
+                n_layers: int = 1, max_batch: int, max_queries: int, max_pages_per_req: int,
+                hot_rows_per_req: int = 0, num_gpu_blocks: int, num_idx_blocks: int,
+                num_host_blocks: int, topk_lds_candidates: int = 0) -> hs_config:
+    return hs_config(64, topk, 32, 128, 64, 576, 512, kv_dtype, idx_dtype, n_layers, max_batch,
+                     max_queries, max_pages_per_req, hot_rows_per_req, topk_lds_candidates, 0,
+                     num_gpu_blocks, num_idx_blocks, num_host_blocks)
+
+
+# ---------------------------------------------------------------- torch plumbing
+
+class Context:
+    """A bound context whose device buffers are torch tensors on `device`.
+
+    Pools and tables are allocated here; the caller fills them (e.g. from the
+    synthetic generator) through the tensors / the host-pool numpy view.
+    """
+
+    def __init__(self, cfg: hs_config, device="cuda:0"):
+        import numpy as np
+        import torch
+
+        self.cfg = cfg
+        self.device = torch.device(device)
+        torch.cuda.set_device(self.device)
+        rb = 656 if cfg.kv_dtype == HS_FP8_E4M3 else 1152
+        ib = 8448 if cfg.idx_dtype == HS_FP8_E4M3 else 16384
+        self.row_bytes = rb
+        self.idx_block_bytes = ib
+        self.hot_rows = cfg.hot_rows_per_req or -(-((cfg.max_queries + 1) * cfg.topk) // 64) * 64
+        u8 = dict(dtype=torch.uint8, device=self.device)
+        i32 = dict(dtype=torch.int32, device=self.device)
+        self.kv_pool = torch.empty(cfg.n_layers * cfg.num_gpu_blocks * 64 * rb, **u8)
+        self.idx_pool = torch.empty(cfg.num_idx_blocks * ib, **u8)
+        P = cfg.max_pages_per_req
+        self.idx_block_table = torch.full((cfg.max_batch, P), -1, **i32)
+        self.block_table = torch.full((cfg.max_batch, P), -1, **i32)
+        self.host_block_table = torch.full((cfg.max_batch, P), -1, **i32)
+        self.hot_blocks = torch.zeros((cfg.max_batch, max(1, self.hot_rows // 64)), **i32)
+        ws = hs_workspace_bytes(cfg)
+        self.workspace = torch.empty(ws + 256, **u8)
+        ws_ptr = (self.workspace.data_ptr() + 255) // 256 * 256
+        self.ctx = hs_create(cfg)
+        self.host_base = hs_host_pool_alloc(self.ctx)
+        nh = hs_host_pool_bytes(cfg)
+        self.host_pool = None
+        if self.host_base and nh:
+            buf = (ctypes.c_uint8 * nh).from_address(self.host_base)
+            self.host_pool = np.frombuffer(buf, dtype=np.uint8)
+        bufs = hs_buffers(self.kv_pool.data_ptr(), self.idx_pool.data_ptr(),
+                          self.idx_block_table.data_ptr(), self.block_table.data_ptr(),
+                          self.host_block_table.data_ptr(), self.hot_blocks.data_ptr(), ws_ptr)
+        hs_bind(self.ctx, bufs)
+        self.reset()
+
+    @staticmethod
+    def stream() -> int:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+
+    def reset(self) -> None:
+        hs_hot_reset(self.ctx, self.stream())
+
+    def index_topk(self, q_idx, w, ctx_lens, topk_out) -> None:
+        B, S = q_idx.shape[0], q_idx.shape[1]
+        hisparse_index_topk(self.ctx, q_idx.data_ptr(), w.data_ptr(), ctx_lens.data_ptr(), B, S,
+                            topk_out.data_ptr(), self.stream())
+
+    def resolve(self, topk, ctx_lens, row_ids_out, stats_out=None) -> None:
+        B, S = topk.shape[0], topk.shape[1]
+        hisparse_resolve(self.ctx, topk.data_ptr(), ctx_lens.data_ptr(), B, S,
+                         row_ids_out.data_ptr(), stats_out.data_ptr() if stats_out is not None else 0,
+                         self.stream())
+
+    def decode(self, layer, q, row_ids, ctx_lens, sm_scale, out, lse=None) -> None:
+        B, S = q.shape[0], q.shape[1]
+        sparse_mla_decode(self.ctx, layer, q.data_ptr(), row_ids.data_ptr(), ctx_lens.data_ptr(),
+                          B, S, sm_scale, out.data_ptr(), lse.data_ptr() if lse is not None else 0,
+                          self.stream())
+
+    def device_error(self) -> int:
+        return hs_read_device_error(self.ctx)
+
+    def hot_state(self):
+        """Copies of (slot_token [B][H], slot_stamp [B][H], tok2slot [B][L], req_step [B]) as
+        int32 numpy arrays, read from the workspace the library bound."""
+        import numpy as np
+        import torch
+        p = hs_hot_state(self.ctx)
+        ws0 = (self.workspace.data_ptr() + 255) // 256 * 256
+        base = self.workspace.data_ptr()
+        B, H, L = self.cfg.max_batch, p.hot_rows, p.tokens_per_req
+
+        def view(addr, n):
+            off = addr - base
+            assert off >= ws0 - base and off + 4 * n <= self.workspace.numel()
+            return self.workspace[off:off + 4 * n].view(torch.int32).cpu().numpy()
+
+        torch.cuda.synchronize()
+        return (view(p.slot_token, B * H).reshape(B, H), view(p.slot_stamp, B * H).reshape(B, H),
+                view(p.tok2slot, B * L).reshape(B, L), view(p.req_step, B).copy())
+
+    def close(self) -> None:
+        if getattr(self, "ctx", None):
+            hs_destroy(self.ctx)
+            self.ctx = None
+            self.host_pool = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,82 @@
+"""The C ABI library loads, exports every declared entry point, and validates configurations
+on the host (no GPU work)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_mla_attention_score_amd import hisparse as hsb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hisparse.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:hs_status|const char\*)\s+(\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = hsb.lib()
+    declared = _declared()
+    assert len(declared) >= 15
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(hsb.EXPORTED) == declared
+
+
+def _cfg(**kw):
+    base = dict(topk=2048, max_batch=64, max_queries=4, max_pages_per_req=2049,
+                num_gpu_blocks=30000, num_idx_blocks=131200, num_host_blocks=118000)
+    base.update(kw)
+    return hsb.make_config(**base)
+
+
+def test_workspace_and_pool_sizes():
+    cfg = _cfg()
+    ws = hsb.hs_workspace_bytes(cfg)
+    lmax = 2049 * 64
+    assert ws > 64 * 4 * lmax * 4          # at least the score scratch
+    assert ws < 4 * 2 ** 30
+    assert hsb.hs_host_pool_bytes(cfg) == 118000 * 64 * 656
+    cfg2 = _cfg(n_layers=4, kv_dtype=hsb.HS_BF16)
+    assert hsb.hs_host_pool_bytes(cfg2) == 4 * 118000 * 64 * 1152
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("block_size", 32, hsb.HS_ERR_UNSUPPORTED),
+    ("n_heads", 128, hsb.HS_ERR_UNSUPPORTED),
+    ("d_qk", 512, hsb.HS_ERR_UNSUPPORTED),
+    ("topk", 4096, hsb.HS_ERR_UNSUPPORTED),
+    ("topk", 0, hsb.HS_ERR_UNSUPPORTED),
+    ("max_queries", 5, hsb.HS_ERR_UNSUPPORTED),
+    ("max_batch", 0, hsb.HS_ERR_INVALID_ARG),
+    ("n_layers", 0, hsb.HS_ERR_INVALID_ARG),
+    ("hot_rows_per_req", 100, hsb.HS_ERR_INVALID_ARG),      # not a multiple of 64
+    ("hot_rows_per_req", 4096, hsb.HS_ERR_INVALID_ARG),     # < S * K = 8192
+    ("kv_dtype", 7, hsb.HS_ERR_UNSUPPORTED),
+    ("num_gpu_blocks", 0, hsb.HS_ERR_INVALID_ARG),
+    ("num_gpu_blocks", 1 << 26, hsb.HS_ERR_INVALID_ARG),     # row ids would overflow int32
+])
+def test_config_validation(field, value, status):
+    cfg = _cfg()
+    setattr(cfg, field, value)
+    with pytest.raises(hsb.HiSparseError) as e:
+        hsb.hs_workspace_bytes(cfg)
+    assert e.value.status == status
+    assert hsb.hs_last_error()
+
+
+def test_default_hot_buffer_follows_the_pages_rule():
+    # 0 selects (S + 1) x top-K: 2 x K without MTP, (spec + 2) x K with MTP3
+    assert hsb.hs_workspace_bytes(_cfg(hot_rows_per_req=0)) == hsb.hs_workspace_bytes(_cfg(hot_rows_per_req=10240))
+    c1 = _cfg(max_queries=1, max_batch=32)
+    assert hsb.hs_workspace_bytes(c1) == hsb.hs_workspace_bytes(_cfg(max_queries=1, max_batch=32, hot_rows_per_req=4096))
+
+
+def test_status_strings():
+    assert hsb.hs_status_string(0) == "HS_OK"
+    assert hsb.hs_status_string(-2) == "HS_ERR_UNSUPPORTED"
+    lib = hsb.lib()
+    assert lib.hs_destroy(None) == hsb.HS_ERR_INVALID_ARG
