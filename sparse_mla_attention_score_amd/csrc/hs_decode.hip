@@ -8,18 +8,21 @@
 //
 // FP8 rows (656 bytes) hold 512 E4M3 codes c with one fp32 scale a, and 64 bf16 rope values.
 // The per-row scale is folded out of the contractions: q . x = a (q_nope . c) + q_rope . rope,
-// and sum_k p_k x_k = sum_k (p_k a_k) c_k, so the MFMAs see exactly converted bf16 codes.
+// and sum_k p_k x_k = sum_k (p_k a_k) c_k, so the MFMAs see the codes converted exactly.
 //
-// Workgroup = (query token, split of its rows), 4 waves; wave w owns heads 16w .. 16w+15 and
-// keeps its 16 x 576 query slice in registers.  Rows are processed in tiles of 64: the tile is
-// gathered from HBM once (8-byte pieces of 8 rows per thread, coalesced along the row) and
-// written to LDS twice, row-major for QK and transposed (dim-major) for PV, the transpose done
-// in registers with byte permutes.  Each wave computes S^T = K Q^T and O^T = V^T P^T on 16x16x32
-// bf16 MFMAs; in that orientation a lane owns one head, so the online-softmax state is
-// per-lane and the probabilities feed the PV MFMA straight from registers (the PV k-slots
-// are assigned to rows in the order the QK result lays them out, and the transposed V tile
-// is stored in the same order).  Splits of one query are combined with log-sum-exp, the same
-// algebra as merging per-shard partial attention (part-2 page, "DCP" section).
+// Workgroup = (query token, split of its rows), 4 waves = 2 head groups (32 heads each) x 2
+// halves.  Rows go in tiles of 64.  A tile is gathered from HBM once (8-byte pieces of 8
+// rows per thread, coalesced along the row), converted to bf16 once, and written to LDS twice:
+// row-major for QK and dim-major for PV (transposed in registers).  The next tile's loads are
+// issued before the current tile is computed.  Each wave computes S^T = K Q^T for its 32 heads
+// on half the tile's rows, and O^T += V^T P^T for its 32 heads on half the value dims over all
+// the rows, on 32x32x16 bf16 MFMAs; the two waves of a head group swap their row maxima and
+// probabilities through LDS.  In this orientation a lane owns one head, so the softmax state is
+// per lane and the probabilities feed the PV MFMA in the layout the QK result has (the PV
+// k-slots are assigned to rows in that order, and the transposed tile is stored in it).  The
+// running maximum is only moved when it grows by more than 2^8, so the accumulators are rarely
+// rescaled.  Splits of one query are combined with log-sum-exp, the same algebra as merging
+// per-shard partial attention (part-2 page, "DCP" section).
 #include "hs_device.h"
 #include "hs_internal.h"
 
@@ -27,130 +30,161 @@ namespace hs {
 namespace {
 
 constexpr int kDecThreads = 256;
+constexpr float kLazyRescale = 8.0f;  // log2 units
 
-template <bool kFp8>
-struct DecodeLds {
-  static constexpr int kNopeStride = kFp8 ? 528 : 1040;  // bytes per row of the nope part
-  static constexpr int kRopeStride = 144;                 // 64 bf16 + pad
-  static constexpr int kVtStride = kFp8 ? 72 : 144;       // bytes per dim of the transposed tile
-  static constexpr int kNopeBytes = kTileRows * kNopeStride;
-  static constexpr int kRopeBytes = kTileRows * kRopeStride;
-  static constexpr int kVtBytes = kDv * kVtStride;
-  static constexpr int kOffRope = kNopeBytes;
-  static constexpr int kOffVt = kOffRope + kRopeBytes;
-  static constexpr int kOffScale = kOffVt + kVtBytes;
+// LDS of one tile (bf16 after conversion).
+struct DecLds {
+  static constexpr int kKStride = kDqk * 2 + 16;          // bytes per row: 576 bf16 + pad
+  static constexpr int kVtStride = kTileRows * 2 + 16;    // bytes per dim: 64 bf16 + pad
+  static constexpr int kOffVt = kTileRows * kKStride;
+  static constexpr int kOffScale = kOffVt + kDv * kVtStride;
   static constexpr int kOffRid = kOffScale + kTileRows * 4;
   static constexpr int kTotal = kOffRid + kTileRows * 4;
 };
+static_assert(DecLds::kTotal <= 160 * 1024, "decode LDS");
 
-// Gather one 64-row tile into LDS (both layouts).  Rows at positions >= n_tile are zero.
+// Position in the transposed tile of row r (0..63): within each 32-row half, 16-row k-steps;
+// within a k-step, lane half hf holds rows {4hf..4hf+3, 8+4hf..8+4hf+3} at 8 hf .. 8 hf + 7.
+__device__ __forceinline__ int vt_pos(int r) {
+  const int rh = r >> 5, kap = (r >> 4) & 1, q = r & 15;
+  const int hf = (q >> 2) & 1, e = (q & 3) + ((q >> 3) << 2);
+  return 32 * rh + 16 * kap + 8 * hf + e;
+}
+
+// Thread work of a gather: two blocks of 8 rows x 8 dims (nope part) and two 16-byte rope
+// pieces.  Block g = tid + 256 it: dim group dg = g % 64, row group rg = g / 64 whose 8 rows are
+// the ones stored at transposed positions 8 rg .. 8 rg + 7.
 template <bool kFp8>
-__device__ __forceinline__ void gather_tile(const uint8_t* __restrict__ kv, unsigned char* lds,
-                                            const int32_t* __restrict__ rid_src, int n_tile,
-                                            int64_t n_rows_pool, int32_t* err) {
-  using Lds = DecodeLds<kFp8>;
+struct TileRegs {
+  u32x2 nope[2][8];       // FP8: 8 codes per row piece
+  u32x4 nope16[kFp8 ? 1 : 2][kFp8 ? 1 : 8];  // bf16 rows: 8 values per row piece
+  u32x4 rope[2];
+  float scale;
+};
+
+__device__ __forceinline__ int row_of_pos(int p) {
+  // inverse of vt_pos
+  const int rh = p >> 5, kap = (p >> 4) & 1, hf = (p >> 3) & 1, e = p & 7;
+  return 32 * rh + 16 * kap + (e < 4 ? 4 * hf + e : 8 + 4 * hf + (e - 4));
+}
+
+template <bool kFp8>
+__device__ __forceinline__ void gather_load(TileRegs<kFp8>& tr, const uint8_t* __restrict__ kv,
+                                            const int32_t* rid) {
   constexpr int kRow = kFp8 ? kFp8Row : kBf16Row;
   const int tid = threadIdx.x;
-  int32_t* rid = reinterpret_cast<int32_t*>(lds + Lds::kOffRid);
-  float* scale = reinterpret_cast<float*>(lds + Lds::kOffScale);
-  if (tid < kTileRows) {
-    int32_t r = tid < n_tile ? rid_src[tid] : -1;
-    if (r >= n_rows_pool || (tid < n_tile && r < 0)) {
-      raise_error(err, HS_DEVERR_BAD_ROW);
-      r = -1;
-    }
-    rid[tid] = r;
-    float a = 0.0f;
-    if (kFp8 && r >= 0) a = *reinterpret_cast<const float*>(kv + (int64_t)r * kRow + 640);
-    scale[tid] = a;
-  }
-  __syncthreads();
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
-    const int e = tid + kDecThreads * it;
-    const int dg = e & 63, rg = e >> 6;
-    const int kap = rg >> 2, g = rg & 3;
-    int rows[8];
+    const int g = tid + kDecThreads * it;
+    const int dg = g & 63, rg = g >> 6;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rows[i] = 32 * kap + 4 * g + i;
-      rows[4 + i] = 32 * kap + 16 + 4 * g + i;
-    }
-    if constexpr (kFp8) {
-      uint32_t lo[8], hi[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int32_t r = rid[rows[i]];
-        u32x2 v = {0u, 0u};
-        if (r >= 0) v = *reinterpret_cast<const u32x2*>(kv + (int64_t)r * kRow + 8 * dg);
-        lo[i] = v[0];
-        hi[i] = v[1];
-        *reinterpret_cast<u32x2*>(lds + rows[i] * Lds::kNopeStride + 8 * dg) = v;
-      }
-      uint32_t a[4], bq[4], c[4], d[4];
-      transpose4x4_bytes(lo[0], lo[1], lo[2], lo[3], a[0], a[1], a[2], a[3]);
-      transpose4x4_bytes(lo[4], lo[5], lo[6], lo[7], bq[0], bq[1], bq[2], bq[3]);
-      transpose4x4_bytes(hi[0], hi[1], hi[2], hi[3], c[0], c[1], c[2], c[3]);
-      transpose4x4_bytes(hi[4], hi[5], hi[6], hi[7], d[0], d[1], d[2], d[3]);
-      unsigned char* vt = lds + Lds::kOffVt + 32 * kap + 8 * g;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        *reinterpret_cast<u32x2*>(vt + (8 * dg + k) * Lds::kVtStride) = u32x2{a[k], bq[k]};
-        *reinterpret_cast<u32x2*>(vt + (8 * dg + 4 + k) * Lds::kVtStride) = u32x2{c[k], d[k]};
-      }
-    } else {
-      u32x4 v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int32_t r = rid[rows[i]];
-        v[i] = u32x4{0u, 0u, 0u, 0u};
-        if (r >= 0) v[i] = *reinterpret_cast<const u32x4*>(kv + (int64_t)r * kRow + 16 * dg);
-        *reinterpret_cast<u32x4*>(lds + rows[i] * Lds::kNopeStride + 16 * dg) = v[i];
-      }
-      unsigned char* vt = lds + Lds::kOffVt + 2 * (32 * kap + 8 * g);
-#pragma unroll
-      for (int dw = 0; dw < 4; ++dw) {
-        u32x4 even, odd;
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-          uint32_t c0, c1;
-          transpose2x2_u16(v[2 * pr][dw], v[2 * pr + 1][dw], c0, c1);
-          even[pr] = c0;
-          odd[pr] = c1;
-        }
-        *reinterpret_cast<u32x4*>(vt + (8 * dg + 2 * dw) * Lds::kVtStride) = even;
-        *reinterpret_cast<u32x4*>(vt + (8 * dg + 2 * dw + 1) * Lds::kVtStride) = odd;
+    for (int e = 0; e < 8; ++e) {
+      const int32_t r = rid[row_of_pos(8 * rg + e)];
+      if constexpr (kFp8) {
+        tr.nope[it][e] = u32x2{0u, 0u};
+        if (r >= 0) tr.nope[it][e] = *reinterpret_cast<const u32x2*>(kv + (int64_t)r * kRow + 8 * dg);
+      } else {
+        tr.nope16[it][e] = u32x4{0u, 0u, 0u, 0u};
+        if (r >= 0) tr.nope16[it][e] = *reinterpret_cast<const u32x4*>(kv + (int64_t)r * kRow + 16 * dg);
       }
     }
   }
-  // rope: 64 rows x 128 bytes (bf16) in 16-byte pieces
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
-    const int cidx = tid + kDecThreads * it;
-    const int row = cidx >> 3, part = cidx & 7;
+    const int c = tid + kDecThreads * it;
+    const int row = c >> 3, part = c & 7;
     const int32_t r = rid[row];
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r >= 0) v = *reinterpret_cast<const u32x4*>(kv + (int64_t)r * kRow + (kFp8 ? 512 : 1024) + 16 * part);
-    *reinterpret_cast<u32x4*>(lds + Lds::kOffRope + row * Lds::kRopeStride + 16 * part) = v;
+    tr.rope[it] = u32x4{0u, 0u, 0u, 0u};
+    if (r >= 0)
+      tr.rope[it] = *reinterpret_cast<const u32x4*>(kv + (int64_t)r * kRow + (kFp8 ? 512 : 1024) + 16 * part);
   }
-  __syncthreads();
+  tr.scale = 0.0f;
+  if (kFp8 && tid < kTileRows) {
+    const int32_t r = rid[tid];
+    if (r >= 0) tr.scale = *reinterpret_cast<const float*>(kv + (int64_t)r * kRow + 640);
+  }
+}
+
+// Convert and store a gathered tile: K row-major (bf16, 576 per row) and V^T (bf16, dim-major,
+// rows in transposed-position order).
+template <bool kFp8>
+__device__ __forceinline__ void gather_store(const TileRegs<kFp8>& tr, unsigned char* lds) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int g = tid + kDecThreads * it;
+    const int dg = g & 63, rg = g >> 6;
+    u32x4 v[8];  // 8 rows x 8 bf16 values (dims 8 dg .. 8 dg + 7)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (kFp8) {
+        v[e] = __builtin_bit_cast(u32x4, e4m3x8_to_bf16(tr.nope[it][e][0], tr.nope[it][e][1]));
+      } else {
+        v[e] = tr.nope16[it][e];
+      }
+      const int row = row_of_pos(8 * rg + e);
+      *reinterpret_cast<u32x4*>(lds + row * DecLds::kKStride + 16 * dg) = v[e];
+    }
+    // transpose the 8 x 8 block of 16-bit values: dim d gets rows (positions) 0..7
+    unsigned char* vt = lds + DecLds::kOffVt + 2 * 8 * rg;
+#pragma unroll
+    for (int dw = 0; dw < 4; ++dw) {
+      u32x4 even, odd;
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) {
+        uint32_t c0, c1;
+        transpose2x2_u16(v[2 * pr][dw], v[2 * pr + 1][dw], c0, c1);
+        even[pr] = c0;
+        odd[pr] = c1;
+      }
+      *reinterpret_cast<u32x4*>(vt + (8 * dg + 2 * dw) * DecLds::kVtStride) = even;
+      *reinterpret_cast<u32x4*>(vt + (8 * dg + 2 * dw + 1) * DecLds::kVtStride) = odd;
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int c = tid + kDecThreads * it;
+    const int row = c >> 3, part = c & 7;
+    *reinterpret_cast<u32x4*>(lds + row * DecLds::kKStride + 1024 + 16 * part) = tr.rope[it];
+  }
+  if (tid < kTileRows) reinterpret_cast<float*>(lds + DecLds::kOffScale)[tid] = kFp8 ? tr.scale : 1.0f;
 }
 
 template <bool kFp8>
 __global__ __launch_bounds__(kDecThreads) void sparse_mla_decode_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ row_ids,
-    const int32_t* __restrict__ ctx_lens, int S, int K, int max_ctx,
+    const int32_t* __restrict__ ctx_lens, int B, int S, int K, int max_ctx,
     const uint8_t* __restrict__ kv, int64_t n_rows_pool, float qk_scale_log2, int splits,
-    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    int xcd_map, uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml, int32_t* __restrict__ err) {
-  using Lds = DecodeLds<kFp8>;
   extern __shared__ __align__(16) unsigned char lds[];
+  __shared__ int32_t rid_next[kTileRows];
+  // probabilities of each wave's row half, in its PV operand layout: [hg][dh][kap][lane]
+  __shared__ __align__(16) u32x4 pshare[2][2][2][64];
+  __shared__ float mshare[2][2][32];  // per-tile row maximum of each half, per head
+  __shared__ float lshare[2][2][32];  // final row sums
 
-  const int bj = blockIdx.x / splits, sp = blockIdx.x % splits;
-  const int b = bj / S, j = bj % S;
+  // Workgroup -> (request, query, split).  With xcd_map, the S*splits workgroups of a request
+  // get ids congruent mod 8, i.e. the same XCD (workgroups are dealt to XCDs round-robin), so
+  // the MTP queries of a request, which select mostly the same rows, share its L2.
+  const int per_req = S * splits;
+  int b, r;
+  if (xcd_map) {
+    const int x = blockIdx.x, xcd = x & 7, slot = x >> 3;
+    b = xcd + 8 * (slot / per_req);
+    r = slot % per_req;
+  } else {
+    b = blockIdx.x / per_req;
+    r = blockIdx.x % per_req;
+  }
+  const int j = r / splits, sp = r % splits;
+  const int bj = b * S + j;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, g = lane >> 4;
-  const int head = 16 * wave + col;
+  // head group hg: heads 32 hg .. 32 hg + 31.  dh: this wave scores tile rows 32 dh .. 32 dh + 31
+  // and accumulates value dims 256 dh .. 256 dh + 255 over all rows.
+  const int hg = wave & 1, dh = wave >> 1;
+  const int col = lane & 31, hf = lane >> 5;
+  const int head = 32 * hg + col;
 
   const int Lb = ctx_lens[b];
   int n = 0;
@@ -158,123 +192,163 @@ __global__ __launch_bounds__(kDecThreads) void sparse_mla_decode_kernel(
   else if (tid == 0 && sp == 0) raise_error(err, HS_DEVERR_SHORT_CONTEXT);
   const int per = ((n + splits - 1) / splits + kTileRows - 1) / kTileRows * kTileRows;
   const int r0 = sp * per, r1 = min(n, r0 + per);
-
-  // Q^T fragments: B operand, k-slots 8g..8g+7 of k-step s = dims 32s + 8g .. +8.
-  bf16x8 qf[18];
-  const uint16_t* qp = q + ((int64_t)bj * kHeads + head) * kDqk + 8 * g;
-#pragma unroll
-  for (int s = 0; s < 18; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 32 * s));
-
-  f32x4 o[32];
-#pragma unroll
-  for (int m = 0; m < 32; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.0f;
-
   const int32_t* rids = row_ids + (int64_t)bj * K;
-  const float* scale = reinterpret_cast<const float*>(lds + Lds::kOffScale);
-  for (int t0 = r0; t0 < r1; t0 += kTileRows) {
-    const int n_tile = min(kTileRows, r1 - t0);
-    gather_tile<kFp8>(kv, lds, rids + t0, n_tile, n_rows_pool, err);
 
-    // ---- S^T = K Q^T for the 64 rows; lane holds rows 16 sig + 4 g + i of head `col`
-    float s2[4][4];
+  // Q^T fragments (B operand): k-step s covers dims 16 s .. 16 s + 15, lane half hf holds
+  // 8 hf .. 8 hf + 7 of them, for head `head`.
+  bf16x8 qf[36];
+  {
+    const uint16_t* qp = q + ((int64_t)bj * kHeads + head) * kDqk + 8 * hf;
 #pragma unroll
-    for (int sig = 0; sig < 4; ++sig) {
-      const int ra = 16 * sig + col;
-      f32x4 c1 = {0.f, 0.f, 0.f, 0.f}, c2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        bf16x8 a;
-        if constexpr (kFp8) {
-          const u32x2 kb = *reinterpret_cast<const u32x2*>(lds + ra * Lds::kNopeStride + 32 * s + 8 * g);
-          a = e4m3x8_to_bf16(kb[0], kb[1]);
-        } else {
-          a = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + ra * Lds::kNopeStride + 64 * s + 16 * g));
-        }
-        c1 = mfma16x16x32(a, qf[s], c1);
-      }
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            lds + Lds::kOffRope + ra * Lds::kRopeStride + 64 * s + 16 * g));
-        c2 = mfma16x16x32(a, qf[16 + s], c2);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * sig + 4 * g + i;
-        const float a = kFp8 ? scale[r] : 1.0f;
-        s2[sig][i] = r < n_tile ? (a * c1[i] + c2[i]) * qk_scale_log2 : -INFINITY;
-      }
-    }
-    // ---- online softmax (per head = per lane column; rows spread over the 4 lane groups)
-    float tmax = s2[0][0];
-#pragma unroll
-    for (int sig = 0; sig < 4; ++sig)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s2[sig][i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    l_part *= alpha;
-#pragma unroll
-    for (int m = 0; m < 32; ++m) o[m] *= alpha;
-    bf16x8 pb[2];
-#pragma unroll
-    for (int sig = 0; sig < 4; ++sig)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(s2[sig][i] - m_new);
-        l_part += p;
-        const float a = kFp8 ? scale[16 * sig + 4 * g + i] : 1.0f;
-        pb[sig >> 1][(sig & 1) * 4 + i] = (__bf16)(p * a);
-      }
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int kap = 0; kap < 2; ++kap) {
-#pragma unroll
-      for (int m = 0; m < 32; ++m) {
-        bf16x8 a;
-        const unsigned char* vp = lds + Lds::kOffVt + (16 * m + col) * Lds::kVtStride;
-        if constexpr (kFp8) {
-          const u32x2 v = *reinterpret_cast<const u32x2*>(vp + 32 * kap + 8 * g);
-          a = e4m3x8_to_bf16(v[0], v[1]);
-        } else {
-          a = as_bf16x8(*reinterpret_cast<const u32x4*>(vp + 2 * (32 * kap + 8 * g)));
-        }
-        o[m] = mfma16x16x32(a, pb[kap], o[m]);
-      }
-    }
-    __syncthreads();  // the tile's LDS is reused by the next gather
+    for (int s = 0; s < 36; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * s));
   }
 
-  float l_tot = l_part + __shfl_xor(l_part, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  f32x16 o[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) o[m] = f32x16{};
+  float m_used = -INFINITY, l_part = 0.0f;
+
+  // row ids of a tile: validated copy in LDS (bad or missing rows read as zero)
+  auto load_rids = [&](int t0) {
+    if (tid < kTileRows) {
+      const int i = t0 + tid;
+      int32_t v = -1;
+      if (i < r1) {
+        v = rids[i];
+        if (v < 0 || v >= n_rows_pool) {
+          raise_error(err, HS_DEVERR_BAD_ROW);
+          v = -1;
+        }
+      }
+      rid_next[tid] = v;
+    }
+  };
+
+  const float* scale = reinterpret_cast<const float*>(lds + DecLds::kOffScale);
+  for (int t0 = r0; t0 < r1; t0 += kTileRows) {
+    const int n_tile = min(kTileRows, r1 - t0);
+    __syncthreads();  // the previous tile's LDS reads are done
+    load_rids(t0);
+    __syncthreads();
+    {
+      TileRegs<kFp8> tr;
+      gather_load<kFp8>(tr, kv, rid_next);
+      gather_store<kFp8>(tr, lds);
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for rows 32 dh .. +31 and this wave's 32 heads
+    const unsigned char* kp = lds + (32 * dh + col) * DecLds::kKStride + 16 * hf;
+    f32x16 c = {};
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + 32 * s));
+      c = mfma32x32x16(a, qf[s], c);
+      if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound how far reads are hoisted
+    }
+    // nope part times the row's scale, then the rope part accumulates on top
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] *= scale[32 * dh + 8 * (i >> 2) + 4 * hf + (i & 3)];
+#pragma unroll
+    for (int s = 32; s < 36; ++s) {
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + 32 * s));
+      c = mfma32x32x16(a, qf[s], c);
+    }
+    // ---- online softmax: lane owns head `head`; rows 8(i/4) + 4 hf + i%4 of its half
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rr = 32 * dh + 8 * (i >> 2) + 4 * hf + (i & 3);
+      c[i] = rr < n_tile ? c[i] * qk_scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, c[i]);
+    }
+    {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    if (hf == 0) mshare[hg][dh][col] = tmax;
+    __syncthreads();
+    tmax = fmaxf(tmax, mshare[hg][dh ^ 1][col]);  // the tile maximum over both halves
+    if (tmax > m_used + kLazyRescale) {  // same decision in both waves of the head group
+      const float alpha = exp2f(m_used - tmax);
+      l_part *= alpha;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) o[m] *= alpha;
+      m_used = tmax;
+    }
+    bf16x8 pb[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      // masked rows give 0, also before any row was seen (m_used = -inf)
+      const float p = c[i] > -INFINITY ? exp2f(c[i] - m_used) : 0.0f;
+      l_part += p;
+      const float a = scale[32 * dh + 8 * (i >> 2) + 4 * hf + (i & 3)];
+      pb[i >> 3][i & 7] = (__bf16)(p * a);
+    }
+    pshare[hg][dh][0][lane] = __builtin_bit_cast(u32x4, pb[0]);
+    pshare[hg][dh][1][lane] = __builtin_bit_cast(u32x4, pb[1]);
+    __syncthreads();
+    // ---- O^T += V^T P^T over all 64 rows (4 k-steps of 16) for dims 256 dh .. +255
+    const unsigned char* vp =
+        lds + DecLds::kOffVt + (256 * dh + col) * DecLds::kVtStride + 2 * (8 * hf);
+#pragma unroll
+    for (int half_rows = 0; half_rows < 2; ++half_rows) {
+#pragma unroll
+      for (int kap = 0; kap < 2; ++kap) {
+        const bf16x8 bp = half_rows == dh ? pb[kap]
+                                          : __builtin_bit_cast(bf16x8, pshare[hg][half_rows][kap][lane]);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
+              vp + 32 * m * DecLds::kVtStride + 2 * (32 * half_rows + 16 * kap)));
+          o[m] = mfma32x32x16(a, bp, o[m]);
+          if ((m & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  }
+
+  // ---- finish: the row sums of both halves, then output (or split partial)
+  float l_half;
+  {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
+    l_half = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  __syncthreads();
+  if (hf == 0) lshare[hg][dh][col] = l_half;
+  __syncthreads();
+  const float l_tot = l_half + lshare[hg][dh ^ 1][col];
   if (splits == 1) {
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    uint16_t* op = out + ((int64_t)bj * kHeads + head) * kDv;
+    uint16_t* op = out + ((int64_t)bj * kHeads + head) * kDv + 256 * dh;
 #pragma unroll
-    for (int m = 0; m < 32; ++m) {
-      const __bf16 v0 = (__bf16)(o[m][0] * inv), v1 = (__bf16)(o[m][1] * inv);
-      const __bf16 v2 = (__bf16)(o[m][2] * inv), v3 = (__bf16)(o[m][3] * inv);
-      const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
-      const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, v2) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
-      *reinterpret_cast<u32x2*>(op + 16 * m + 4 * g) = u32x2{w0, w1};
-    }
-    if (lse && g == 0) lse[(int64_t)bj * kHeads + head] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const __bf16 v0 = (__bf16)(o[m][4 * g4 + 0] * inv), v1 = (__bf16)(o[m][4 * g4 + 1] * inv);
+        const __bf16 v2 = (__bf16)(o[m][4 * g4 + 2] * inv), v3 = (__bf16)(o[m][4 * g4 + 3] * inv);
+        const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
+        const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, v2) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
+        *reinterpret_cast<u32x2*>(op + 32 * m + 8 * g4 + 4 * hf) = u32x2{w0, w1};
+      }
+    if (lse && hf == 0 && dh == 0)
+      lse[(int64_t)bj * kHeads + head] = (m_used + log2f(l_tot)) * 0.69314718055994531f;
   } else {
     const int64_t part = (int64_t)bj * splits + sp;
-    if (g == 0) {
-      part_ml[(part * kHeads + head) * 2 + 0] = m_run;
+    if (hf == 0 && dh == 0) {
+      part_ml[(part * kHeads + head) * 2 + 0] = m_used;
       part_ml[(part * kHeads + head) * 2 + 1] = l_tot;
     }
     if (r1 > r0) {
-      float* pp = part_o + (part * kHeads + head) * kDv;
+      float* pp = part_o + (part * kHeads + head) * kDv + 256 * dh;
 #pragma unroll
-      for (int m = 0; m < 32; ++m) *reinterpret_cast<f32x4*>(pp + 16 * m + 4 * g) = o[m];
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<f32x4*>(pp + 32 * m + 8 * g4 + 4 * hf) =
+              f32x4{o[m][4 * g4], o[m][4 * g4 + 1], o[m][4 * g4 + 2], o[m][4 * g4 + 3]};
     }
   }
 }
@@ -309,13 +383,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
           part_o + (((int64_t)bj * splits + s) * kHeads + h) * kDv + 128 * qtr + d);
       acc += v * f[s];
     }
-    uint32_t w0, w1;
-    {
-      const __bf16 v0 = (__bf16)(acc[0] * inv), v1 = (__bf16)(acc[1] * inv);
-      const __bf16 v2 = (__bf16)(acc[2] * inv), v3 = (__bf16)(acc[3] * inv);
-      w0 = (uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
-      w1 = (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
-    }
+    const __bf16 v0 = (__bf16)(acc[0] * inv), v1 = (__bf16)(acc[1] * inv);
+    const __bf16 v2 = (__bf16)(acc[2] * inv), v3 = (__bf16)(acc[3] * inv);
+    const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
+    const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
     *reinterpret_cast<u32x2*>(op + d) = u32x2{w0, w1};
   }
   if (lse && qtr == 0) lse[(int64_t)bj * kHeads + h] = (M + log2f(L)) * 0.69314718055994531f;
@@ -326,14 +397,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
 
 using namespace hs;
 
-size_t hs_decode_lds_bytes(int kv_dtype) {
-  return kv_dtype == HS_FP8_E4M3 ? DecodeLds<true>::kTotal : DecodeLds<false>::kTotal;
-}
+size_t hs_decode_lds_bytes(int) { return DecLds::kTotal; }
 
 int hs_choose_splits(const hs_ctx* ctx, int B, int S) {
+  // enough workgroups for one per CU (one workgroup fills a CU's LDS)
   const int nq = B * S;
   const int tiles = (ctx->cfg.topk + kTileRows - 1) / kTileRows;
-  int splits = (512 + nq - 1) / nq;
+  int splits = (256 + nq - 1) / nq;
   if (splits > tiles) splits = tiles;
   if (splits > ctx->lay.splits_cap) splits = ctx->lay.splits_cap;
   if (splits < 1) splits = 1;
@@ -348,18 +418,19 @@ hipError_t hs_launch_decode(const hs_ctx* ctx, int layer, const void* q, const i
   const uint8_t* kv = static_cast<const uint8_t*>(ctx->buf.kv_pool) +
                       (int64_t)layer * n_rows_pool * ctx->row_bytes;
   const float qk_scale_log2 = sm_scale * 1.4426950408889634f;
+  const int xcd_map = (B % 8 == 0) ? 1 : 0;
   const dim3 grid((unsigned)(B * S * splits)), block(kDecThreads);
   if (c.kv_dtype == HS_FP8_E4M3)
-    hipLaunchKernelGGL(sparse_mla_decode_kernel<true>, grid, block, DecodeLds<true>::kTotal, stream,
-                       static_cast<const uint16_t*>(q), row_ids, ctx_lens, S, c.topk,
+    hipLaunchKernelGGL(sparse_mla_decode_kernel<true>, grid, block, DecLds::kTotal, stream,
+                       static_cast<const uint16_t*>(q), row_ids, ctx_lens, B, S, c.topk,
                        c.max_pages_per_req * kBlock, kv, n_rows_pool, qk_scale_log2, splits,
-                       static_cast<uint16_t*>(out), lse, ctx->ws.part_o, ctx->ws.part_ml,
+                       xcd_map, static_cast<uint16_t*>(out), lse, ctx->ws.part_o, ctx->ws.part_ml,
                        ctx->ws.err);
   else
-    hipLaunchKernelGGL(sparse_mla_decode_kernel<false>, grid, block, DecodeLds<false>::kTotal,
-                       stream, static_cast<const uint16_t*>(q), row_ids, ctx_lens, S, c.topk,
+    hipLaunchKernelGGL(sparse_mla_decode_kernel<false>, grid, block, DecLds::kTotal, stream,
+                       static_cast<const uint16_t*>(q), row_ids, ctx_lens, B, S, c.topk,
                        c.max_pages_per_req * kBlock, kv, n_rows_pool, qk_scale_log2, splits,
-                       static_cast<uint16_t*>(out), lse, ctx->ws.part_o, ctx->ws.part_ml,
+                       xcd_map, static_cast<uint16_t*>(out), lse, ctx->ws.part_o, ctx->ws.part_ml,
                        ctx->ws.err);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
@@ -368,12 +439,11 @@ hipError_t hs_launch_decode(const hs_ctx* ctx, int layer, const void* q, const i
   return hipGetLastError();
 }
 
-// Raise the dynamic-LDS limit of the kernels that need more than the default.
+// Raise the dynamic-LDS limit of the decode kernels.
 hipError_t hs_set_kernel_attributes() {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sparse_mla_decode_kernel<true>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     DecodeLds<true>::kTotal);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, DecLds::kTotal);
   if (e != hipSuccess) return e;
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&sparse_mla_decode_kernel<false>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, DecodeLds<false>::kTotal);
+                             hipFuncAttributeMaxDynamicSharedMemorySize, DecLds::kTotal);
 }

@@ -77,27 +77,31 @@ __device__ __forceinline__ float wave_max(float v) {
 // Returns this thread's exclusive prefix; *total gets the block sum.
 template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  static_assert(NT % 64 == 0 && NT <= 4096, "block size");
+  constexpr int kWaves = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o);
+    const int y = __shfl_up(x, o);
     if (lane >= o) x += y;
   }
   if (lane == 63) scratch[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int i = 0; i < NT / 64; ++i) {
-      int t = scratch[i];
-      scratch[i] = acc;
-      acc += t;
+  if (wave == 0) {
+    int t = lane < kWaves ? scratch[lane] : 0;
+    int u = t;
+#pragma unroll
+    for (int o = 1; o < kWaves; o <<= 1) {
+      const int y = __shfl_up(u, o);
+      if (lane >= o) u += y;
     }
-    scratch[NT / 64] = acc;
+    if (lane < kWaves) scratch[lane] = u - t;
+    if (lane == kWaves - 1) scratch[kWaves] = u;
   }
   __syncthreads();
   const int res = scratch[wave] + x - v;
-  *total = scratch[NT / 64];
+  *total = scratch[kWaves];
   __syncthreads();
   return res;
 }

@@ -28,16 +28,61 @@
 namespace hs {
 namespace {
 
+// Key fragment of one 32-token tile for one lane: token (l % 32), 64 FP8 bytes or 128 bf16
+// bytes starting at dim 64 * (l / 32).
+template <bool kFp8>
+struct KeyTile {
+  u32x4 v[kFp8 ? 4 : 8];
+  float scale;
+};
+
+template <bool kFp8>
+__device__ __forceinline__ void load_key_tile(KeyTile<kFp8>& kt, const uint8_t* base, int o, int half) {
+  if constexpr (kFp8) {
+    const u32x4* kp = reinterpret_cast<const u32x4*>(base + o * 128 + 64 * half);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) kt.v[v] = __builtin_nontemporal_load(kp + v);
+    kt.scale = __builtin_nontemporal_load(reinterpret_cast<const float*>(base + 8192 + o * 4));
+  } else {
+    const u32x4* kp = reinterpret_cast<const u32x4*>(base + o * 256 + 128 * half);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) kt.v[v] = __builtin_nontemporal_load(kp + v);
+    kt.scale = 1.0f;
+  }
+}
+
+// B operand of k-step s: dims 64 * half + 8 s .. +8 of the lane's token.
+template <bool kFp8>
+__device__ __forceinline__ bf16x8 key_operand(const KeyTile<kFp8>& kt, int s) {
+  if constexpr (kFp8) return e4m3x8_to_bf16(kt.v[s / 2][(s % 2) * 2], kt.v[s / 2][(s % 2) * 2 + 1]);
+  else return as_bf16x8(kt.v[s]);
+}
+
+// Queries handled by one wave: two at most, so that Q (32 VGPRs per query), a three-tile
+// prefetch ring and the accumulators fit two waves per SIMD.
+template <int S>
+struct SweepShape {
+  static constexpr int kQpw = S < 2 ? S : 2;
+  static constexpr int kGroups = (S + kQpw - 1) / kQpw;
+  static constexpr int kThreads = 256 * kGroups;
+};
+
 template <int S, bool kFp8>
-__global__ __launch_bounds__(256) void index_score_kernel(
+__global__ __launch_bounds__(SweepShape<S>::kThreads) void index_score_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const int32_t* __restrict__ ctx_lens, const uint8_t* __restrict__ idx_pool,
     const int32_t* __restrict__ idx_block_table, int max_pages, int64_t num_idx_blocks, int B,
     float* __restrict__ scores, int64_t lmax, uint32_t* __restrict__ hist,
     int32_t* __restrict__ err) {
+  using Shape = SweepShape<S>;
+  constexpr int kQpw = Shape::kQpw;
+  constexpr int kThreads = Shape::kThreads;
   constexpr int kBlkBytes = kFp8 ? kIdxFp8Block : kIdxBf16Block;
-  // 16-bit LDS counters, two bins per word: one workgroup sees at most 2,048 tokens.
+  constexpr int kRing = 3;  // tiles in flight per wave (current + 2 ahead)
+  // 16-bit LDS counters, two bins per word: one workgroup sees at most 4,096 tokens.
   __shared__ uint32_t lhist[S][kHistBins / 2];
+  __shared__ __align__(16) float lw[S][kIdxHeads];  // half the head weights (see epilogue)
+  __shared__ int32_t lblk[kPagesPerItem];
 
   const int b = blockIdx.x % B;
   const int item = blockIdx.x / B;
@@ -51,78 +96,106 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   if (p_begin >= n_pages) return;
   const int p_end = min(n_pages, p_begin + kPagesPerItem);
 
-  for (int i = threadIdx.x; i < S * kHistBins / 2; i += 256) (&lhist[0][0])[i] = 0;
+  for (int i = threadIdx.x; i < S * kHistBins / 2; i += kThreads) (&lhist[0][0])[i] = 0;
+  if (threadIdx.x < S * kIdxHeads)
+    (&lw[0][0])[threadIdx.x] = 0.5f * w[b * S * kIdxHeads + threadIdx.x];
+  if (threadIdx.x < kPagesPerItem) {
+    const int p = p_begin + threadIdx.x;
+    int32_t blk = -1;
+    if (p < p_end) {
+      blk = idx_block_table[(int64_t)b * max_pages + p];
+      if (blk < 0 || blk >= num_idx_blocks) {
+        raise_error(err, HS_DEVERR_BAD_BLOCK);
+        blk = -1;
+      }
+    }
+    lblk[threadIdx.x] = blk;
+  }
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int stream = wave & 3, group = wave >> 2;
+  const int j0 = group * kQpw;
   const int half = lane >> 5, col = lane & 31;
 
   // A operand: Q[j][head = col][dims 64*half + 8*s .. +8] for k-step s.
-  bf16x8 qa[S][8];
+  bf16x8 qa[kQpw][8];
 #pragma unroll
-  for (int j = 0; j < S; ++j) {
+  for (int jj = 0; jj < kQpw; ++jj) {
+    const int j = min(j0 + jj, S - 1);
     const uint16_t* qp = q_idx + ((int64_t)(b * S + j) * kIdxHeads + col) * kIdxDim + 64 * half;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qa[j][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 8 * s));
+    for (int s = 0; s < 8; ++s) qa[jj][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 8 * s));
   }
-  // Weights of the 16 head rows this lane's accumulator holds.
-  float wr[S][16];
-#pragma unroll
-  for (int j = 0; j < S; ++j)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) wr[j][i] = w[(b * S + j) * kIdxHeads + 8 * (i / 4) + 4 * half + (i % 4)];
   __syncthreads();
 
-  for (int p = p_begin + wave; p < p_end; p += 4) {
-    const int blk = idx_block_table[(int64_t)b * max_pages + p];
-    if (blk < 0 || blk >= num_idx_blocks) {
-      if (lane == 0) raise_error(err, HS_DEVERR_BAD_BLOCK);
-      continue;
-    }
-    const uint8_t* base = idx_pool + (int64_t)blk * kBlkBytes;
+  // Each wave walks a fixed number of tiles: tile k is half (k & 1) of page
+  // p_begin + stream + 4 * (k >> 1).  Tiles past the workgroup's pages (or on a bad block) read
+  // block 0 and are masked, so there are no branches around the loads and the prefetch ring
+  // stays in flight.
+  constexpr int kTilesPerWave = 2 * kPagesPerItem / 4;
+  auto tile_src = [&](int k, int& t0) -> const uint8_t* {
+    const int rel = stream + 4 * (k >> 1);
+    const int32_t blk = lblk[rel];
+    t0 = blk >= 0 ? (p_begin + rel) * kBlock + (k & 1) * 32 : INT32_MAX / 2;
+    return idx_pool + (int64_t)(blk >= 0 ? blk : 0) * kBlkBytes;
+  };
+
+  KeyTile<kFp8> ring[kRing];
+  int ring_t0[kRing];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int o = tt * 32 + col;
-      const int t = p * kBlock + o;
-      bf16x8 kb[8];
-      float scale = 1.0f;
-      if constexpr (kFp8) {
-        const u32x4* kp = reinterpret_cast<const u32x4*>(base + o * 128 + 64 * half);
-        u32x4 raw[4];
+  for (int u = 0; u < kRing - 1; ++u)
+    load_key_tile<kFp8>(ring[u], tile_src(u, ring_t0[u]), (u & 1) * 32 + col, half);
+  for (int k0 = 0; k0 < kTilesPerWave; k0 += kRing) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) raw[v] = kp[v];
-        scale = *reinterpret_cast<const float*>(base + 8192 + o * 4);
+    for (int u = 0; u < kRing; ++u) {
+      const int k = k0 + u;
+      if (k < kTilesPerWave) {  // uniform; only the last round of a ragged ring is partial
+        const int un = (u + kRing - 1) % kRing;
+        const int kn = min(k + kRing - 1, kTilesPerWave - 1);
+        load_key_tile<kFp8>(ring[un], tile_src(kn, ring_t0[un]), (kn & 1) * 32 + col, half);
+        const int t = ring_t0[u] + col;
+        f32x16 acc[kQpw];
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-          kb[s] = e4m3x8_to_bf16(raw[s / 2][(s % 2) * 2], raw[s / 2][(s % 2) * 2 + 1]);
-      } else {
-        const u32x4* kp = reinterpret_cast<const u32x4*>(base + o * 256 + 128 * half);
+        for (int jj = 0; jj < kQpw; ++jj) acc[jj] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < 8; ++s) kb[s] = as_bf16x8(kp[s]);
-      }
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 kb = key_operand<kFp8>(ring[u], s);
 #pragma unroll
-      for (int j = 0; j < S; ++j) {
-        f32x16 acc = {};
+          for (int jj = 0; jj < kQpw; ++jj) acc[jj] = mfma32x32x16(qa[jj][s], kb, acc[jj]);
+        }
 #pragma unroll
-        for (int s = 0; s < 8; ++s) acc = mfma32x32x16(qa[j][s], kb[s], acc);
-        float part = 0.0f;
+        for (int jj = 0; jj < kQpw; ++jj) {
+          const int j = j0 + jj;
+          if (j >= S) break;
+          // w * max(c, 0) == (w / 2) * (c + |c|): both factors are exact power-of-two
+          // rescalings, so the products round identically; c + |c| needs no NaN canonicalising
+          float part = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) part += wr[j][i] * fmaxf(acc[i], 0.0f);
-        // add the other half's 16 heads of the same token (lane l ^ 32)
-        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
-                                                   false, false);
-        const float total = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * scale;
-        // scores are >= 0: clearing the sign bit maps -0 to +0
-        const uint32_t bits = __float_as_uint(total) & 0x7fffffffu;
-        if (half == 0 && t < L - S + 1 + j) {
-          scores[(int64_t)(b * S + j) * lmax + t] = __uint_as_float(bits);
-          const uint32_t bin = bits >> kHistShift;
-          atomicAdd(&lhist[j][bin >> 1], 1u << (16 * (bin & 1)));
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 wv = *reinterpret_cast<const f32x4*>(&lw[j][8 * g4 + 4 * half]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float c = acc[jj][4 * g4 + i];
+              part = __builtin_fmaf(wv[i], c + __builtin_fabsf(c), part);
+            }
+          }
+          // add the other half's 16 heads of the same token (lane l ^ 32)
+          auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
+                                                     false, false);
+          const float total = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * ring[u].scale;
+          // scores are >= 0: clearing the sign bit maps -0 to +0
+          const uint32_t bits = __float_as_uint(total) & 0x7fffffffu;
+          if (half == 0 && t < L - S + 1 + j) {
+            scores[(int64_t)(b * S + j) * lmax + t] = __uint_as_float(bits);
+            const uint32_t bin = bits >> kHistShift;
+            atomicAdd(&lhist[j][bin >> 1], 1u << (16 * (bin & 1)));
+          }
         }
       }
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < S * kHistBins / 2; i += 256) {
+  for (int i = threadIdx.x; i < S * kHistBins / 2; i += kThreads) {
     const uint32_t v = (&lhist[0][0])[i];
     if (v == 0) continue;
     const int j = i / (kHistBins / 2), pair = i % (kHistBins / 2);
@@ -220,23 +293,37 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     // ---- fast path: one pass, bin beta collected on chip
     if (tid == 0) sh.misc[2] = 0;
     __syncthreads();
-    for (int c = 0; c < n_chunks; ++c) {
-      const int t = c * kSelThreads + tid;
-      uint32_t key = 0;
-      if (t < Lj) key = __float_as_uint(sc[t]);
-      const int bin = t < Lj ? (int)(key >> kHistShift) : -1;
-      const uint64_t m = __ballot(bin > beta);
-      if (lane == 0) {
-        const int word = (c * kSelThreads + wave * 64) / 32;
-        bm[word] = (uint32_t)m;
-        bm[word + 1] = (uint32_t)(m >> 32);
+    // 8 chunks per round: all loads of a round are in flight together
+    constexpr int kPer = 8;
+    for (int c0 = 0; c0 < n_chunks; c0 += kPer) {
+      uint32_t keys[kPer];
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const int t = (c0 + e) * kSelThreads + tid;
+        keys[e] = t < Lj ? __float_as_uint(__builtin_nontemporal_load(sc + t)) : 0u;
       }
-      if (bin == beta) {
-        const int pos = atomicAdd(&sh.misc[2], 1);
-        if (pos < cand_cap) cand[pos] = ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)t);
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const int c = c0 + e;
+        if (c < n_chunks) {
+          const int t = c * kSelThreads + tid;
+          const int bin = t < Lj ? (int)(keys[e] >> kHistShift) : -1;
+          const uint64_t m = __ballot(bin > beta);
+          if (lane == 0) {
+            const int word = (c * kSelThreads + wave * 64) / 32;
+            bm[word] = (uint32_t)m;
+            bm[word + 1] = (uint32_t)(m >> 32);
+          }
+          if (bin == beta) {
+            const int pos = atomicAdd(&sh.misc[2], 1);
+            if (pos < cand_cap) cand[pos] = ((uint64_t)keys[e] << 32) | (uint32_t)(~(uint32_t)t);
+          }
+        }
       }
     }
-    __threadfence();  // bitmap words are complete in L2 before the atomics below
+    // every reader is in this workgroup: the barrier's workgroup-scope release/acquire orders
+    // the word stores before the atomics below (no device-scope fence, which would write
+    // back the XCD's L2)
     __syncthreads();
     const int n = min(sh.misc[2], cand_cap);
     if (tid == 0 && n != cnt_beta) raise_error(err, HS_DEVERR_TOPK_COUNT);
@@ -310,10 +397,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
       }
     }
   }
-  __threadfence();
   __syncthreads();
 
-  // ---- emission in ascending token order
+  // ---- emission in ascending token order (words read at device scope: the atomics above
+  // were performed in L2)
   const int n_words = (Lj + 31) / 32;
   const int per = (n_words + kSelThreads - 1) / kSelThreads;
   const int w0 = tid * per, w1 = min(n_words, w0 + per);
@@ -339,7 +426,7 @@ hipError_t launch_scores(const hs_ctx* ctx, const void* q_idx, const float* w,
                          const int32_t* ctx_lens, int B, hipStream_t stream) {
   const hs_config& c = ctx->cfg;
   const int items = (c.max_pages_per_req + kPagesPerItem - 1) / kPagesPerItem;
-  dim3 grid((unsigned)(B * items)), block(256);
+  dim3 grid((unsigned)(B * items)), block(SweepShape<S>::kThreads);
   hipLaunchKernelGGL((index_score_kernel<S, kFp8>), grid, block, 0, stream,
                      static_cast<const uint16_t*>(q_idx), w, ctx_lens,
                      static_cast<const uint8_t*>(ctx->buf.idx_pool), ctx->buf.idx_block_table,

@@ -28,7 +28,7 @@ constexpr int kMaxHot = 16384;
 // a non-negative fp32), histogrammed by the score sweep itself.
 constexpr int kHistBins = 4096;
 constexpr int kHistShift = 19;
-constexpr int kPagesPerItem = 32;      // pages scored by one sweep workgroup (2,048 tokens)
+constexpr int kPagesPerItem = 64;      // pages scored by one sweep workgroup (4,096 tokens)
 constexpr int kDefaultCandCap = 4096;  // on-chip candidates of the threshold bin
 
 // Decode split-K.

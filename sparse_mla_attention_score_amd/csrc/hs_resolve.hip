@@ -28,6 +28,20 @@ namespace hs {
 namespace {
 
 constexpr int kResThreads = 1024;
+constexpr int kPerU = kMaxUnion / kResThreads;  // union entries per thread, at most
+constexpr int kPerH = kMaxHot / kResThreads;    // hot slots per thread, at most
+
+// Number of entries of the ascending list a[0..n) that are < x, or <= x when or_equal.
+__device__ __forceinline__ int count_below(const int32_t* a, int n, int32_t x, bool or_equal) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const int32_t v = a[mid];
+    if (v < x || (or_equal && v == x)) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
 
 __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     const int32_t* __restrict__ topk, const int32_t* __restrict__ ctx_lens, int S, int K,
@@ -40,8 +54,9 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     uint8_t* __restrict__ kv_pool, int n_layers, int row_bytes, int union_cap,
     int32_t* __restrict__ row_ids, int32_t* __restrict__ stats, int32_t* __restrict__ err) {
   extern __shared__ __align__(16) unsigned char dyn[];
-  // union_cap (power of two >= S*K) entries each: sorted union, per-token row (or miss code),
-  // miss source row, miss destination (victim slot, then its row); then H slot flags.
+  // union_cap (a power of two, >= S*K and >= 1024) entries each: sorted union U, per-token
+  // row or miss code `cls` (also the staging area of the input lists), miss source row,
+  // miss destination (victim slot, then its row); then H slot flags.
   int32_t* U = reinterpret_cast<int32_t*>(dyn);
   int32_t* cls = U + union_cap;
   int32_t* msrc = cls + union_cap;
@@ -71,25 +86,39 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     return;
   }
 
-  // ---- 1. sorted union of the S lists (tokens outside [0, Lb) are dropped and flagged)
+  // ---- 1. sorted union of the S ascending lists.  Invalid entries (-1 padding, tokens
+  // outside [0, Lb)) become INT32_MAX and sort last.  The lists are staged in `cls`.
   const int n_in = S * K;
+  if (tid < 8) cnt[tid] = 0;
   for (int i = tid; i < union_cap; i += kResThreads) {
     int32_t t = i < n_in ? tk[i] : -1;
     if (t >= Lb) {
       raise_error(err, HS_DEVERR_BAD_ROW);
       t = -1;
     }
-    U[i] = t < 0 ? INT32_MAX : t;
+    cls[i] = t < 0 ? INT32_MAX : t;
   }
   for (int i = tid; i < H; i += kResThreads) flag[i] = 0;
-  if (tid == 0) cnt[1] = S > 1 ? 1 : 0;
   __syncthreads();
-  if (S == 1) {  // one list is ascending by contract; sort it anyway if it is not
-    for (int i = tid + 1; i < union_cap; i += kResThreads)
-      if (U[i - 1] > U[i]) cnt[1] = 1;
+  for (int i = tid; i < n_in; i += kResThreads)
+    if (i % K != 0 && cls[i - 1] > cls[i]) cnt[7] = 1;  // a list is not ascending
+  __syncthreads();
+  if (cnt[7] == 0) {
+    // stable merge by rank: entry k of list j lands at k plus, for every other list, the
+    // number of its entries before it (ties go to the lower list)
+    for (int i = tid; i < n_in; i += kResThreads) {
+      const int j = i / K, k = i - j * K;
+      const int32_t x = cls[i];
+      int pos = k;
+      for (int jj = 0; jj < S; ++jj)
+        if (jj != j) pos += count_below(cls + jj * K, K, x, jj < j);
+      U[pos] = x;
+    }
+    for (int i = n_in + tid; i < union_cap; i += kResThreads) U[i] = INT32_MAX;
     __syncthreads();
-  }
-  if (cnt[1]) {
+  } else {  // out-of-contract input: sort the concatenation
+    for (int i = tid; i < union_cap; i += kResThreads) U[i] = cls[i];
+    __syncthreads();
     for (int k = 2; k <= union_cap; k <<= 1) {
       for (int jj = k >> 1; jj > 0; jj >>= 1) {
         for (int i = tid; i < union_cap; i += kResThreads) {
@@ -107,184 +136,201 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
       }
     }
   }
-  // compaction of distinct valid entries (a single list is already sorted and distinct)
-  int nU = 0;
+  // in-place compaction of distinct valid entries; each thread owns a contiguous run
+  int nU;
   {
-    int carry = 0;
-    for (int base = 0; base < union_cap; base += kResThreads) {
-      const int i = base + tid;
-      const int32_t v = U[i];
-      const bool keep = v != INT32_MAX && (i == 0 || U[i - 1] != v);
-      int tot;
-      const int pos = carry + block_exclusive_scan<kResThreads>(keep ? 1 : 0, scan, &tot);
-      if (keep) cls[pos] = v;
-      carry += tot;
+    const int per = union_cap / kResThreads;
+    const int i0 = tid * per;
+    int32_t v[kPerU];
+    int32_t prev = i0 > 0 ? U[i0 - 1] : INT32_MIN;
+    int keep = 0;
+#pragma unroll
+    for (int e = 0; e < kPerU; ++e) {
+      v[e] = INT32_MAX;
+      if (e < per) v[e] = U[i0 + e];
     }
-    nU = carry;
-    __syncthreads();
-    for (int i = tid; i < nU; i += kResThreads) U[i] = cls[i];
+#pragma unroll
+    for (int e = 0; e < kPerU; ++e) {
+      const int32_t pe = e == 0 ? prev : v[e - 1];
+      if (e < per && v[e] != INT32_MAX && v[e] != pe) ++keep;
+    }
+    int tot;
+    int pos = block_exclusive_scan<kResThreads>(keep, scan, &tot);  // all reads done before
+#pragma unroll
+    for (int e = 0; e < kPerU; ++e) {
+      const int32_t pe = e == 0 ? prev : v[e - 1];
+      if (e < per && v[e] != INT32_MAX && v[e] != pe) U[pos++] = v[e];
+    }
+    nU = tot;
     __syncthreads();
   }
 
-  // ---- 2. classify: resident / hot hit (stamp) / miss
-  int n_res = 0, n_hit = 0, n_miss = 0;
+  // ---- 2. classify: resident / hot hit (stamped) / miss.  Thread owns a contiguous run.
+  int n_miss;
   {
-    int carry = 0, res_c = 0, hit_c = 0;
-    for (int base = 0; base < nU; base += kResThreads) {
-      const int i = base + tid;
-      int is_miss = 0, is_res = 0, is_hit = 0;
-      if (i < nU) {
-        const int32_t u = U[i];
-        const int page = u >> 6;
-        const int32_t blk = bt[page];
-        int32_t c = -1;
-        if (blk >= 0) {
-          if (blk < num_gpu_blocks) c = blk * kBlock + (u & 63);
-          else raise_error(err, HS_DEVERR_BAD_BLOCK);
-          is_res = 1;
-        } else {
-          const int32_t s = t2s[u];
-          if (s >= 0 && s < H) {
-            flag[s] = 1;
-            st_stamp[s] = step;
-            const int32_t hb = hot[s >> 6];
-            if (hb >= 0 && hb < num_gpu_blocks) c = hb * kBlock + (s & 63);
-            else raise_error(err, HS_DEVERR_BAD_BLOCK);
-            is_hit = 1;
-          } else {
-            const int32_t hb = hbt[page];
-            if (hb < 0) raise_error(err, HS_DEVERR_NO_HOST_COPY);
-            else if (hb >= num_host_blocks) raise_error(err, HS_DEVERR_BAD_BLOCK);
-            else is_miss = 1;
-          }
-        }
-        cls[i] = c;
+    const int per = (nU + kResThreads - 1) / kResThreads;  // <= kPerU
+    const int i0 = tid * per;
+    int32_t u[kPerU], blk[kPerU], slot[kPerU], hb[kPerU];
+    int n_res = 0, n_hit = 0, my_miss = 0;
+#pragma unroll
+    for (int e = 0; e < kPerU; ++e) {
+      u[e] = -1;
+      blk[e] = -1;
+      if (e < per && i0 + e < nU) {
+        u[e] = U[i0 + e];
+        blk[e] = bt[u[e] >> 6];
       }
-      int tot;
-      const int rank = carry + block_exclusive_scan<kResThreads>(is_miss, scan, &tot);
-      if (is_miss) {
-        cls[i] = -2 - rank;                           // miss code carries its rank
-        msrc[rank] = hbt[U[i] >> 6] * kBlock + (U[i] & 63);
-      }
-      carry += tot;
-      int t2;
-      block_exclusive_scan<kResThreads>(is_res, scan, &t2);
-      res_c += t2;
-      block_exclusive_scan<kResThreads>(is_hit, scan, &t2);
-      hit_c += t2;
     }
-    n_miss = carry;
-    n_res = res_c;
-    n_hit = hit_c;
+#pragma unroll
+    for (int e = 0; e < kPerU; ++e) {
+      slot[e] = -1;
+      if (u[e] >= 0 && blk[e] < 0) slot[e] = t2s[u[e]];
+    }
+#pragma unroll
+    for (int e = 0; e < kPerU; ++e) {
+      hb[e] = -1;
+      if (u[e] >= 0 && blk[e] < 0 && !(slot[e] >= 0 && slot[e] < H)) hb[e] = hbt[u[e] >> 6];
+    }
+#pragma unroll
+    for (int e = 0; e < kPerU; ++e) {
+      if (u[e] < 0) continue;
+      int32_t c = -1;
+      if (blk[e] >= 0) {
+        if (blk[e] < num_gpu_blocks) c = blk[e] * kBlock + (u[e] & 63);
+        else raise_error(err, HS_DEVERR_BAD_BLOCK);
+        ++n_res;
+      } else if (slot[e] >= 0 && slot[e] < H) {
+        const int32_t s = slot[e];
+        flag[s] = 1;
+        st_stamp[s] = step;
+        const int32_t h = hot[s >> 6];
+        if (h >= 0 && h < num_gpu_blocks) c = h * kBlock + (s & 63);
+        else raise_error(err, HS_DEVERR_BAD_BLOCK);
+        ++n_hit;
+      } else if (hb[e] < 0) {
+        raise_error(err, HS_DEVERR_NO_HOST_COPY);
+      } else if (hb[e] >= num_host_blocks) {
+        raise_error(err, HS_DEVERR_BAD_BLOCK);
+      } else {
+        c = -2;  // miss; rank assigned below
+        ++my_miss;
+      }
+      cls[i0 + e] = c;
+    }
+    atomicAdd(&cnt[0], n_res);
+    atomicAdd(&cnt[1], n_hit);
+    int tot;
+    int rank = block_exclusive_scan<kResThreads>(my_miss, scan, &tot);
+#pragma unroll
+    for (int e = 0; e < kPerU; ++e) {
+      if (u[e] >= 0 && cls[i0 + e] == -2) {
+        cls[i0 + e] = -2 - rank;  // miss code carries its rank (ascending token order)
+        msrc[rank] = hb[e] * kBlock + (u[e] & 63);
+        ++rank;
+      }
+    }
+    n_miss = tot;
   }
-  __syncthreads();
 
-  // ---- 3. victims: the first n_miss untouched slots of the recency list
-  int n_assign = 0;
+  // ---- 3. victims: the first n_miss untouched slots of the recency list, then the new list
+  // (untouched slots in old order, then every touched slot in ascending slot order)
+  const int perH = (H + kResThreads - 1) / kResThreads;  // <= kPerH
+  const int h0 = tid * perH;
+  int32_t ord[kPerH];
+  int n_assign;
   {
-    int carry = 0;
-    for (int base = 0; base < H; base += kResThreads) {
-      const int i = base + tid;
-      int32_t s = -1;
-      int cand = 0;
-      if (i < H) {
-        s = order_cur[i];
-        cand = (s >= 0 && s < H && !flag[s]) ? 1 : 0;
-      }
-      int tot;
-      const int r = carry + block_exclusive_scan<kResThreads>(cand, scan, &tot);
-      if (cand && r < n_miss) mdst[r] = s;
-      carry += tot;
+    int my_cand = 0;
+#pragma unroll
+    for (int e = 0; e < kPerH; ++e) {
+      ord[e] = -1;
+      if (e < perH && h0 + e < H) ord[e] = order_cur[h0 + e];
     }
-    n_assign = min(n_miss, carry);
+#pragma unroll
+    for (int e = 0; e < kPerH; ++e)
+      if (ord[e] >= 0 && ord[e] < H && !flag[ord[e]]) ++my_cand;
+    int tot;
+    int r = block_exclusive_scan<kResThreads>(my_cand, scan, &tot);
+#pragma unroll
+    for (int e = 0; e < kPerH; ++e) {
+      if (ord[e] >= 0 && ord[e] < H && !flag[ord[e]]) {
+        if (r < n_miss) mdst[r] = ord[e];
+        ++r;
+      }
+    }
+    n_assign = min(n_miss, tot);
     if (tid == 0 && n_assign < n_miss) raise_error(err, HS_DEVERR_HOT_FULL);
   }
   __syncthreads();
   for (int r = tid; r < n_assign; r += kResThreads) flag[mdst[r]] = 1;
   __syncthreads();
-  // new recency list: untouched in old order, then touched in ascending slot order
   {
-    int carry = 0;
-    for (int base = 0; base < H; base += kResThreads) {
-      const int i = base + tid;
-      int32_t s = -1;
-      int keep = 0;
-      if (i < H) {
-        s = order_cur[i];
-        keep = (s >= 0 && s < H && !flag[s]) ? 1 : 0;
-      }
-      int tot;
-      const int r = carry + block_exclusive_scan<kResThreads>(keep, scan, &tot);
-      if (keep) order_next[r] = s;
-      carry += tot;
+    int keep = 0, touched = 0;
+#pragma unroll
+    for (int e = 0; e < kPerH; ++e) {
+      if (ord[e] >= 0 && ord[e] < H && !flag[ord[e]]) ++keep;
+      if (e < perH && h0 + e < H && flag[h0 + e]) ++touched;
     }
-    const int n_untouched = carry;
-    carry = 0;
-    for (int base = 0; base < H; base += kResThreads) {
-      const int s = base + tid;
-      const int touched = (s < H && flag[s]) ? 1 : 0;
-      int tot;
-      const int r = carry + block_exclusive_scan<kResThreads>(touched, scan, &tot);
-      if (touched) order_next[n_untouched + r] = s;
-      carry += tot;
+    int n_keep, n_touch;
+    int pk = block_exclusive_scan<kResThreads>(keep, scan, &n_keep);
+    int pt = block_exclusive_scan<kResThreads>(touched, scan, &n_touch);
+#pragma unroll
+    for (int e = 0; e < kPerH; ++e) {
+      if (ord[e] >= 0 && ord[e] < H && !flag[ord[e]]) order_next[pk++] = ord[e];
+      if (e < perH && h0 + e < H && flag[h0 + e]) order_next[n_keep + pt++] = h0 + e;
     }
   }
 
-  // ---- 4. assign victims to misses (ascending token order = rank order)
-  int new_fills = 0;
-  {
-    int fills = 0;
-    for (int i = tid; i < nU; i += kResThreads) {
-      const int32_t c = cls[i];
-      if (c > -2) continue;
-      const int r = -2 - c;
-      if (r >= n_assign) {
-        cls[i] = -1;
-        continue;
-      }
-      const int32_t u = U[i];
-      const int32_t v = mdst[r];
-      const int32_t old = st_tok[v];
-      if (old >= 0 && old < lmax) t2s[old] = -1;
-      else ++fills;
-      st_tok[v] = u;
-      st_stamp[v] = step;
-      t2s[u] = v;
-      const int32_t hb = hot[v >> 6];
-      int32_t row = -1;
-      if (hb >= 0 && hb < num_gpu_blocks) row = hb * kBlock + (v & 63);
-      else raise_error(err, HS_DEVERR_BAD_BLOCK);
-      cls[i] = row;
-      mdst[r] = row;
+  // ---- 4. assign victims to misses (rank order = ascending token order)
+  int fills = 0;
+  for (int i = tid; i < nU; i += kResThreads) {
+    const int32_t c = cls[i];
+    if (c > -2) continue;
+    const int r = -2 - c;
+    if (r >= n_assign) {
+      cls[i] = -1;
+      continue;
     }
-    if (tid == 0) cnt[0] = 0;
-    __syncthreads();
-    atomicAdd(&cnt[0], fills);
-    __syncthreads();
-    new_fills = cnt[0];
+    const int32_t u = U[i];
+    const int32_t v = mdst[r];
+    const int32_t old = st_tok[v];
+    if (old >= 0 && old < lmax) t2s[old] = -1;
+    else ++fills;
+    st_tok[v] = u;
+    st_stamp[v] = step;
+    t2s[u] = v;
+    const int32_t h = hot[v >> 6];
+    int32_t row = -1;
+    if (h >= 0 && h < num_gpu_blocks) row = h * kBlock + (v & 63);
+    else raise_error(err, HS_DEVERR_BAD_BLOCK);
+    cls[i] = row;
+    mdst[r] = row;
   }
+  atomicAdd(&cnt[2], fills);
+  __syncthreads();
 
-  // ---- 5. single-row copies from the pinned host pool, all layers
+  // ---- 5. single-row copies from the pinned host pool, all layers, 16 bytes per thread,
+  // eight loads in flight per thread
   {
     const int chunks = row_bytes / 16;
+    const int per_row = n_layers * chunks;
     const int64_t gpu_layer = num_gpu_blocks * kBlock * (int64_t)row_bytes;
     const int64_t host_layer = num_host_blocks * kBlock * (int64_t)row_bytes;
-    const int64_t total = (int64_t)n_assign * n_layers * chunks;
-    constexpr int kBatch = 4;
-    for (int64_t base = tid; base < total; base += (int64_t)kResThreads * kBatch) {
+    const int total = n_assign * per_row;
+    constexpr int kBatch = 8;
+    for (int base = tid; base < total; base += kResThreads * kBatch) {
       u32x4 v[kBatch];
       int64_t dst[kBatch];
 #pragma unroll
       for (int e = 0; e < kBatch; ++e) {
-        const int64_t idx = base + (int64_t)e * kResThreads;
+        const int idx = base + e * kResThreads;
         dst[e] = -1;
         if (idx < total) {
-          const int r = (int)(idx / (n_layers * chunks));
-          const int rem = (int)(idx % (n_layers * chunks));
-          const int layer = rem / chunks, q = rem % chunks;
+          const int r = idx / per_row;
+          const int rem = idx - r * per_row;
+          const int layer = rem / chunks, q = rem - layer * chunks;
           if (mdst[r] >= 0) {
             const int64_t so = layer * host_layer + (int64_t)msrc[r] * row_bytes + q * 16;
-            v[e] = *reinterpret_cast<const u32x4*>(host_pool + so);
+            v[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(host_pool + so));
             dst[e] = layer * gpu_layer + (int64_t)mdst[r] * row_bytes + q * 16;
           }
         }
@@ -294,30 +340,21 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
         if (dst[e] >= 0) *reinterpret_cast<u32x4*>(kv_pool + dst[e]) = v[e];
     }
   }
-  __syncthreads();
 
   // ---- 6. row ids, positionally
-  for (int i = tid; i < S * K; i += kResThreads) {
+  for (int i = tid; i < n_in; i += kResThreads) {
     const int32_t t = tk[i];
     int32_t r = -1;
-    if (t >= 0 && t < Lb) {
-      int lo = 0, hi = nU - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (U[mid] < t) lo = mid + 1;
-        else hi = mid;
-      }
-      r = cls[lo];
-    }
+    if (t >= 0 && t < Lb && nU > 0) r = cls[count_below(U, nU, t, false)];
     out[i] = r;
   }
   if (tid == 0) {
-    const int used = min(H, req_used[b] + new_fills);
+    const int used = min(H, req_used[b] + cnt[2]);
     req_used[b] = used;
     req_step[b] = step + 1;
     if (stats) {
-      stats[b * 4 + 0] = n_res;
-      stats[b * 4 + 1] = n_hit;
+      stats[b * 4 + 0] = cnt[0];
+      stats[b * 4 + 1] = cnt[1];
       stats[b * 4 + 2] = n_miss;
       stats[b * 4 + 3] = (used + kBlock - 1) / kBlock;
     }
