@@ -109,6 +109,9 @@ hs_status hs::compute_layout(const hs_config& c, Layout* L) {
   L->off_scores = take(B * S * L->lmax * 4);
   L->off_hist = take(B * S * kHistBins * 4);
   L->off_bitmap = take(B * S * L->bm_words * 4);
+  L->off_miss_src = take(B * S * c.topk * 4);
+  L->off_miss_dst = take(B * S * c.topk * 4);
+  L->off_miss_cnt = take(B * 4);
   L->off_part_o = take(B * S * cap * kHeads * kDv * 4);
   L->off_part_ml = take(B * S * cap * kHeads * 2 * 4);
   L->total = off;
@@ -234,6 +237,9 @@ hs_status hs_bind(hs_ctx* ctx, const hs_buffers* b) {
   ctx->ws.scores = reinterpret_cast<float*>(w + L.off_scores);
   ctx->ws.hist = reinterpret_cast<uint32_t*>(w + L.off_hist);
   ctx->ws.bitmap = reinterpret_cast<uint32_t*>(w + L.off_bitmap);
+  ctx->ws.miss_src = reinterpret_cast<int32_t*>(w + L.off_miss_src);
+  ctx->ws.miss_dst = reinterpret_cast<int32_t*>(w + L.off_miss_dst);
+  ctx->ws.miss_cnt = reinterpret_cast<int32_t*>(w + L.off_miss_cnt);
   ctx->ws.part_o = reinterpret_cast<float*>(w + L.off_part_o);
   ctx->ws.part_ml = reinterpret_cast<float*>(w + L.off_part_ml);
   ctx->bound = true;

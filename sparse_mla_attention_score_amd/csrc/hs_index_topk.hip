@@ -29,7 +29,8 @@ namespace hs {
 namespace {
 
 // Key fragment of one 32-token tile for one lane: token (l % 32), 64 FP8 bytes or 128 bf16
-// bytes starting at dim 64 * (l / 32).
+// bytes starting at dim 64 * (l / 32).  Plain (cacheable) loads: the waves of the other query
+// group read the same tile right after.
 template <bool kFp8>
 struct KeyTile {
   u32x4 v[kFp8 ? 4 : 8];
@@ -41,12 +42,12 @@ __device__ __forceinline__ void load_key_tile(KeyTile<kFp8>& kt, const uint8_t* 
   if constexpr (kFp8) {
     const u32x4* kp = reinterpret_cast<const u32x4*>(base + o * 128 + 64 * half);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) kt.v[v] = __builtin_nontemporal_load(kp + v);
-    kt.scale = __builtin_nontemporal_load(reinterpret_cast<const float*>(base + 8192 + o * 4));
+    for (int v = 0; v < 4; ++v) kt.v[v] = kp[v];
+    kt.scale = *reinterpret_cast<const float*>(base + 8192 + o * 4);
   } else {
     const u32x4* kp = reinterpret_cast<const u32x4*>(base + o * 256 + 128 * half);
 #pragma unroll
-    for (int v = 0; v < 8; ++v) kt.v[v] = __builtin_nontemporal_load(kp + v);
+    for (int v = 0; v < 8; ++v) kt.v[v] = kp[v];
     kt.scale = 1.0f;
   }
 }
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(SweepShape<S>::kThreads) void index_score_kernel(
   constexpr int kQpw = Shape::kQpw;
   constexpr int kThreads = Shape::kThreads;
   constexpr int kBlkBytes = kFp8 ? kIdxFp8Block : kIdxBf16Block;
-  constexpr int kRing = 3;  // tiles in flight per wave (current + 2 ahead)
+  constexpr int kRing = 4;  // tiles in flight per wave (current + 3 ahead)
   // 16-bit LDS counters, two bins per word: one workgroup sees at most 4,096 tokens.
   __shared__ uint32_t lhist[S][kHistBins / 2];
   __shared__ __align__(16) float lw[S][kIdxHeads];  // half the head weights (see epilogue)

@@ -48,13 +48,17 @@ struct Workspace {
   float* scores;         // [Bmax][Smax][Lmax] indexer scores of one call
   uint32_t* hist;        // [Bmax][Smax][kHistBins] first-digit histogram (kept zero between calls)
   uint32_t* bitmap;      // [Bmax][Smax][bm_words] selected-token bitmap
+  int32_t* miss_src;     // [Bmax][Smax*K] host row of each miss of the last resolve
+  int32_t* miss_dst;     // [Bmax][Smax*K] device row (hot slot) it is copied to
+  int32_t* miss_cnt;     // [Bmax] misses of the last resolve
   float* part_o;         // [Bmax*Smax*splits_cap][64][512] split-K partial outputs
   float* part_ml;        // [Bmax*Smax*splits_cap][64][2] split-K (max, sum) in log2 units
 };
 
 struct Layout {
   size_t off_slot_token, off_slot_stamp, off_lru_order, off_tok2slot, off_req_step, off_req_used,
-      off_err, off_scores, off_hist, off_bitmap, off_part_o, off_part_ml, total;
+      off_err, off_scores, off_hist, off_bitmap, off_miss_src, off_miss_dst, off_miss_cnt,
+      off_part_o, off_part_ml, total;
   int32_t hot_rows;
   int64_t lmax;       // max_pages_per_req * 64
   int64_t bm_words;   // bitmap words per (request, query): lmax rounded up to 1,024, / 32

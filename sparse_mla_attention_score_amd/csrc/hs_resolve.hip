@@ -13,14 +13,15 @@
 // not touch the LRU; victims are the slots untouched in this call in (stamp, slot) order,
 // empty slots first; the i-th miss in ascending token order takes the i-th victim.
 //
-// Implementation: one 1,024-thread workgroup per request.  The S top-K lists are merged into
+// Implementation: one 1,024-thread workgroup per request decides, a second kernel copies.  The S top-K lists are merged into
 // their sorted union on chip (bitonic sort + compaction).  The (stamp, slot) order is kept as
 // an explicit recency list of slots, double-buffered by the parity of the call counter: the
 // victims are the first untouched entries of the old list, and the new list is the untouched
 // entries in old order followed by the touched slots in ascending slot order, which is the
 // (stamp, slot) order after this call.  Every choice is a prefix sum, so the result does not
-// depend on thread timing.  Miss rows are then copied from the mapped host pool by the GPU,
-// 16 bytes per thread, all layers sharing the request's top-K.
+// depend on thread timing.  Each request's miss list then goes to a copy kernel that spreads
+// the rows of the whole batch over the GPU (one request's misses alone cannot fill the host
+// link), reading the mapped host pool directly, all layers sharing the request's top-K.
 #include "hs_device.h"
 #include "hs_internal.h"
 
@@ -50,9 +51,9 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     int64_t num_host_blocks, int max_batch, int32_t* __restrict__ slot_token,
     int32_t* __restrict__ slot_stamp, int32_t* __restrict__ lru_order,
     int32_t* __restrict__ tok2slot, int64_t lmax, int32_t* __restrict__ req_step,
-    int32_t* __restrict__ req_used, const uint8_t* __restrict__ host_pool,
-    uint8_t* __restrict__ kv_pool, int n_layers, int row_bytes, int union_cap,
-    int32_t* __restrict__ row_ids, int32_t* __restrict__ stats, int32_t* __restrict__ err) {
+    int32_t* __restrict__ req_used, int32_t* __restrict__ miss_src, int32_t* __restrict__ miss_dst,
+    int32_t* __restrict__ miss_cnt, int union_cap, int32_t* __restrict__ row_ids,
+    int32_t* __restrict__ stats, int32_t* __restrict__ err) {
   extern __shared__ __align__(16) unsigned char dyn[];
   // union_cap (a power of two, >= S*K and >= 1024) entries each: sorted union U, per-token
   // row or miss code `cls` (also the staging area of the input lists), miss source row,
@@ -81,7 +82,10 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
   int32_t* order_next = lru_order + ((int64_t)((step + 1) & 1) * max_batch + b) * H;
 
   if (Lb < S || Lb > max_pages * kBlock) {
-    if (tid == 0) raise_error(err, HS_DEVERR_SHORT_CONTEXT);
+    if (tid == 0) {
+      raise_error(err, HS_DEVERR_SHORT_CONTEXT);
+      miss_cnt[b] = 0;
+    }
     for (int i = tid; i < S * K; i += kResThreads) out[i] = -1;
     return;
   }
@@ -308,38 +312,12 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
   atomicAdd(&cnt[2], fills);
   __syncthreads();
 
-  // ---- 5. single-row copies from the pinned host pool, all layers, 16 bytes per thread,
-  // eight loads in flight per thread
-  {
-    const int chunks = row_bytes / 16;
-    const int per_row = n_layers * chunks;
-    const int64_t gpu_layer = num_gpu_blocks * kBlock * (int64_t)row_bytes;
-    const int64_t host_layer = num_host_blocks * kBlock * (int64_t)row_bytes;
-    const int total = n_assign * per_row;
-    constexpr int kBatch = 8;
-    for (int base = tid; base < total; base += kResThreads * kBatch) {
-      u32x4 v[kBatch];
-      int64_t dst[kBatch];
-#pragma unroll
-      for (int e = 0; e < kBatch; ++e) {
-        const int idx = base + e * kResThreads;
-        dst[e] = -1;
-        if (idx < total) {
-          const int r = idx / per_row;
-          const int rem = idx - r * per_row;
-          const int layer = rem / chunks, q = rem - layer * chunks;
-          if (mdst[r] >= 0) {
-            const int64_t so = layer * host_layer + (int64_t)msrc[r] * row_bytes + q * 16;
-            v[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(host_pool + so));
-            dst[e] = layer * gpu_layer + (int64_t)mdst[r] * row_bytes + q * 16;
-          }
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < kBatch; ++e)
-        if (dst[e] >= 0) *reinterpret_cast<u32x4*>(kv_pool + dst[e]) = v[e];
-    }
+  // ---- 5. publish the miss list; the copy kernel moves the rows
+  for (int r2 = tid; r2 < n_assign; r2 += kResThreads) {
+    miss_src[(int64_t)b * n_in + r2] = msrc[r2];
+    miss_dst[(int64_t)b * n_in + r2] = mdst[r2];
   }
+  if (tid == 0) miss_cnt[b] = n_assign;
 
   // ---- 6. row ids, positionally
   for (int i = tid; i < n_in; i += kResThreads) {
@@ -358,6 +336,71 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
       stats[b * 4 + 2] = n_miss;
       stats[b * 4 + 3] = (used + kBlock - 1) / kBlock;
     }
+  }
+}
+
+// Single-row copies of every miss of the batch, spread over the whole grid: host row
+// miss_src -> device row miss_dst, for every layer, 16 bytes per work item, eight loads in
+// flight per thread.  Rows whose destination is invalid (-1) are skipped.
+constexpr int kCopyThreads = 256;
+constexpr int kCopyBlocks = 256;
+
+__global__ __launch_bounds__(kCopyThreads) void miss_copy_kernel(
+    const int32_t* __restrict__ miss_src, const int32_t* __restrict__ miss_dst,
+    const int32_t* __restrict__ miss_cnt, int B, int per_req, const uint8_t* __restrict__ host_pool,
+    uint8_t* __restrict__ kv_pool, int n_layers, int row_bytes, int64_t num_gpu_blocks,
+    int64_t num_host_blocks) {
+  __shared__ int scan[kCopyThreads / 64 + 1];
+  // prefix sums of the per-request miss counts (B may exceed the block: chunks with carry)
+  extern __shared__ int req_start[];  // [B + 1]
+  int carry = 0;
+  for (int base = 0; base < B; base += kCopyThreads) {
+    const int i = base + threadIdx.x;
+    const int v = i < B ? min(max(miss_cnt[i], 0), per_req) : 0;
+    int tot;
+    const int x = block_exclusive_scan<kCopyThreads>(v, scan, &tot);
+    if (i < B) req_start[i] = carry + x;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) req_start[B] = carry;
+  __syncthreads();
+  const int chunks = row_bytes / 16;
+  const int per_row = n_layers * chunks;
+  const int64_t total = (int64_t)carry * per_row;
+  const int64_t gpu_layer = num_gpu_blocks * kBlock * (int64_t)row_bytes;
+  const int64_t host_layer = num_host_blocks * kBlock * (int64_t)row_bytes;
+  const int64_t stride = (int64_t)gridDim.x * kCopyThreads;
+  constexpr int kBatch = 8;
+  for (int64_t base = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x; base < total;
+       base += stride * kBatch) {
+    u32x4 v[kBatch];
+    int64_t dst[kBatch];
+#pragma unroll
+    for (int e = 0; e < kBatch; ++e) {
+      const int64_t idx = base + e * stride;
+      dst[e] = -1;
+      if (idx < total) {
+        const int row = (int)(idx / per_row);
+        const int rem = (int)(idx - (int64_t)row * per_row);
+        const int layer = rem / chunks, q = rem - layer * chunks;
+        int lo = 0, hi = B - 1;  // request whose range holds `row`
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (req_start[mid] <= row) lo = mid;
+          else hi = mid - 1;
+        }
+        const int64_t k = (int64_t)lo * per_req + (row - req_start[lo]);
+        const int32_t s = miss_src[k], d = miss_dst[k];
+        if (d >= 0 && d < num_gpu_blocks * kBlock && s >= 0 && s < num_host_blocks * kBlock) {
+          v[e] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(host_pool + layer * host_layer + (int64_t)s * row_bytes + q * 16));
+          dst[e] = layer * gpu_layer + (int64_t)d * row_bytes + q * 16;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kBatch; ++e)
+      if (dst[e] >= 0) *reinterpret_cast<u32x4*>(kv_pool + dst[e]) = v[e];
   }
 }
 
@@ -409,10 +452,15 @@ hipError_t hs_launch_resolve(const hs_ctx* ctx, const int32_t* topk, const int32
                      ctx->buf.hot_blocks, c.max_pages_per_req, H, (int64_t)c.num_gpu_blocks,
                      (int64_t)c.num_host_blocks, c.max_batch, ctx->ws.slot_token,
                      ctx->ws.slot_stamp, ctx->ws.lru_order, ctx->ws.tok2slot, ctx->lay.lmax,
-                     ctx->ws.req_step, ctx->ws.req_used,
+                     ctx->ws.req_step, ctx->ws.req_used, ctx->ws.miss_src, ctx->ws.miss_dst,
+                     ctx->ws.miss_cnt, cap, row_ids, stats, ctx->ws.err);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || c.num_host_blocks == 0) return e;
+  hipLaunchKernelGGL(miss_copy_kernel, dim3(kCopyBlocks), dim3(kCopyThreads), (size_t)(B + 1) * 4,
+                     stream, ctx->ws.miss_src, ctx->ws.miss_dst, ctx->ws.miss_cnt, B, S * c.topk,
                      static_cast<const uint8_t*>(ctx->host_pool_dev),
-                     static_cast<uint8_t*>(ctx->buf.kv_pool), c.n_layers, ctx->row_bytes, cap,
-                     row_ids, stats, ctx->ws.err);
+                     static_cast<uint8_t*>(ctx->buf.kv_pool), c.n_layers, ctx->row_bytes,
+                     (int64_t)c.num_gpu_blocks, (int64_t)c.num_host_blocks);
   return hipGetLastError();
 }
 
