@@ -61,6 +61,7 @@ def main() -> int:
     import synth
     from sparse_mla_attention_score_amd import accounting as acc
     from sparse_mla_attention_score_amd import hisparse as hsb
+    from sparse_mla_attention_score_amd import rocprof_summary as rprof
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -134,6 +135,8 @@ def main() -> int:
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     misses = []
+    # per-kernel HIP events, recorded by the library on the stream each kernel is launched on
+    ctx.kernel_timing(True)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_host = time.perf_counter()
@@ -144,6 +147,10 @@ def main() -> int:
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
     elapsed_ms = start.elapsed_time(end)
+    ktimes = ctx.kernel_times()
+    ctx.kernel_timing(False)
+    kernels_us = {k: round(ms * 1e3 / n, 1) for k, (ms, n) in ktimes.items() if n}
+    kernel_launches = {k: n for k, (ms, n) in ktimes.items() if n}
     err = ctx.device_error()
     if err:
         log(f"device error word after timed steps: {err:#x}")
@@ -159,15 +166,24 @@ def main() -> int:
     ms_per_step = elapsed_ms / args.steps
     layer_steps_per_s = args.steps * NL / (elapsed_ms / 1e3)
     # algorithmic work of the timed steps
-    idx_b = gat_b = att_f = 0
+    idx_b = gat_b = att_f = sweep_b = sweep_f = 0
     for i in range(args.steps):
-        wk = acc.step_work(wl.ctx_at(args.warmup + i), S, K, NL, wl.kv_dtype, wl.idx_dtype)
+        lens_i = wl.ctx_at(args.warmup + i)
+        wk = acc.step_work(lens_i, S, K, NL, wl.kv_dtype, wl.idx_dtype)
         idx_b += wk["indexer_bytes"]
         gat_b += wk["gather_bytes"]
         att_f += wk["attention_flops"]
+        sweep_b += sum(acc.sweep_bytes(int(L), S, wl.idx_dtype) for L in lens_i)
+        sweep_f += wk["indexer_flops"]
     idx_b /= args.steps
     gat_b /= args.steps
     att_f /= args.steps
+    sweep_b /= args.steps
+    sweep_f /= args.steps
+    # roofline of the dominant kernel: the indexer score sweep (one launch per step)
+    t_sweep_ms = ktimes["index_score"][0] / ktimes["index_score"][1]
+    sweep_gbps = sweep_b / (t_sweep_ms * 1e-3) / 1e9
+    traffic = rprof.read_traffic(os.path.join(ROOT, "profiles", f"index_score_kernel_{wl.name}_traffic.txt"))
     idx_gbps = idx_b / (t_idx * 1e-3) / 1e9
     gat_gbps = gat_b / (t_dec * 1e-3) / 1e9
     both_gbps = (idx_b + gat_b) / ((t_idx + t_dec) * 1e-3) / 1e9
@@ -207,9 +223,15 @@ def main() -> int:
                       "mfma_util_bf16_dense": round(mfma_util, 4)},
         "host_link": {"misses_last_step": last_miss, "misses_warmup_steps": misses_warm,
                       "gbps": round(host_gbps, 2)},
-        "roofline": {"kernel": "hisparse_index_topk (score sweep + top-K select)",
-                     "bound": "hbm", "achieved": round(idx_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(idx_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "kernels_us": kernels_us,
+        "kernel_launches": kernel_launches,
+        "roofline": {"kernel": "index_score_kernel (indexer score sweep)",
+                     "bound": "hbm", "achieved": round(sweep_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(sweep_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": int(sweep_b),
+                     "avg_launch_us": round(t_sweep_ms * 1e3, 1),
+                     "mfma_frac_bf16_dense": round(sweep_f / (t_sweep_ms * 1e-3) / (BF16_DENSE_TFLOPS * 1e12), 4)},
         "cpu_baseline": cpu,
         "host_wall_s": round(t_host, 4),
     }

@@ -27,7 +27,9 @@
  *   - Arguments are checked on the host without synchronising.  Faults only the device can
  *     see (a placeholder page without a host copy, a block or row id out of range, a
  *     context shorter than its query count) set a sticky device error word, read with
- *     hs_read_device_error() outside the hot loop; the offending item is skipped.
+ *     hs_read_device_error() outside the hot loop; the offending item is skipped, no access
+ *     leaves its buffer, and the other results of that call are unspecified (a skipped key
+ *     page leaves its tokens' scores stale, a skipped row reads as zeros).
  *   - Device buffers are borrowed: the caller allocates them (e.g. with PyTorch) and keeps
  *     them alive while bound.  The library owns only the context and the pinned host pool.
  *   - The three step calls allocate nothing, never synchronise and take every per-step
@@ -216,6 +218,28 @@ hs_status hs_hot_state(const hs_ctx* ctx, hs_hot_state_ptrs* out);
 
 /* Number of split-K partitions sparse_mla_decode uses for a (B, S) batch. */
 hs_status hs_decode_splits(const hs_ctx* ctx, int32_t B, int32_t S, int32_t* splits);
+
+/* Per-kernel device timing, for measurement.  While enabled, every kernel launched by the
+ * step calls (and hs_hot_reset) is bracketed by a pair of HIP events recorded on the caller's
+ * stream, so the pair times that launch alone.  hs_kernel_times waits for the recorded events,
+ * writes the summed milliseconds and the launch count of each kernel (indexed by
+ * hs_kernel_id; `n` entries at most) since timing was enabled or last read, and starts a new
+ * period.  Enabling creates a fixed pool of 16,384 events (no device memory); launches past
+ * its capacity are not timed and hs_kernel_times then returns HS_ERR_STATE (counts written).
+ * Disabling destroys the pool and drops unread records.  Off by default. */
+typedef enum {
+  HS_KERNEL_INDEX_SCORE = 0,  /* indexer score sweep (+ first-digit histogram) */
+  HS_KERNEL_TOPK_SELECT = 1,  /* top-K select */
+  HS_KERNEL_RESOLVE = 2,      /* resolver: residency, hot hits, LRU victims, row ids */
+  HS_KERNEL_MISS_COPY = 3,    /* host-to-device copy of the misses' rows */
+  HS_KERNEL_DECODE = 4,       /* sparse MLA decode attention */
+  HS_KERNEL_DECODE_MERGE = 5, /* split-K merge of the decode */
+  HS_KERNEL_HOT_RESET = 6,    /* hot-buffer reset */
+  HS_KERNEL_COUNT = 7
+} hs_kernel_id;
+
+hs_status hs_kernel_timing(hs_ctx* ctx, int32_t enable);
+hs_status hs_kernel_times(hs_ctx* ctx, double* ms, int64_t* launches, int32_t n);
 
 const char* hs_status_string(hs_status status);
 const char* hs_last_error(void);

@@ -40,6 +40,12 @@ def indexer_bytes(ctx: int, S: int, K: int, idx_dtype: int = 1) -> int:
     return ctx * IDX_KEY_BYTES[idx_dtype] + S * IDX_QUERY_BYTES + S * K * 4
 
 
+def sweep_bytes(ctx: int, S: int, idx_dtype: int = 1) -> int:
+    """One request, score sweep only: every key streamed once, S queries + weights in (the
+    scores it hands to the select are an intermediate, not counted)."""
+    return ctx * IDX_KEY_BYTES[idx_dtype] + S * IDX_QUERY_BYTES
+
+
 def indexer_flops(ctx: int, S: int) -> int:
     """One request: each of the S queries scores the rows it sees."""
     return sum((ctx - S + 1 + j) * IDX_FLOPS_PER_KEY for j in range(S))

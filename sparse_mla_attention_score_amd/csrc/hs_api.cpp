@@ -8,9 +8,62 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "hisparse.h"
 #include "hs_internal.h"
+
+namespace hs {
+
+struct KernelTimer {
+  static constexpr size_t kEvents = 16384;
+  struct Rec {
+    int kernel;
+    hipEvent_t begin, end;
+  };
+  std::vector<hipEvent_t> pool;
+  size_t next = 0;
+  std::vector<Rec> recs;
+  bool overflow = false;
+  bool open = false;  // a begin mark waits for its end mark
+};
+
+}  // namespace hs
+
+void hs_timer_mark(const hs_ctx* ctx, int kernel, bool begin, hipStream_t stream) {
+  hs::KernelTimer* t = ctx->timer;
+  if (!t) return;
+  if (begin) {
+    t->open = false;
+    if (t->next + 2 > t->pool.size()) {
+      t->overflow = true;
+      return;
+    }
+    hipEvent_t a = t->pool[t->next++];
+    if (hipEventRecord(a, stream) != hipSuccess) {
+      t->overflow = true;
+      return;
+    }
+    t->recs.push_back({kernel, a, nullptr});
+    t->open = true;
+  } else if (t->open) {
+    t->open = false;
+    hipEvent_t b = t->pool[t->next++];
+    if (hipEventRecord(b, stream) != hipSuccess) {
+      t->recs.pop_back();
+      t->overflow = true;
+      return;
+    }
+    t->recs.back().end = b;
+  }
+}
+
+static void timer_free(hs_ctx* ctx) {
+  if (!ctx->timer) return;
+  for (hipEvent_t e : ctx->timer->pool) (void)hipEventDestroy(e);
+  delete ctx->timer;
+  ctx->timer = nullptr;
+}
 
 hipError_t hs_set_kernel_attributes();
 hipError_t hs_resolve_set_attributes(size_t lds_bytes);
@@ -120,6 +173,62 @@ hs_status hs::compute_layout(const hs_config& c, Layout* L) {
 
 extern "C" {
 
+hs_status hs_kernel_timing(hs_ctx* ctx, int32_t enable) {
+  if (!ctx) return fail(HS_ERR_INVALID_ARG, "ctx is NULL");
+  if (!enable) {
+    timer_free(ctx);
+    return ok();
+  }
+  if (ctx->timer) return ok();
+  hipError_t e = hipSetDevice(ctx->device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  auto* t = new hs::KernelTimer();
+  t->pool.reserve(hs::KernelTimer::kEvents);
+  for (size_t i = 0; i < hs::KernelTimer::kEvents; ++i) {
+    hipEvent_t ev;
+    e = hipEventCreate(&ev);
+    if (e != hipSuccess) break;
+    t->pool.push_back(ev);
+  }
+  ctx->timer = t;
+  if (e != hipSuccess) {
+    timer_free(ctx);
+    return hip_fail(e, "hipEventCreate");
+  }
+  return ok();
+}
+
+hs_status hs_kernel_times(hs_ctx* ctx, double* ms, int64_t* launches, int32_t n) {
+  if (!ctx || !ms || !launches || n < 0) return fail(HS_ERR_INVALID_ARG, "bad argument");
+  if (!ctx->timer) return fail(HS_ERR_STATE, "kernel timing is not enabled");
+  hs::KernelTimer* t = ctx->timer;
+  for (int32_t i = 0; i < n; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  hipError_t e = hipSuccess;
+  for (const auto& r : t->recs) {
+    if (!r.end) continue;
+    e = hipEventSynchronize(r.end);
+    if (e != hipSuccess) break;
+    float v = 0.0f;
+    e = hipEventElapsedTime(&v, r.begin, r.end);
+    if (e != hipSuccess) break;
+    if (r.kernel >= 0 && r.kernel < n) {
+      ms[r.kernel] += v;
+      launches[r.kernel] += 1;
+    }
+  }
+  const bool overflow = t->overflow;
+  t->recs.clear();
+  t->next = 0;
+  t->overflow = false;
+  t->open = false;
+  if (e != hipSuccess) return hip_fail(e, "hs_kernel_times");
+  if (overflow) return fail(HS_ERR_STATE, "event pool exhausted: some launches were not timed");
+  return ok();
+}
+
 const char* hs_status_string(hs_status s) {
   switch (s) {
     case HS_OK: return "HS_OK";
@@ -182,6 +291,7 @@ hs_status hs_create(const hs_config* cfg, hs_ctx** out) {
 
 hs_status hs_destroy(hs_ctx* ctx) {
   if (!ctx) return fail(HS_ERR_INVALID_ARG, "ctx is NULL");
+  timer_free(ctx);
   if (ctx->host_pool) (void)hipHostFree(ctx->host_pool);
   delete ctx;
   return ok();

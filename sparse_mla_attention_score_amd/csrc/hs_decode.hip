@@ -420,6 +420,7 @@ hipError_t hs_launch_decode(const hs_ctx* ctx, int layer, const void* q, const i
   const float qk_scale_log2 = sm_scale * 1.4426950408889634f;
   const int xcd_map = (B % 8 == 0) ? 1 : 0;
   const dim3 grid((unsigned)(B * S * splits)), block(kDecThreads);
+  hs_timer_mark(ctx, HS_KERNEL_DECODE, true, stream);
   if (c.kv_dtype == HS_FP8_E4M3)
     hipLaunchKernelGGL(sparse_mla_decode_kernel<true>, grid, block, DecLds::kTotal, stream,
                        static_cast<const uint16_t*>(q), row_ids, ctx_lens, B, S, c.topk,
@@ -432,10 +433,13 @@ hipError_t hs_launch_decode(const hs_ctx* ctx, int layer, const void* q, const i
                        c.max_pages_per_req * kBlock, kv, n_rows_pool, qk_scale_log2, splits,
                        xcd_map, static_cast<uint16_t*>(out), lse, ctx->ws.part_o, ctx->ws.part_ml,
                        ctx->ws.err);
+  hs_timer_mark(ctx, HS_KERNEL_DECODE, false, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
+  hs_timer_mark(ctx, HS_KERNEL_DECODE_MERGE, true, stream);
   hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(B * S)), dim3(256), 0, stream,
                      ctx->ws.part_o, ctx->ws.part_ml, splits, static_cast<uint16_t*>(out), lse);
+  hs_timer_mark(ctx, HS_KERNEL_DECODE_MERGE, false, stream);
   return hipGetLastError();
 }
 

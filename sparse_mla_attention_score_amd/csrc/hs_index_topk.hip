@@ -8,14 +8,15 @@
 // and the selection is the min(K, L_j) tokens ranked by (score desc, token asc), emitted in
 // ascending token order.
 //
-// Sweep: one workgroup scores 32 pages (2,048 tokens) of one request for all S queries.  The
-// contraction [S*32 heads x 128] x [128 x tokens] runs on bf16 MFMA (32x32x16): FP8 keys are
-// converted to bf16 exactly, the per-token fp32 scale is applied after the ReLU (positive
-// scales commute with it).  Each wave streams a page: lane l reads 64 contiguous key bytes
-// of token l%32 (dims 64*(l/32) .. +64); the 128 dims are assigned to MFMA k-slots in that
-// order, and the queries held in registers use the same assignment.  Scores go to a
-// per-(request, query) scratch row; their first radix digit (bits [30:19]) is counted in LDS
-// and added to a global histogram.
+// Sweep: one workgroup scores 64 pages (4,096 tokens) of one request for all S queries: four
+// waves stream pages for each group of (at most) two queries, and the groups stay within one
+// prefetch round of each other so that each page comes from HBM once.  The contraction
+// [S*32 heads x 128] x [128 x tokens] runs on bf16 MFMA (32x32x16): FP8 keys are converted to
+// bf16 exactly, the per-token fp32 scale is applied after the ReLU (positive scales commute
+// with it).  Lane l reads 64 contiguous key bytes of token l%32 (dims 64*(l/32) .. +64); the
+// 128 dims are assigned to MFMA k-slots in that order, and the queries held in registers use
+// the same assignment.  Scores go to a per-(request, query) scratch row; their first radix
+// digit (bits [30:19]) is counted in LDS and added to a global histogram.
 //
 // Select: one workgroup per (request, query).  The histogram gives the threshold bin; one
 // pass over the scores marks the tokens above it in a bitmap (wave ballots) and collects the
@@ -147,6 +148,9 @@ __global__ __launch_bounds__(SweepShape<S>::kThreads) void index_score_kernel(
   for (int u = 0; u < kRing - 1; ++u)
     load_key_tile<kFp8>(ring[u], tile_src(u, ring_t0[u]), (u & 1) * 32 + col, half);
   for (int k0 = 0; k0 < kTilesPerWave; k0 += kRing) {
+    // Both query groups read the same pages; keeping them within one ring round of each other
+    // lets the second group's reads hit in L2 instead of going to HBM again.
+    if constexpr (Shape::kGroups > 1) __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
       const int k = k0 + u;
@@ -428,11 +432,13 @@ hipError_t launch_scores(const hs_ctx* ctx, const void* q_idx, const float* w,
   const hs_config& c = ctx->cfg;
   const int items = (c.max_pages_per_req + kPagesPerItem - 1) / kPagesPerItem;
   dim3 grid((unsigned)(B * items)), block(SweepShape<S>::kThreads);
+  hs_timer_mark(ctx, HS_KERNEL_INDEX_SCORE, true, stream);
   hipLaunchKernelGGL((index_score_kernel<S, kFp8>), grid, block, 0, stream,
                      static_cast<const uint16_t*>(q_idx), w, ctx_lens,
                      static_cast<const uint8_t*>(ctx->buf.idx_pool), ctx->buf.idx_block_table,
                      c.max_pages_per_req, (int64_t)c.num_idx_blocks, B, ctx->ws.scores,
                      ctx->lay.lmax, ctx->ws.hist, ctx->ws.err);
+  hs_timer_mark(ctx, HS_KERNEL_INDEX_SCORE, false, stream);
   return hipGetLastError();
 }
 
@@ -469,9 +475,11 @@ hipError_t hs_launch_index_topk(const hs_ctx* ctx, const void* q_idx, const floa
   if (e != hipSuccess) return e;
   const int cap = hs_select_cand_cap(ctx->cfg);
   const size_t dyn = (size_t)cap * sizeof(uint64_t);
+  hs_timer_mark(ctx, HS_KERNEL_TOPK_SELECT, true, stream);
   hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)(B * S)), dim3(kSelThreads), dyn, stream,
                      ctx_lens, B, S, ctx->cfg.topk, ctx->cfg.max_pages_per_req * kBlock,
                      ctx->ws.scores, ctx->lay.lmax, ctx->ws.hist, ctx->ws.bitmap,
                      (int64_t)ctx->lay.bm_words, topk_out, cap, ctx->ws.err);
+  hs_timer_mark(ctx, HS_KERNEL_TOPK_SELECT, false, stream);
   return hipGetLastError();
 }

@@ -69,6 +69,10 @@ hs_status compute_layout(const hs_config& c, Layout* out);
 
 }  // namespace hs
 
+namespace hs {
+struct KernelTimer;  // per-kernel event timing (hs_api.cpp)
+}  // namespace hs
+
 struct hs_ctx {
   hs_config cfg;
   hs::Layout lay;
@@ -81,7 +85,12 @@ struct hs_ctx {
   bool bound;
   hs_buffers buf;
   hs::Workspace ws;
+  hs::KernelTimer* timer;   // null unless hs_kernel_timing enabled it
 };
+
+// Brackets one kernel launch with timing events when the context's timer is enabled
+// (begin = true before the launch, false after it); a no-op otherwise.
+void hs_timer_mark(const hs_ctx* ctx, int kernel, bool begin, hipStream_t stream);
 
 // Kernel launchers (each enqueues on `stream`, returns hipSuccess or the launch error).
 hipError_t hs_launch_hot_reset(const hs_ctx* ctx, hipStream_t stream);

@@ -447,6 +447,7 @@ hipError_t hs_launch_resolve(const hs_ctx* ctx, const int32_t* topk, const int32
   const int H = ctx->lay.hot_rows;
   const int cap = union_cap_for(S, c.topk);
   const size_t lds = hs_resolve_lds_bytes(S, c.topk, H);
+  hs_timer_mark(ctx, HS_KERNEL_RESOLVE, true, stream);
   hipLaunchKernelGGL(resolve_kernel, dim3((unsigned)B), dim3(kResThreads), lds, stream, topk,
                      ctx_lens, S, c.topk, ctx->buf.block_table, ctx->buf.host_block_table,
                      ctx->buf.hot_blocks, c.max_pages_per_req, H, (int64_t)c.num_gpu_blocks,
@@ -454,13 +455,16 @@ hipError_t hs_launch_resolve(const hs_ctx* ctx, const int32_t* topk, const int32
                      ctx->ws.slot_stamp, ctx->ws.lru_order, ctx->ws.tok2slot, ctx->lay.lmax,
                      ctx->ws.req_step, ctx->ws.req_used, ctx->ws.miss_src, ctx->ws.miss_dst,
                      ctx->ws.miss_cnt, cap, row_ids, stats, ctx->ws.err);
+  hs_timer_mark(ctx, HS_KERNEL_RESOLVE, false, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || c.num_host_blocks == 0) return e;
+  hs_timer_mark(ctx, HS_KERNEL_MISS_COPY, true, stream);
   hipLaunchKernelGGL(miss_copy_kernel, dim3(kCopyBlocks), dim3(kCopyThreads), (size_t)(B + 1) * 4,
                      stream, ctx->ws.miss_src, ctx->ws.miss_dst, ctx->ws.miss_cnt, B, S * c.topk,
                      static_cast<const uint8_t*>(ctx->host_pool_dev),
                      static_cast<uint8_t*>(ctx->buf.kv_pool), c.n_layers, ctx->row_bytes,
                      (int64_t)c.num_gpu_blocks, (int64_t)c.num_host_blocks);
+  hs_timer_mark(ctx, HS_KERNEL_MISS_COPY, false, stream);
   return hipGetLastError();
 }
 
@@ -474,10 +478,12 @@ hipError_t hs_launch_hot_reset(const hs_ctx* ctx, hipStream_t stream) {
   if (n_hist > n) n = n_hist;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
+  hs_timer_mark(ctx, HS_KERNEL_HOT_RESET, true, stream);
   hipLaunchKernelGGL(hot_reset_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      ctx->ws.slot_token, ctx->ws.slot_stamp, ctx->ws.lru_order, n_slots,
                      ctx->lay.hot_rows, ctx->ws.tok2slot, n_tok, ctx->ws.req_step, ctx->ws.req_used,
                      c.max_batch, ctx->ws.hist, n_hist, n, ctx->ws.err);
+  hs_timer_mark(ctx, HS_KERNEL_HOT_RESET, false, stream);
   return hipGetLastError();
 }
 

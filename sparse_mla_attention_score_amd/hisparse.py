@@ -23,10 +23,16 @@ HS_DEVERR_SHORT_CONTEXT = 0x8
 HS_DEVERR_TOPK_COUNT = 0x10
 HS_DEVERR_HOT_FULL = 0x20
 
+# hs_kernel_id
+KERNEL_NAMES = ["index_score", "topk_select", "resolve", "miss_copy", "decode", "decode_merge",
+                "hot_reset"]
+HS_KERNEL_COUNT = len(KERNEL_NAMES)
+
 EXPORTED = ["hs_create", "hs_destroy", "hs_workspace_bytes", "hs_host_pool_bytes",
             "hs_host_pool_alloc", "hs_bind", "hs_hot_reset", "hisparse_index_topk",
             "hisparse_resolve", "sparse_mla_decode", "hs_read_device_error", "hs_decode_splits",
-            "hs_hot_state", "hs_status_string", "hs_last_error"]
+            "hs_hot_state", "hs_kernel_timing", "hs_kernel_times", "hs_status_string",
+            "hs_last_error"]
 
 
 class hs_config(ctypes.Structure):
@@ -86,6 +92,9 @@ def lib() -> ctypes.CDLL:
             "hs_read_device_error": [P, ctypes.POINTER(i32)],
             "hs_decode_splits": [P, i32, i32, ctypes.POINTER(i32)],
             "hs_hot_state": [P, ctypes.POINTER(hs_hot_state_ptrs)],
+            "hs_kernel_timing": [P, i32],
+            "hs_kernel_times": [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
+                                i32],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -186,6 +195,18 @@ def hs_hot_state(ctx: int) -> hs_hot_state_ptrs:
     return out
 
 
+def hs_kernel_timing(ctx: int, enable: bool) -> None:
+    _check(lib().hs_kernel_timing(ctx, 1 if enable else 0), "hs_kernel_timing")
+
+
+def hs_kernel_times(ctx: int) -> dict:
+    """{kernel name: (summed ms, launches)} since timing was enabled or last read."""
+    ms = (ctypes.c_double * HS_KERNEL_COUNT)()
+    n = (ctypes.c_int64 * HS_KERNEL_COUNT)()
+    _check(lib().hs_kernel_times(ctx, ms, n, HS_KERNEL_COUNT), "hs_kernel_times")
+    return {name: (ms[i], n[i]) for i, name in enumerate(KERNEL_NAMES)}
+
+
 def make_config(*, topk: int = 2048, kv_dtype: int = HS_FP8_E4M3, idx_dtype: int = HS_FP8_E4M3,
                 n_layers: int = 1, max_batch: int, max_queries: int, max_pages_per_req: int,
                 hot_rows_per_req: int = 0, num_gpu_blocks: int, num_idx_blocks: int,
@@ -268,6 +289,12 @@ class Context:
 
     def device_error(self) -> int:
         return hs_read_device_error(self.ctx)
+
+    def kernel_timing(self, enable: bool) -> None:
+        hs_kernel_timing(self.ctx, enable)
+
+    def kernel_times(self) -> dict:
+        return hs_kernel_times(self.ctx)
 
     def hot_state(self):
         """Copies of (slot_token [B][H], slot_stamp [B][H], tok2slot [B][L], req_step [B]) as

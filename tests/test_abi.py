@@ -80,3 +80,19 @@ def test_status_strings():
     assert hsb.hs_status_string(-2) == "HS_ERR_UNSUPPORTED"
     lib = hsb.lib()
     assert lib.hs_destroy(None) == hsb.HS_ERR_INVALID_ARG
+
+
+def test_kernel_timing_argument_checks():
+    lib = hsb.lib()
+    assert lib.hs_kernel_timing(None, 1) == hsb.HS_ERR_INVALID_ARG
+    ms = (ctypes.c_double * hsb.HS_KERNEL_COUNT)()
+    n = (ctypes.c_int64 * hsb.HS_KERNEL_COUNT)()
+    assert lib.hs_kernel_times(None, ms, n, hsb.HS_KERNEL_COUNT) == hsb.HS_ERR_INVALID_ARG
+
+
+def test_kernel_ids_match_header():
+    text = open(HEADER).read()
+    ids = dict((m[0], int(m[1])) for m in re.findall(r"(HS_KERNEL_\w+)\s*=\s*(\d+)", text))
+    assert ids["HS_KERNEL_COUNT"] == hsb.HS_KERNEL_COUNT
+    for i, name in enumerate(hsb.KERNEL_NAMES):
+        assert ids[f"HS_KERNEL_{name.upper()}"] == i

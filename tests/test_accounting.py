@@ -44,3 +44,10 @@ def test_step_work_128k_config():
     assert w["indexer_bytes"] == 64 * (131072 * 132 + 4 * (32 * 128 * 2 + 32 * 4) + 4 * 2048 * 4)
     assert abs(w["gather_bytes"] / 1e6 - 381.7) < 0.1
     assert abs(w["attention_flops"] / 1e9 - 73.0) < 0.05
+
+
+def test_sweep_bytes_are_keys_and_queries():
+    # FP8: 128 codes + a 4-byte scale per key; per query 32 x 128 bf16 + 32 fp32 weights
+    assert acc.sweep_bytes(131072, 4) == 131072 * 132 + 4 * (32 * 128 * 2 + 32 * 4)
+    assert acc.sweep_bytes(8192, 1, idx_dtype=0) == 8192 * 256 + 32 * 128 * 2 + 32 * 4
+    assert acc.indexer_bytes(131072, 4, 2048) - acc.sweep_bytes(131072, 4) == 4 * 2048 * 4
