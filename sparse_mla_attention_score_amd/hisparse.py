@@ -296,24 +296,29 @@ class Context:
     def kernel_times(self) -> dict:
         return hs_kernel_times(self.ctx)
 
-    def hot_state(self):
+    def hot_state(self, requests=None):
         """Copies of (slot_token [B][H], slot_stamp [B][H], tok2slot [B][L], req_step [B]) as
-        int32 numpy arrays, read from the workspace the library bound."""
-        import numpy as np
+        int32 numpy arrays, read from the workspace the library bound; with `requests`, only
+        those requests' rows (in that order)."""
         import torch
         p = hs_hot_state(self.ctx)
         ws0 = (self.workspace.data_ptr() + 255) // 256 * 256
         base = self.workspace.data_ptr()
         B, H, L = self.cfg.max_batch, p.hot_rows, p.tokens_per_req
+        pick = None if requests is None else torch.as_tensor(list(requests), device=self.device)
 
-        def view(addr, n):
+        def view(addr, rows, cols):
             off = addr - base
+            n = rows * cols
             assert off >= ws0 - base and off + 4 * n <= self.workspace.numel()
-            return self.workspace[off:off + 4 * n].view(torch.int32).cpu().numpy()
+            t = self.workspace[off:off + 4 * n].view(torch.int32).view(rows, cols)
+            if pick is not None:
+                t = t.index_select(0, pick)
+            return t.cpu().numpy()
 
         torch.cuda.synchronize()
-        return (view(p.slot_token, B * H).reshape(B, H), view(p.slot_stamp, B * H).reshape(B, H),
-                view(p.tok2slot, B * L).reshape(B, L), view(p.req_step, B).copy())
+        return (view(p.slot_token, B, H), view(p.slot_stamp, B, H), view(p.tok2slot, B, L),
+                view(p.req_step, B, 1).reshape(-1).copy())
 
     def close(self) -> None:
         if getattr(self, "ctx", None):

@@ -13,6 +13,7 @@ Comparison rules (readings stated in the design doc):
 from __future__ import annotations
 
 import math
+import time
 
 import numpy as np
 import torch
@@ -32,7 +33,7 @@ def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
 
 class GpuWorkload:
     def __init__(self, wl: synth.Workload, device: str = "cuda:0", topk_lds_candidates: int = 0,
-                 layout: synth.Layout | None = None):
+                 layout: synth.Layout | None = None, verbose: bool = False):
         self.wl = wl
         self.lay = layout or synth.make_layout(wl)
         lay = self.lay
@@ -44,13 +45,25 @@ class GpuWorkload:
                               num_host_blocks=lay.num_host_blocks,
                               topk_lds_candidates=topk_lds_candidates)
         self.ctx = hsb.Context(cfg, device)
+        t0 = time.time()
         idx_stage = np.zeros(lay.num_idx_blocks * wl.idx_block_bytes, np.uint8)
         synth.fill_idx_pool(wl, lay, idx_stage)
         self.ctx.idx_pool.copy_(torch.from_numpy(idx_stage))
         del idx_stage
-        kv_stage = np.zeros(wl.n_layers * lay.num_gpu_blocks * 64 * wl.row_bytes, np.uint8)
-        synth.fill_kv(wl, lay, kv_stage, self.ctx.host_pool)
-        self.ctx.kv_pool.copy_(torch.from_numpy(kv_stage))
+        if verbose:
+            print(f"[{wl.name}] indexer pool filled ({time.time() - t0:.1f} s)", flush=True)
+        # one layer at a time: the staging buffer holds one layer's resident rows
+        nb = lay.num_gpu_blocks * 64 * wl.row_bytes
+        hb = lay.num_host_blocks * 64 * wl.row_bytes
+        kv_stage = np.zeros(nb, np.uint8)
+        for layer in range(wl.n_layers):
+            if layer:
+                kv_stage.fill(0)
+            host = self.ctx.host_pool[layer * hb:(layer + 1) * hb] if hb else None
+            synth.fill_kv(wl, lay, kv_stage, host, layers=[layer])
+            self.ctx.kv_pool[layer * nb:(layer + 1) * nb].copy_(torch.from_numpy(kv_stage))
+            if verbose:
+                print(f"[{wl.name}] layer {layer} rows filled ({time.time() - t0:.1f} s)", flush=True)
         del kv_stage
         self.ctx.idx_block_table.copy_(torch.from_numpy(lay.idx_block_table))
         self.ctx.block_table.copy_(torch.from_numpy(lay.block_table))
