@@ -10,19 +10,23 @@
 // The per-row scale is folded out of the contractions: q . x = a (q_nope . c) + q_rope . rope,
 // and sum_k p_k x_k = sum_k (p_k a_k) c_k, so the MFMAs see the codes converted exactly.
 //
-// Workgroup = (query token, split of its rows), 4 waves = 2 head groups (32 heads each) x 2
-// halves.  Rows go in tiles of 64.  A tile is gathered from HBM once (8-byte pieces of 8
-// rows per thread, coalesced along the row), converted to bf16 once, and written to LDS twice:
-// row-major for QK and dim-major for PV (transposed in registers).  The next tile's loads are
-// issued before the current tile is computed.  Each wave computes S^T = K Q^T for its 32 heads
-// on half the tile's rows, and O^T += V^T P^T for its 32 heads on half the value dims over all
-// the rows, on 32x32x16 bf16 MFMAs; the two waves of a head group swap their row maxima and
-// probabilities through LDS.  In this orientation a lane owns one head, so the softmax state is
+// Both kernels: workgroup = (query token, split of its rows); rows go in tiles of 64; in the
+// MFMA orientation S^T = K Q^T and O^T += V^T P^T a lane owns one head, so the softmax state is
 // per lane and the probabilities feed the PV MFMA in the layout the QK result has (the PV
-// k-slots are assigned to rows in that order, and the transposed tile is stored in it).  The
-// running maximum is only moved when it grows by more than 2^8, so the accumulators are rarely
-// rescaled.  Splits of one query are combined with log-sum-exp, the same algebra as merging
-// per-shard partial attention (part-2 page, "DCP" section).
+// k-slots are assigned to rows in that order).  The running maximum is only moved when it grows
+// by more than 2^8, so the accumulators are rarely rescaled.  Splits of one query are combined
+// with log-sum-exp, the same algebra as merging per-shard partial attention (part-2 page, "DCP"
+// section).
+//
+// FP8 rows (sparse_mla_decode_fp8_kernel, below): 8 waves = 4 groups of 16 heads x 2 halves of
+// the dims; tiles stay FP8 in LDS, double-buffered and filled by direct loads one tile ahead.
+//
+// bf16 rows (sparse_mla_decode_kernel): 4 waves = 2 head groups (32 heads each) x 2 halves.  A
+// tile is gathered from HBM once (8-byte pieces of 8 rows per thread, coalesced along the row)
+// and written to LDS twice: row-major for QK and dim-major for PV (transposed in registers).
+// Each wave computes S^T for its 32 heads on half the tile's rows and O^T for its 32 heads on
+// half the value dims over all the rows, on 32x32x16 bf16 MFMAs; the two waves of a head group
+// swap their row maxima and probabilities through LDS.
 #include "hs_device.h"
 #include "hs_internal.h"
 
@@ -353,6 +357,309 @@ __global__ __launch_bounds__(kDecThreads) void sparse_mla_decode_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// FP8 rows: tiles stay FP8 in LDS.
+//
+// A tile is fetched by direct global->LDS loads (16 bytes per lane; rows keep their stored
+// 656-byte pitch) one tile ahead of the tile being computed, so the gather's latency hides
+// behind the MFMAs and no registers hold rows in flight.  Operands are converted to bf16 exactly
+// as they are read: K with plain 8-byte reads (row-major), V^T with the transposing 8-byte read
+// (ds_read_b64_tr_b8: in each group of 16 lanes, lanes 2k and 2k+1 address the two halves of a
+// 16-byte segment of "row" k and lane r receives byte r of all eight segments), which hands a
+// lane the 8 rows of one value dim that its MFMA k-slots take.  The rows behind the k-slots are
+// addressed in the order the probabilities come out of the QK result, so nothing is permuted in
+// memory.  Barriers between the waves wait for LDS traffic only, never for the prefetch.
+//
+// Work split: wave (hq, dh) holds Q for heads 16 hq .. +15 over half of the 576 QK dims (nope
+// 256 dh .. +255 and rope 32 dh .. +31) and accumulates O^T for those heads over value dims
+// 256 dh .. +255, on 16x16x32 bf16 MFMAs.  The two dim halves' partial scores are added through
+// LDS, after which both waves of a head group run the same softmax.  Holding a quarter of the
+// heads and half the dims keeps a wave under 256 registers, so two waves share each SIMD and
+// one's MFMAs overlap the other's conversions and softmax.
+constexpr int kF8RowChunks = kFp8Row / 16;                   // 41 pieces of 16 bytes per row
+constexpr int kF8TileBytes = kTileRows * kFp8Row;            // 41,984
+constexpr int kF8TileLoads = kTileRows * kF8RowChunks / 64;  // 41 wave-wide loads per tile
+static_assert(kTileRows * kF8RowChunks % 64 == 0, "whole wave-wide loads per tile");
+static_assert(kF8RowChunks == 41 && kTileRows * kF8RowChunks <= 2688, "division by 41 below");
+
+// s_waitcnt vmcnt(N) (expcnt, lgkmcnt unconstrained), gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that waits for this wave's LDS traffic only (not for loads in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15 | (3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One wave-wide direct load: lane l's 16 bytes at `src` land at LDS byte address lds + 16 l.
+// Issued from asm on purpose: the compiler does not see these loads, so it adds no waits for
+// them in front of LDS reads it cannot prove disjoint (e.g. the transposing reads); the
+// kernel waits for them itself (wait_vmcnt, which only ever waits for more than the
+// compiler's own bookkeeping would, as vector-memory operations complete in order).  No other
+// instruction of the kernel uses m0.
+__device__ __forceinline__ void lds_load16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)p;
+}
+
+typedef int lds_i32x2 __attribute__((vector_size(8)));
+
+__device__ __forceinline__ u32x2 lds_read_tr8(const unsigned char* p) {
+  const lds_i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) lds_i32x2*)(p));
+  return u32x2{(uint32_t)v[0], (uint32_t)v[1]};
+}
+
+constexpr int kF8Threads = 512;  // 8 waves: 4 groups of 16 heads x 2 halves of the dims
+constexpr int kF8Waves = kF8Threads / 64;
+constexpr int kF8LoadsMinW = kF8TileLoads / kF8Waves;  // tile loads every wave issues (5)
+
+__global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
+    const uint16_t* __restrict__ q, const int32_t* __restrict__ row_ids,
+    const int32_t* __restrict__ ctx_lens, int B, int S, int K, int max_ctx,
+    const uint8_t* __restrict__ kv, int64_t n_rows_pool, float qk_scale_log2, int splits,
+    int xcd_map, uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    float* __restrict__ part_ml, int32_t* __restrict__ err) {
+  // two tiles of raw rows (distinct objects, one filled while the other is read)
+  __shared__ __align__(16) unsigned char tile_a[kF8TileBytes];
+  __shared__ __align__(16) unsigned char tile_b[kF8TileBytes];
+  __shared__ int32_t rids[kMaxTopk];               // this workgroup's row ids (-1: skipped)
+  __shared__ __align__(16) f32x4 sx[kF8Waves][4][64];  // partial scores, accumulator layout
+  __shared__ __align__(16) float row_sc[kTileRows];    // FP8 scale of each row of the tile
+  __shared__ __align__(16) float row_bias[kTileRows];  // 0, or -inf for a skipped row
+  // The tiles are written only by the asm loads: hand their addresses to asm so that the
+  // compiler does not take them for never-written memory.
+  asm volatile("" : : "v"(tile_a), "v"(tile_b) : "memory");
+
+  const int per_req = S * splits;
+  int b, r;
+  if (xcd_map) {
+    const int slot = blockIdx.x / 8;
+    b = (blockIdx.x % 8) + 8 * (slot / per_req);
+    r = slot % per_req;
+  } else {
+    b = blockIdx.x / per_req;
+    r = blockIdx.x % per_req;
+  }
+  const int j = r / splits, sp = r % splits;
+  const int bj = b * S + j;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // hq: heads 16 hq .. +15.  dh: this wave's half of the QK dims (nope 256 dh .. +255, rope
+  // 32 dh .. +31) and of the value dims (256 dh .. +255).  In the 16x16 MFMA layouts lane l
+  // works on head 16 hq + l%16 and on rows / dims in groups of 4 selected by l/16.
+  const int hq = wave & 3, dh = wave >> 2;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int head = 16 * hq + c16;
+
+  const int Lb = ctx_lens[b];
+  int n = 0;
+  if (Lb >= S && Lb <= max_ctx) n = min(K, Lb - S + 1 + j);
+  else if (tid == 0 && sp == 0) raise_error(err, HS_DEVERR_SHORT_CONTEXT);
+  const int per = ((n + splits - 1) / splits + kTileRows - 1) / kTileRows * kTileRows;
+  const int r0 = min(n, sp * per), r1 = min(n, r0 + per);
+  const int nrows = r1 - r0;
+
+  // staged up to a whole tile (-1 past the range), so tile loads read them without bounds
+  const int nrows_pad = (nrows + kTileRows - 1) / kTileRows * kTileRows;
+  for (int i = tid; i < nrows_pad; i += kF8Threads) {
+    int32_t v = -1;
+    if (i < nrows) {
+      v = row_ids[(int64_t)bj * K + r0 + i];
+      if (v < 0 || v >= n_rows_pool) {
+        raise_error(err, HS_DEVERR_BAD_ROW);
+        v = -1;
+      }
+    }
+    rids[i] = v;
+  }
+  // Q^T fragments (B operand): k-step s < 8 covers nope dims 256 dh + 32 s .. +31, s = 8 the
+  // rope dims 512 + 32 dh .. +31; lane group g holds 8 of the 32.
+  bf16x8 qf[9];
+  {
+    const uint16_t* qp = q + ((int64_t)bj * kHeads + head) * kDqk + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 256 * dh + 32 * s));
+    qf[8] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 512 + 32 * dh));
+  }
+  f32x4 o[16];  // O^T for value dims 256 dh + 16 db + 4 g + i, head `head`
+#pragma unroll
+  for (int db = 0; db < 16; ++db) o[db] = f32x4{};
+  float m_used = -INFINITY, l_part = 0.0f;
+  // Q and the row ids are in before any tile load is issued, and the compiler knows it: its
+  // waits for them would otherwise sit inside the tile loop and also drain the prefetch.  (The
+  // empty asm takes the fragments, so their loads cannot sink below this point.)
+#pragma unroll
+  for (int s = 0; s < 9; ++s) asm volatile("" : "+v"(qf[s]));
+  wait_vmcnt<0>();
+  asm volatile("" ::: "memory");
+  __syncthreads();  // row ids staged
+
+  // Loads of tile rows [t0, t0 + 64) of the range into LDS address `buf`: wave-wide load ins
+  // covers the 64 consecutive 16-byte pieces ins*64 .. ins*64+63 of the tile; wave w issues
+  // w, w+8, ...
+  auto issue = [&](uint32_t buf, int t0) {
+#pragma unroll
+    for (int i = 0; i < (kF8TileLoads + kF8Waves - 1) / kF8Waves; ++i) {
+      const int ins = kF8Waves * i + wave;
+      if (ins < kF8TileLoads) {
+        int c = ins * 64 + lane;
+        // recomputed per tile: hoisting the lane addresses out of the tile loop costs registers
+        asm volatile("" : "+v"(c));
+        const int row = (c * 1599) >> 16;  // c / 41 for c < 2,688
+        const int piece = c - row * kF8RowChunks;
+        const int32_t rid = max(rids[t0 + row], 0);  // a skipped row reads row 0, masked later
+        lds_load16(kv + (int64_t)rid * kFp8Row + 16 * piece, buf + ins * 1024);
+      }
+    }
+  };
+
+  // Transposed V reads: lane group g takes the k-slots 8g .. 8g+7 of a 32-row k-step, which
+  // hold the rows the P operand puts there (rows 4g .. 4g+3 and 16+4g .. 16+4g+3 of the step).
+  const int kk8 = (lane & 15) >> 1;
+  const int v_lane_off = (kk8 < 4 ? 4 * g + kk8 : 16 + 4 * g + (kk8 - 4)) * kFp8Row + 256 * dh + 8 * (lane & 1);
+
+  auto compute = [&](const unsigned char* buf, int t0) {
+    // ---- per-row scale and validity of the tile, in contiguous arrays
+    if (tid < kTileRows) {
+      row_sc[tid] = *reinterpret_cast<const float*>(buf + tid * kFp8Row + 640);
+      row_bias[tid] = (tid < nrows - t0 && rids[t0 + tid] >= 0) ? 0.0f : -INFINITY;
+    }
+    // ---- partial S^T = K Q^T over this wave's dims: 4 blocks of 16 rows (mb), lane holds rows
+    // 16 mb + 4 g + i of head `head`
+    f32x4 c[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const unsigned char* kp = buf + (16 * mb + c16) * kFp8Row + 256 * dh + 8 * g;
+      c[mb] = f32x4{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const u32x2 raw = *reinterpret_cast<const u32x2*>(kp + 32 * s);
+        c[mb] = mfma16x16x32(e4m3x8_to_bf16(raw[0], raw[1]), qf[s], c[mb]);
+      }
+    }
+    lds_barrier();  // row_sc / row_bias written
+    f32x4 sc4[4], bias4[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      sc4[mb] = *reinterpret_cast<const f32x4*>(&row_sc[16 * mb + 4 * g]);
+      bias4[mb] = *reinterpret_cast<const f32x4*>(&row_bias[16 * mb + 4 * g]);
+      c[mb] *= sc4[mb];  // nope part times the row's scale; the rope part adds on top
+      const unsigned char* rp = buf + (16 * mb + c16) * kFp8Row + 512 + 64 * dh + 16 * g;
+      c[mb] = mfma16x16x32(as_bf16x8(*reinterpret_cast<const u32x4*>(rp)), qf[8], c[mb]);
+      sx[wave][mb][lane] = c[mb];
+    }
+    lds_barrier();
+    // ---- add the other dim half's partial (wave ^ 4); both waves then hold the same scores
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      c[mb] += sx[wave ^ 4][mb][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[mb][i] = __builtin_fmaf(c[mb][i], qk_scale_log2, bias4[mb][i]);
+        tmax = fmaxf(tmax, c[mb][i]);
+      }
+    }
+    // the head's maximum over the 4 lane groups
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    if (tmax > m_used + kLazyRescale) {
+      const float alpha = exp2f(m_used - tmax);
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < 16; ++db) o[db] *= alpha;
+      m_used = tmax;
+    }
+    // P (times the row scale) as the B operand of two 32-row k-steps: k-slot 8g + e holds row
+    // 4g + e (e < 4) or 16 + 4g + e - 4 of the step
+    bf16x8 pb[2];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = c[mb][i] > -INFINITY ? exp2f(c[mb][i] - m_used) : 0.0f;
+        l_part += p;
+        pb[mb >> 1][4 * (mb & 1) + i] = (__bf16)(p * sc4[mb][i]);
+      }
+    // ---- O^T += V^T P^T: 16 blocks of 16 value dims x 2 k-steps of 32 rows
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const unsigned char* vp = buf + 32 * kk * kFp8Row + v_lane_off;
+#pragma unroll
+      for (int db = 0; db < 16; ++db) {
+        const u32x2 raw = lds_read_tr8(vp + 16 * db);
+        o[db] = mfma16x16x32(e4m3x8_to_bf16(raw[0], raw[1]), pb[kk], o[db]);
+      }
+    }
+  };
+
+  // tile i of the range lives in tile_a (even i) or tile_b (odd i); tile i+1 loads while
+  // tile i is computed
+  auto step = [&](const unsigned char* cur, const unsigned char* nxt, int t0) {
+    if (t0 + kTileRows < nrows) {
+      issue(lds_address(nxt), t0 + kTileRows);
+      wait_vmcnt<kF8LoadsMinW>();  // this wave's loads of `cur` have landed
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();  // ... and every other wave's
+    compute(cur, t0);
+    lds_barrier();  // `cur`, the exchange buffer and the row arrays are free again
+  };
+  if (nrows > 0) issue(lds_address(tile_a), 0);
+  for (int t0 = 0; t0 < nrows; t0 += 2 * kTileRows) {
+    step(tile_a, tile_b, t0);
+    if (t0 + kTileRows >= nrows) break;
+    step(tile_b, tile_a, t0 + kTileRows);
+  }
+
+  // ---- finish: the head's row sum over the 4 lane groups (both dim halves hold the same)
+  float l_tot = l_part + __shfl_xor(l_part, 16);
+  {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_tot), __float_as_uint(l_tot), false, false);
+    l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  if (splits == 1) {
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    uint16_t* op = out + ((int64_t)bj * kHeads + head) * kDv + 256 * dh + 4 * g;
+#pragma unroll
+    for (int db = 0; db < 16; ++db) {
+      const __bf16 v0 = (__bf16)(o[db][0] * inv), v1 = (__bf16)(o[db][1] * inv);
+      const __bf16 v2 = (__bf16)(o[db][2] * inv), v3 = (__bf16)(o[db][3] * inv);
+      const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
+      const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, v2) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
+      *reinterpret_cast<u32x2*>(op + 16 * db) = u32x2{w0, w1};
+    }
+    if (lse && g == 0 && dh == 0)
+      lse[(int64_t)bj * kHeads + head] = (m_used + log2f(l_tot)) * 0.69314718055994531f;
+  } else {
+    const int64_t part = (int64_t)bj * splits + sp;
+    if (g == 0 && dh == 0) {
+      part_ml[(part * kHeads + head) * 2 + 0] = m_used;
+      part_ml[(part * kHeads + head) * 2 + 1] = l_tot;
+    }
+    if (nrows > 0) {
+      float* pp = part_o + (part * kHeads + head) * kDv + 256 * dh + 4 * g;
+#pragma unroll
+      for (int db = 0; db < 16; ++db) *reinterpret_cast<f32x4*>(pp + 16 * db) = o[db];
+    }
+  }
+}
+
 // Combine the split partials of each query: M = max m_s, L = sum l_s 2^(m_s - M),
 // out = sum O_s 2^(m_s - M) / L, lse = (M + log2 L) ln 2.
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ part_o,
@@ -419,16 +726,16 @@ hipError_t hs_launch_decode(const hs_ctx* ctx, int layer, const void* q, const i
                       (int64_t)layer * n_rows_pool * ctx->row_bytes;
   const float qk_scale_log2 = sm_scale * 1.4426950408889634f;
   const int xcd_map = (B % 8 == 0) ? 1 : 0;
-  const dim3 grid((unsigned)(B * S * splits)), block(kDecThreads);
+  const dim3 grid((unsigned)(B * S * splits));
   hs_timer_mark(ctx, HS_KERNEL_DECODE, true, stream);
   if (c.kv_dtype == HS_FP8_E4M3)
-    hipLaunchKernelGGL(sparse_mla_decode_kernel<true>, grid, block, DecLds::kTotal, stream,
+    hipLaunchKernelGGL(sparse_mla_decode_fp8_kernel, grid, dim3(kF8Threads), 0, stream,
                        static_cast<const uint16_t*>(q), row_ids, ctx_lens, B, S, c.topk,
                        c.max_pages_per_req * kBlock, kv, n_rows_pool, qk_scale_log2, splits,
                        xcd_map, static_cast<uint16_t*>(out), lse, ctx->ws.part_o, ctx->ws.part_ml,
                        ctx->ws.err);
   else
-    hipLaunchKernelGGL(sparse_mla_decode_kernel<false>, grid, block, DecLds::kTotal, stream,
+    hipLaunchKernelGGL(sparse_mla_decode_kernel<false>, grid, dim3(kDecThreads), DecLds::kTotal, stream,
                        static_cast<const uint16_t*>(q), row_ids, ctx_lens, B, S, c.topk,
                        c.max_pages_per_req * kBlock, kv, n_rows_pool, qk_scale_log2, splits,
                        xcd_map, static_cast<uint16_t*>(out), lse, ctx->ws.part_o, ctx->ws.part_ml,
@@ -443,11 +750,8 @@ hipError_t hs_launch_decode(const hs_ctx* ctx, int layer, const void* q, const i
   return hipGetLastError();
 }
 
-// Raise the dynamic-LDS limit of the decode kernels.
+// Raise the dynamic-LDS limit of the bf16-row decode kernel.
 hipError_t hs_set_kernel_attributes() {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sparse_mla_decode_kernel<true>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, DecLds::kTotal);
-  if (e != hipSuccess) return e;
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&sparse_mla_decode_kernel<false>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, DecLds::kTotal);
 }
