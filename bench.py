@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--config", type=int, default=3, help="workload index (3 = the 128K metric config)")
     ap.add_argument("--scale", type=int, default=1, help="divide context lengths (development only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-requests", type=int, default=4)
+    ap.add_argument("--cpu-sample-requests", type=int, default=64)
     return ap.parse_args()
 
 

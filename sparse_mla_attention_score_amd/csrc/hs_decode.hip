@@ -382,6 +382,15 @@ constexpr int kF8TileLoads = kTileRows * kF8RowChunks / 64;  // 41 wave-wide loa
 static_assert(kTileRows * kF8RowChunks % 64 == 0, "whole wave-wide loads per tile");
 static_assert(kF8RowChunks == 41 && kTileRows * kF8RowChunks <= 2688, "division by 41 below");
 
+// Within the 32 16-byte pieces of a row's FP8 codes, rows with bit 4 set keep piece c at
+// position c ^ 8.  With the 656-byte pitch, rows r and r + 16 otherwise start on the same LDS
+// bank, and the transposed V reads take rows r and r + 16 together; the swap moves the second
+// onto the 32 banks the first leaves free.  (An involution: the same map finds a piece's
+// position and a position's piece.)
+__device__ __forceinline__ int nope_swizzle(int piece, int row) {
+  return piece < 32 ? piece ^ (8 * ((row >> 4) & 1)) : piece;
+}
+
 // s_waitcnt vmcnt(N) (expcnt, lgkmcnt unconstrained), gfx9 encoding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -517,15 +526,18 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
         const int row = (c * 1599) >> 16;  // c / 41 for c < 2,688
         const int piece = c - row * kF8RowChunks;
         const int32_t rid = max(rids[t0 + row], 0);  // a skipped row reads row 0, masked later
-        lds_load16(kv + (int64_t)rid * kFp8Row + 16 * piece, buf + ins * 1024);
+        lds_load16(kv + (int64_t)rid * kFp8Row + 16 * nope_swizzle(piece, row), buf + ins * 1024);
       }
     }
   };
 
   // Transposed V reads: lane group g takes the k-slots 8g .. 8g+7 of a 32-row k-step, which
   // hold the rows the P operand puts there (rows 4g .. 4g+3 and 16+4g .. 16+4g+3 of the step).
+  // Rows 16+ of a step (kk8 >= 4) have their pieces swizzled: value dims 16 db .. +15 sit at
+  // piece db ^ 8, i.e. 128 bytes later for db < 8 and earlier for db >= 8.
   const int kk8 = (lane & 15) >> 1;
   const int v_lane_off = (kk8 < 4 ? 4 * g + kk8 : 16 + 4 * g + (kk8 - 4)) * kFp8Row + 256 * dh + 8 * (lane & 1);
+  const int v_sw = kk8 >= 4 ? 128 : 0;
 
   auto compute = [&](const unsigned char* buf, int t0) {
     // ---- per-row scale and validity of the tile, in contiguous arrays
@@ -542,7 +554,9 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
       c[mb] = f32x4{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const u32x2 raw = *reinterpret_cast<const u32x2*>(kp + 32 * s);
+        // rows of odd blocks have bit 4 set: their pieces 2s, 2s+1 sit at 2(s^4), 2(s^4)+1
+        const int ss = (mb & 1) ? (s ^ 4) : s;
+        const u32x2 raw = *reinterpret_cast<const u32x2*>(kp + 32 * ss);
         c[mb] = mfma16x16x32(e4m3x8_to_bf16(raw[0], raw[1]), qf[s], c[mb]);
       }
     }
@@ -599,7 +613,7 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
       const unsigned char* vp = buf + 32 * kk * kFp8Row + v_lane_off;
 #pragma unroll
       for (int db = 0; db < 16; ++db) {
-        const u32x2 raw = lds_read_tr8(vp + 16 * db);
+        const u32x2 raw = lds_read_tr8(vp + 16 * db + (db < 8 ? v_sw : -v_sw));
         o[db] = mfma16x16x32(e4m3x8_to_bf16(raw[0], raw[1]), pb[kk], o[db]);
       }
     }

@@ -60,31 +60,30 @@ __device__ __forceinline__ bf16x8 key_operand(const KeyTile<kFp8>& kt, int s) {
   else return as_bf16x8(kt.v[s]);
 }
 
-// Queries handled by one wave: two at most, so that Q (32 VGPRs per query), a three-tile
-// prefetch ring and the accumulators fit two waves per SIMD.
-template <int S>
-struct SweepShape {
-  static constexpr int kQpw = S < 2 ? S : 2;
-  static constexpr int kGroups = (S + kQpw - 1) / kQpw;
-  static constexpr int kThreads = 256 * kGroups;
-};
+// One workgroup = 4 waves; each wave streams its own pages and scores them for all S
+// queries.  Q lives in LDS (one padded 272-byte row per (query, head), so the 32 heads a
+// fragment read touches fall on different banks), which leaves the registers to a four-tile
+// prefetch ring and the accumulators at two waves per SIMD, with no page read twice and no
+// barrier in the loop.
+constexpr int kSweepThreads = 256;
+constexpr int kQRowBytes = kIdxDim * 2 + 16;
 
 template <int S, bool kFp8>
-__global__ __launch_bounds__(SweepShape<S>::kThreads) void index_score_kernel(
+__global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const int32_t* __restrict__ ctx_lens, const uint8_t* __restrict__ idx_pool,
     const int32_t* __restrict__ idx_block_table, int max_pages, int64_t num_idx_blocks, int B,
     float* __restrict__ scores, int64_t lmax, uint32_t* __restrict__ hist,
     int32_t* __restrict__ err) {
-  using Shape = SweepShape<S>;
-  constexpr int kQpw = Shape::kQpw;
-  constexpr int kThreads = Shape::kThreads;
   constexpr int kBlkBytes = kFp8 ? kIdxFp8Block : kIdxBf16Block;
   constexpr int kRing = 4;  // tiles in flight per wave (current + 3 ahead)
+  constexpr int kTilesPerWave = 2 * kPagesPerItem / 4;
+  static_assert(kTilesPerWave % kRing == 0, "whole ring rounds");
   // 16-bit LDS counters, two bins per word: one workgroup sees at most 4,096 tokens.
   __shared__ uint32_t lhist[S][kHistBins / 2];
   __shared__ __align__(16) float lw[S][kIdxHeads];  // half the head weights (see epilogue)
   __shared__ int32_t lblk[kPagesPerItem];
+  __shared__ __align__(16) unsigned char lq[S * kIdxHeads * kQRowBytes];
 
   const int b = blockIdx.x % B;
   const int item = blockIdx.x / B;
@@ -98,7 +97,7 @@ __global__ __launch_bounds__(SweepShape<S>::kThreads) void index_score_kernel(
   if (p_begin >= n_pages) return;
   const int p_end = min(n_pages, p_begin + kPagesPerItem);
 
-  for (int i = threadIdx.x; i < S * kHistBins / 2; i += kThreads) (&lhist[0][0])[i] = 0;
+  for (int i = threadIdx.x; i < S * kHistBins / 2; i += kSweepThreads) (&lhist[0][0])[i] = 0;
   if (threadIdx.x < S * kIdxHeads)
     (&lw[0][0])[threadIdx.x] = 0.5f * w[b * S * kIdxHeads + threadIdx.x];
   if (threadIdx.x < kPagesPerItem) {
@@ -113,33 +112,30 @@ __global__ __launch_bounds__(SweepShape<S>::kThreads) void index_score_kernel(
     }
     lblk[threadIdx.x] = blk;
   }
+  // Q rows (query j, head h) of 128 bf16, 16-byte pieces
+  for (int i = threadIdx.x; i < S * kIdxHeads * 16; i += kSweepThreads) {
+    const int row = i >> 4, pc = i & 15;
+    *reinterpret_cast<u32x4*>(lq + row * kQRowBytes + 16 * pc) =
+        *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)b * S * kIdxHeads + row) * kIdxDim + 8 * pc);
+  }
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int stream = wave & 3, group = wave >> 2;
-  const int j0 = group * kQpw;
   const int half = lane >> 5, col = lane & 31;
-
-  // A operand: Q[j][head = col][dims 64*half + 8*s .. +8] for k-step s.
-  bf16x8 qa[kQpw][8];
-#pragma unroll
-  for (int jj = 0; jj < kQpw; ++jj) {
-    const int j = min(j0 + jj, S - 1);
-    const uint16_t* qp = q_idx + ((int64_t)(b * S + j) * kIdxHeads + col) * kIdxDim + 64 * half;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qa[jj][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 8 * s));
-  }
   __syncthreads();
 
-  // Each wave walks a fixed number of tiles: tile k is half (k & 1) of page
-  // p_begin + stream + 4 * (k >> 1).  Tiles past the workgroup's pages (or on a bad block) read
-  // block 0 and are masked, so there are no branches around the loads and the prefetch ring
-  // stays in flight.
-  constexpr int kTilesPerWave = 2 * kPagesPerItem / 4;
+  // Tile k of this wave is half (k & 1) of page p_begin + wave + 4 * (k >> 1).  Tiles past the
+  // workgroup's pages (or on a bad block) read block 0 and are masked, so there are no branches
+  // around the loads and the prefetch ring stays in flight.
   auto tile_src = [&](int k, int& t0) -> const uint8_t* {
-    const int rel = stream + 4 * (k >> 1);
+    const int rel = wave + 4 * (k >> 1);
     const int32_t blk = lblk[rel];
     t0 = blk >= 0 ? (p_begin + rel) * kBlock + (k & 1) * 32 : INT32_MAX / 2;
     return idx_pool + (int64_t)(blk >= 0 ? blk : 0) * kBlkBytes;
+  };
+  // A operand of k-step s for query j: Q[j][head = col][dims 64*half + 8*s .. +8]
+  const unsigned char* qlane = lq + col * kQRowBytes + 128 * half;
+  auto q_frag = [&](int j, int s) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(qlane + j * kIdxHeads * kQRowBytes + 16 * s));
   };
 
   KeyTile<kFp8> ring[kRing];
@@ -148,59 +144,72 @@ __global__ __launch_bounds__(SweepShape<S>::kThreads) void index_score_kernel(
   for (int u = 0; u < kRing - 1; ++u)
     load_key_tile<kFp8>(ring[u], tile_src(u, ring_t0[u]), (u & 1) * 32 + col, half);
   for (int k0 = 0; k0 < kTilesPerWave; k0 += kRing) {
-    // Both query groups read the same pages; keeping them within one ring round of each other
-    // lets the second group's reads hit in L2 instead of going to HBM again.
-    if constexpr (Shape::kGroups > 1) __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
       const int k = k0 + u;
-      if (k < kTilesPerWave) {  // uniform; only the last round of a ragged ring is partial
-        const int un = (u + kRing - 1) % kRing;
-        const int kn = min(k + kRing - 1, kTilesPerWave - 1);
-        load_key_tile<kFp8>(ring[un], tile_src(kn, ring_t0[un]), (kn & 1) * 32 + col, half);
-        const int t = ring_t0[u] + col;
-        f32x16 acc[kQpw];
+      const int un = (u + kRing - 1) % kRing;
+      const int kn = min(k + kRing - 1, kTilesPerWave - 1);
+      load_key_tile<kFp8>(ring[un], tile_src(kn, ring_t0[un]), (kn & 1) * 32 + col, half);
+      const int t = ring_t0[u] + col;
+      f32x16 acc[S];
 #pragma unroll
-        for (int jj = 0; jj < kQpw; ++jj) acc[jj] = f32x16{};
+      for (int j = 0; j < S; ++j) acc[j] = f32x16{};
+      // Q fragments are read one k-step ahead of their MFMAs (bounded so that the reads do not
+      // all hoist and take the ring's registers)
+      bf16x8 qcur[S], qnext[S];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const bf16x8 kb = key_operand<kFp8>(ring[u], s);
+      for (int j = 0; j < S; ++j) qcur[j] = q_frag(j, 0);
 #pragma unroll
-          for (int jj = 0; jj < kQpw; ++jj) acc[jj] = mfma32x32x16(qa[jj][s], kb, acc[jj]);
+      for (int s = 0; s < 8; ++s) {
+        if (s < 7) {
+#pragma unroll
+          for (int j = 0; j < S; ++j) qnext[j] = q_frag(j, s + 1);
         }
+        const bf16x8 kb = key_operand<kFp8>(ring[u], s);
 #pragma unroll
-        for (int jj = 0; jj < kQpw; ++jj) {
-          const int j = j0 + jj;
-          if (j >= S) break;
-          // w * max(c, 0) == (w / 2) * (c + |c|): both factors are exact power-of-two
-          // rescalings, so the products round identically; c + |c| needs no NaN canonicalising
-          float part = 0.0f;
+        for (int j = 0; j < S; ++j) acc[j] = mfma32x32x16(qcur[j], kb, acc[j]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 wv = *reinterpret_cast<const f32x4*>(&lw[j][8 * g4 + 4 * half]);
+        for (int j = 0; j < S; ++j) qcur[j] = qnext[j];
+      }
+      // w * max(c, 0) == (w / 2) * (c + |c|): both factors are exact power-of-two
+      // rescalings, so the products round identically; c + |c| needs no NaN canonicalising
+      float part[S];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float c = acc[jj][4 * g4 + i];
-              part = __builtin_fmaf(wv[i], c + __builtin_fabsf(c), part);
-            }
+      for (int j = 0; j < S; ++j) {
+        part[j] = 0.0f;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 wv = *reinterpret_cast<const f32x4*>(&lw[j][8 * g4 + 4 * half]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float c = acc[j][4 * g4 + i];
+            part[j] = __builtin_fmaf(wv[i], c + __builtin_fabsf(c), part[j]);
           }
-          // add the other half's 16 heads of the same token (lane l ^ 32)
-          auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
-                                                     false, false);
-          const float total = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * ring[u].scale;
-          // scores are >= 0: clearing the sign bit maps -0 to +0
-          const uint32_t bits = __float_as_uint(total) & 0x7fffffffu;
-          if (half == 0 && t < L - S + 1 + j) {
-            scores[(int64_t)(b * S + j) * lmax + t] = __uint_as_float(bits);
-            const uint32_t bin = bits >> kHistShift;
-            atomicAdd(&lhist[j][bin >> 1], 1u << (16 * (bin & 1)));
-          }
+        }
+      }
+      // Add the other half's 16 heads of the same token (lane l ^ 32).  For a pair of queries
+      // the swap leaves the first one's total in lanes 0-31 and the second's in lanes 32-63,
+      // so one store and one histogram update serve both; an odd last query goes alone.
+#pragma unroll
+      for (int jp = 0; jp < S; jp += 2) {
+        const int jq = min(jp + 1, S - 1);
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[jp]),
+                                                   __float_as_uint(part[jq]), false, false);
+        const float total = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * ring[u].scale;
+        // scores are >= 0: clearing the sign bit maps -0 to +0
+        const uint32_t bits = __float_as_uint(total) & 0x7fffffffu;
+        const int j = jp + half;
+        if (j <= jq && (jq > jp || half == 0) && t < L - S + 1 + j) {
+          scores[(int64_t)(b * S + j) * lmax + t] = __uint_as_float(bits);
+          const uint32_t bin = bits >> kHistShift;
+          atomicAdd(&lhist[j][bin >> 1], 1u << (16 * (bin & 1)));
         }
       }
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < S * kHistBins / 2; i += kThreads) {
+  for (int i = threadIdx.x; i < S * kHistBins / 2; i += kSweepThreads) {
     const uint32_t v = (&lhist[0][0])[i];
     if (v == 0) continue;
     const int j = i / (kHistBins / 2), pair = i % (kHistBins / 2);
@@ -431,7 +440,7 @@ hipError_t launch_scores(const hs_ctx* ctx, const void* q_idx, const float* w,
                          const int32_t* ctx_lens, int B, hipStream_t stream) {
   const hs_config& c = ctx->cfg;
   const int items = (c.max_pages_per_req + kPagesPerItem - 1) / kPagesPerItem;
-  dim3 grid((unsigned)(B * items)), block(SweepShape<S>::kThreads);
+  dim3 grid((unsigned)(B * items)), block(kSweepThreads);
   hs_timer_mark(ctx, HS_KERNEL_INDEX_SCORE, true, stream);
   hipLaunchKernelGGL((index_score_kernel<S, kFp8>), grid, block, 0, stream,
                      static_cast<const uint16_t*>(q_idx), w, ctx_lens,
