@@ -20,9 +20,10 @@
 //
 // Select: one workgroup per (request, query).  The histogram gives the threshold bin; one
 // pass over the scores marks the tokens above it in a bitmap (wave ballots) and collects the
-// bin's tokens on chip, where a bitonic sort by (score desc, token asc) picks the rest.  If
-// the bin is too large for the chip, a general radix refinement over the remaining bits and
-// an index-ordered pass for exact ties does the same.  The bitmap is then emitted in order.
+// bin's tokens on chip, where a radix select over the key's remaining 19 bits and a token
+// order among equal keys pick the rest.  If the bin is too large for the chip, the same
+// refinement runs over the scores in memory, with an index-ordered pass for exact ties.  The
+// bitmap is then emitted in order.
 #include "hs_device.h"
 #include "hs_internal.h"
 
@@ -307,8 +308,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     // ---- fast path: one pass, bin beta collected on chip
     if (tid == 0) sh.misc[2] = 0;
     __syncthreads();
-    // 8 chunks per round: all loads of a round are in flight together
-    constexpr int kPer = 8;
+    // 16 chunks per round: all loads of a round are in flight together
+    constexpr int kPer = 16;
     for (int c0 = 0; c0 < n_chunks; c0 += kPer) {
       uint32_t keys[kPer];
 #pragma unroll
@@ -341,30 +342,49 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     __syncthreads();
     const int n = min(sh.misc[2], cand_cap);
     if (tid == 0 && n != cnt_beta) raise_error(err, HS_DEVERR_TOPK_COUNT);
-    int n2 = 1;
-    while (n2 < n) n2 <<= 1;
-    for (int i = n + tid; i < n2; i += kSelThreads) cand[i] = 0;
-    __syncthreads();
-    // bitonic sort, descending
-    for (int k = 2; k <= n2; k <<= 1) {
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        for (int i = tid; i < n2; i += kSelThreads) {
-          const int ixj = i ^ jj;
-          if (ixj > i) {
-            const uint64_t a = cand[i], c2 = cand[ixj];
-            const bool desc = (i & k) == 0;
-            if (desc ? (a < c2) : (a > c2)) {
-              cand[i] = c2;
-              cand[ixj] = a;
-            }
-          }
-        }
-        __syncthreads();
+    // The `need` largest candidates by (key desc, token asc): every candidate's key starts
+    // with the digit beta, so the other 19 bits are refined on chip in two digits (10 + 9)
+    // down to the need-th largest key T; keys above T are taken, and among keys equal to T
+    // the ones with the smallest tokens.
+    uint32_t prefix = (uint32_t)beta;
+    int shift = kHistShift;  // key bits above `shift` are fixed by `prefix`
+    int need_left = need;
+    const int digit_bits[2] = {10, 9};
+    for (int d = 0; d < 2; ++d) {
+      const int dshift = shift - digit_bits[d];
+      const int nb = 1 << digit_bits[d];
+      for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < n; i += kSelThreads) {
+        const uint32_t key = (uint32_t)(cand[i] >> 32);
+        if ((key >> shift) == prefix) atomicAdd(&sh.hist[(key >> dshift) & (nb - 1)], 1u);
       }
+      __syncthreads();
+      int ab;
+      const int dig = find_threshold_bin(sh, nb, need_left, &ab);
+      need_left -= ab;
+      prefix = (prefix << digit_bits[d]) | (uint32_t)max(dig, 0);
+      shift = dshift;
     }
-    for (int i = tid; i < need && i < n; i += kSelThreads) {
-      const uint32_t t = ~(uint32_t)(cand[i] & 0xffffffffu);
-      atomicOr(&bm[t >> 5], 1u << (t & 31));
+    const uint32_t T = prefix;
+    // keys above T are taken; the tokens of keys equal to T are listed (in sh.hist, free now)
+    if (tid == 0) sh.misc[3] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kSelThreads) {
+      const uint64_t ci = cand[i];
+      const uint32_t key = (uint32_t)(ci >> 32), t = ~(uint32_t)ci;
+      if (key > T) atomicOr(&bm[t >> 5], 1u << (t & 31));
+      else if (key == T) sh.hist[atomicAdd(&sh.misc[3], 1)] = t;
+    }
+    __syncthreads();
+    // of those, the need_left smallest tokens (all of them unless the ties straddle K)
+    const int n_eq = sh.misc[3];
+    for (int e = tid; e < n_eq; e += kSelThreads) {
+      const uint32_t t = sh.hist[e];
+      int rank = 0;
+      if (n_eq > need_left)
+        for (int m = 0; m < n_eq; ++m) rank += sh.hist[m] < t ? 1 : 0;
+      if (rank < need_left) atomicOr(&bm[t >> 5], 1u << (t & 31));
     }
   } else {
     // ---- general path: refine the threshold over the remaining 19 bits, then an ordered
@@ -456,13 +476,10 @@ hipError_t launch_scores(const hs_ctx* ctx, const void* q_idx, const float* w,
 
 using namespace hs;
 
-// On-chip candidate capacity of the select: a power of two (the bitonic sort's size).
+// On-chip candidate capacity of the select.
 int hs_select_cand_cap(const hs_config& c) {
-  int want = c.topk_lds_candidates > 0 ? c.topk_lds_candidates : kDefaultCandCap;
-  if (want > kDefaultCandCap) want = kDefaultCandCap;
-  int cap = 1;
-  while (cap * 2 <= want) cap *= 2;
-  return cap;
+  const int want = c.topk_lds_candidates > 0 ? c.topk_lds_candidates : kDefaultCandCap;
+  return want < kDefaultCandCap ? want : kDefaultCandCap;
 }
 
 hipError_t hs_launch_index_topk(const hs_ctx* ctx, const void* q_idx, const float* w,
