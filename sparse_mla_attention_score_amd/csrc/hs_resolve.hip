@@ -13,8 +13,8 @@
 // not touch the LRU; victims are the slots untouched in this call in (stamp, slot) order,
 // empty slots first; the i-th miss in ascending token order takes the i-th victim.
 //
-// Implementation: one 1,024-thread workgroup per request decides, a second kernel copies.  The S top-K lists are merged into
-// their sorted union on chip (bitonic sort + compaction).  The (stamp, slot) order is kept as
+// Implementation: one 1,024-thread workgroup per request decides, a second kernel copies.  The
+// S top-K lists become their sorted union through a token bitmap of the request.  The (stamp, slot) order is kept as
 // an explicit recency list of slots, double-buffered by the parity of the call counter: the
 // victims are the first untouched entries of the old list, and the new list is the untouched
 // entries in old order followed by the touched slots in ascending slot order, which is the
@@ -53,7 +53,8 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     int32_t* __restrict__ tok2slot, int64_t lmax, int32_t* __restrict__ req_step,
     int32_t* __restrict__ req_used, int32_t* __restrict__ miss_src, int32_t* __restrict__ miss_dst,
     int32_t* __restrict__ miss_cnt, int union_cap, int32_t* __restrict__ row_ids,
-    int32_t* __restrict__ stats, int32_t* __restrict__ err) {
+    int32_t* __restrict__ stats, uint32_t* __restrict__ ubits, int64_t ubits_stride,
+    int32_t* __restrict__ err) {
   extern __shared__ __align__(16) unsigned char dyn[];
   // union_cap (a power of two, >= S*K and >= 1024) entries each: sorted union U, per-token
   // row or miss code `cls` (also the staging area of the input lists), miss source row,
@@ -90,80 +91,37 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     return;
   }
 
-  // ---- 1. sorted union of the S ascending lists.  Invalid entries (-1 padding, tokens
-  // outside [0, Lb)) become INT32_MAX and sort last.  The lists are staged in `cls`.
+  // ---- 1. sorted union of the S lists through a token bitmap of the request (workspace
+  // scratch): a bit per selected token, then the set bits read out in order.  Padding (-1)
+  // is skipped; tokens outside [0, Lb) are flagged and skipped.
   const int n_in = S * K;
+  const int n_words = (Lb + 31) >> 5;
+  uint32_t* ub = ubits + (int64_t)b * ubits_stride;
   if (tid < 8) cnt[tid] = 0;
-  for (int i = tid; i < union_cap; i += kResThreads) {
-    int32_t t = i < n_in ? tk[i] : -1;
-    if (t >= Lb) {
-      raise_error(err, HS_DEVERR_BAD_ROW);
-      t = -1;
-    }
-    cls[i] = t < 0 ? INT32_MAX : t;
-  }
+  for (int i = tid; i < n_words; i += kResThreads) ub[i] = 0u;
   for (int i = tid; i < H; i += kResThreads) flag[i] = 0;
-  __syncthreads();
-  for (int i = tid; i < n_in; i += kResThreads)
-    if (i % K != 0 && cls[i - 1] > cls[i]) cnt[7] = 1;  // a list is not ascending
-  __syncthreads();
-  if (cnt[7] == 0) {
-    // stable merge by rank: entry k of list j lands at k plus, for every other list, the
-    // number of its entries before it (ties go to the lower list)
-    for (int i = tid; i < n_in; i += kResThreads) {
-      const int j = i / K, k = i - j * K;
-      const int32_t x = cls[i];
-      int pos = k;
-      for (int jj = 0; jj < S; ++jj)
-        if (jj != j) pos += count_below(cls + jj * K, K, x, jj < j);
-      U[pos] = x;
-    }
-    for (int i = n_in + tid; i < union_cap; i += kResThreads) U[i] = INT32_MAX;
-    __syncthreads();
-  } else {  // out-of-contract input: sort the concatenation
-    for (int i = tid; i < union_cap; i += kResThreads) U[i] = cls[i];
-    __syncthreads();
-    for (int k = 2; k <= union_cap; k <<= 1) {
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        for (int i = tid; i < union_cap; i += kResThreads) {
-          const int ixj = i ^ jj;
-          if (ixj > i) {
-            const int32_t a = U[i], c = U[ixj];
-            const bool asc = (i & k) == 0;
-            if (asc ? (a > c) : (a < c)) {
-              U[i] = c;
-              U[ixj] = a;
-            }
-          }
-        }
-        __syncthreads();
-      }
-    }
+  __syncthreads();  // the zeroing stores have completed before any bit is set
+  for (int i = tid; i < n_in; i += kResThreads) {
+    const int32_t t = tk[i];
+    if (t >= Lb) raise_error(err, HS_DEVERR_BAD_ROW);
+    else if (t >= 0) atomicOr(&ub[t >> 5], 1u << (t & 31));
   }
-  // in-place compaction of distinct valid entries; each thread owns a contiguous run
+  __syncthreads();  // the atomics were performed in L2; the words are read back at agent scope
   int nU;
   {
-    const int per = union_cap / kResThreads;
-    const int i0 = tid * per;
-    int32_t v[kPerU];
-    int32_t prev = i0 > 0 ? U[i0 - 1] : INT32_MIN;
-    int keep = 0;
-#pragma unroll
-    for (int e = 0; e < kPerU; ++e) {
-      v[e] = INT32_MAX;
-      if (e < per) v[e] = U[i0 + e];
-    }
-#pragma unroll
-    for (int e = 0; e < kPerU; ++e) {
-      const int32_t pe = e == 0 ? prev : v[e - 1];
-      if (e < per && v[e] != INT32_MAX && v[e] != pe) ++keep;
-    }
+    const int per = (n_words + kResThreads - 1) / kResThreads;
+    const int w0 = min(n_words, tid * per), w1 = min(n_words, w0 + per);
+    int c = 0;
+    for (int wd = w0; wd < w1; ++wd) c += __popc(load_agent(&ub[wd]));
     int tot;
-    int pos = block_exclusive_scan<kResThreads>(keep, scan, &tot);  // all reads done before
-#pragma unroll
-    for (int e = 0; e < kPerU; ++e) {
-      const int32_t pe = e == 0 ? prev : v[e - 1];
-      if (e < per && v[e] != INT32_MAX && v[e] != pe) U[pos++] = v[e];
+    int pos = block_exclusive_scan<kResThreads>(c, scan, &tot);
+    for (int wd = w0; wd < w1; ++wd) {
+      uint32_t v = load_agent(&ub[wd]);
+      while (v) {
+        const int bit = __ffs(v) - 1;
+        v &= v - 1;
+        U[pos++] = wd * 32 + bit;
+      }
     }
     nU = tot;
     __syncthreads();
@@ -454,7 +412,8 @@ hipError_t hs_launch_resolve(const hs_ctx* ctx, const int32_t* topk, const int32
                      (int64_t)c.num_host_blocks, c.max_batch, ctx->ws.slot_token,
                      ctx->ws.slot_stamp, ctx->ws.lru_order, ctx->ws.tok2slot, ctx->lay.lmax,
                      ctx->ws.req_step, ctx->ws.req_used, ctx->ws.miss_src, ctx->ws.miss_dst,
-                     ctx->ws.miss_cnt, cap, row_ids, stats, ctx->ws.err);
+                     ctx->ws.miss_cnt, cap, row_ids, stats, ctx->ws.bitmap,
+                     (int64_t)c.max_queries * ctx->lay.bm_words, ctx->ws.err);
   hs_timer_mark(ctx, HS_KERNEL_RESOLVE, false, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || c.num_host_blocks == 0) return e;
