@@ -19,11 +19,14 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, 
          "-Wall", "-Wno-unused-function",
          # packed fp32 instructions stay off (plain fp32 code only)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source additions.  The sweep keeps its MFMA accumulators in VGPRs: read back from AGPRs
+# they would cost one VALU move per accumulator element and tile.
+SOURCE_FLAGS = {"hs_index_topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                      if "not a recognized feature for this target" not in l)

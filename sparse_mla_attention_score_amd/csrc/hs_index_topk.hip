@@ -8,14 +8,13 @@
 // and the selection is the min(K, L_j) tokens ranked by (score desc, token asc), emitted in
 // ascending token order.
 //
-// Sweep: one workgroup scores 64 pages (4,096 tokens) of one request for all S queries: four
-// waves stream pages for each group of (at most) two queries, and the groups stay within one
-// prefetch round of each other so that each page comes from HBM once.  The contraction
+// Sweep: one workgroup scores 64 pages (4,096 tokens) of one request for all S queries; each
+// of its four waves streams 16 of the pages, so each page comes from HBM once.  The contraction
 // [S*32 heads x 128] x [128 x tokens] runs on bf16 MFMA (32x32x16): FP8 keys are converted to
 // bf16 exactly, the per-token fp32 scale is applied after the ReLU (positive scales commute
 // with it).  Lane l reads 64 contiguous key bytes of token l%32 (dims 64*(l/32) .. +64); the
-// 128 dims are assigned to MFMA k-slots in that order, and the queries held in registers use
-// the same assignment.  Scores go to a per-(request, query) scratch row; their first radix
+// 128 dims are assigned to MFMA k-slots in that order, and the query fragments read from LDS
+// use the same assignment.  Scores go to a per-(request, query) scratch row; their first radix
 // digit (bits [30:19]) is counted in LDS and added to a global histogram.
 //
 // Select: one workgroup per (request, query).  The histogram gives the threshold bin; one
@@ -62,10 +61,14 @@ __device__ __forceinline__ bf16x8 key_operand(const KeyTile<kFp8>& kt, int s) {
 }
 
 // One workgroup = 4 waves; each wave streams its own pages and scores them for all S
-// queries.  Q lives in LDS (one padded 272-byte row per (query, head), so the 32 heads a
-// fragment read touches fall on different banks), which leaves the registers to a four-tile
-// prefetch ring and the accumulators at two waves per SIMD, with no page read twice and no
-// barrier in the loop.
+// queries, so no page is read twice and the loop has no barrier.  Q lives in LDS (one padded
+// 272-byte row per (query, head), so the 32 heads a fragment read touches fall on different
+// banks).  Per tile, the key operands are converted once; then each query runs a chain of 8
+// MFMAs while the previous query's weighted ReLU sum (VALU) runs beside it, the last query's
+// sum overlapping the next tile's first chain.  The slot a tile came from is refilled right
+// after its conversion, so two tiles stay in flight behind the one being scored.  With FP8
+// keys the 16 head weights each lane needs per query stay in registers; bf16 tiles are twice
+// as large and read the weights from LDS instead.  All of it fits two waves per SIMD.
 constexpr int kSweepThreads = 256;
 constexpr int kQRowBytes = kIdxDim * 2 + 16;
 
@@ -77,12 +80,13 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
     float* __restrict__ scores, int64_t lmax, uint32_t* __restrict__ hist,
     int32_t* __restrict__ err) {
   constexpr int kBlkBytes = kFp8 ? kIdxFp8Block : kIdxBf16Block;
-  constexpr int kRing = 4;  // tiles in flight per wave (current + 3 ahead)
+  constexpr int kRing = 2;  // tile slots per wave
   constexpr int kTilesPerWave = 2 * kPagesPerItem / 4;
   static_assert(kTilesPerWave % kRing == 0, "whole ring rounds");
+  constexpr bool kWeightsInRegs = kFp8;
   // 16-bit LDS counters, two bins per word: one workgroup sees at most 4,096 tokens.
   __shared__ uint32_t lhist[S][kHistBins / 2];
-  __shared__ __align__(16) float lw[S][kIdxHeads];  // half the head weights (see epilogue)
+  __shared__ __align__(16) float lw[S][kIdxHeads];  // half the head weights (see finish)
   __shared__ int32_t lblk[kPagesPerItem];
   __shared__ __align__(16) unsigned char lq[S * kIdxHeads * kQRowBytes];
 
@@ -133,82 +137,108 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
     t0 = blk >= 0 ? (p_begin + rel) * kBlock + (k & 1) * 32 : INT32_MAX / 2;
     return idx_pool + (int64_t)(blk >= 0 ? blk : 0) * kBlkBytes;
   };
-  // A operand of k-step s for query j: Q[j][head = col][dims 64*half + 8*s .. +8]
-  const unsigned char* qlane = lq + col * kQRowBytes + 128 * half;
-  auto q_frag = [&](int j, int s) {
-    return as_bf16x8(*reinterpret_cast<const u32x4*>(qlane + j * kIdxHeads * kQRowBytes + 16 * s));
-  };
 
+  // Weights lane (col, half) applies to query j: heads 8 g4 + 4 half .. +4, g4 = 0..3.
+  f32x4 wreg[kWeightsInRegs ? S : 1][4];
+  if constexpr (kWeightsInRegs) {
+#pragma unroll
+    for (int j = 0; j < S; ++j)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) wreg[j][g4] = *reinterpret_cast<const f32x4*>(&lw[j][8 * g4 + 4 * half]);
+  }
+  // LDS offsets of this lane's Q (and weight) reads.  They are made opaque again every tile:
+  // otherwise the loop-invariant reads are hoisted out of the loop, and all of Q does not fit
+  // the registers.
+  int q_off = col * kQRowBytes + 128 * half, w_off = half;
+
+  // Slot u % kRing holds tile u from its load (issued once tile u - kRing is converted) until
+  // its own conversion.
   KeyTile<kFp8> ring[kRing];
   int ring_t0[kRing];
 #pragma unroll
-  for (int u = 0; u < kRing - 1; ++u)
+  for (int u = 0; u < kRing; ++u)
     load_key_tile<kFp8>(ring[u], tile_src(u, ring_t0[u]), (u & 1) * 32 + col, half);
+
+  f32x16 acc[S];
+  float part[S];
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    acc[j] = f32x16{};
+    part[j] = 0.0f;
+  }
+  // Weighted ReLU sum of query j over the lane's 16 heads, then (after the second query of a
+  // pair, or a lone last query) the store and histogram update of token t.
+  // w * max(c, 0) == (w / 2) * (c + |c|): both factors are exact power-of-two rescalings, so
+  // the products round identically; c + |c| needs no NaN canonicalising.
+  auto finish = [&](int j, int t, float sc) {
+    float p = 0.0f;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      f32x4 wv;
+      if constexpr (kWeightsInRegs) wv = wreg[j][g4];
+      else wv = reinterpret_cast<const f32x4*>(&lw[j][8 * g4])[w_off];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float c = acc[j][4 * g4 + i];
+        p = __builtin_fmaf(wv[i], c + __builtin_fabsf(c), p);
+      }
+    }
+    part[j] = p;
+    if ((j & 1) || j == S - 1) {
+      // Add the other half's 16 heads of the same token (lane l ^ 32).  The swap leaves the
+      // first query's total in lanes 0-31 and the second's in lanes 32-63, so one store and
+      // one histogram update serve both.
+      const int jp = j & ~1, jq = j;
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[jp]), __float_as_uint(part[jq]),
+                                                 false, false);
+      const float total = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * sc;
+      // scores are >= 0: clearing the sign bit maps -0 to +0
+      const uint32_t bits = __float_as_uint(total) & 0x7fffffffu;
+      const int jj = jp + half;
+      if (jj <= jq && (jq > jp || half == 0) && t < L - S + 1 + jj) {
+        scores[(int64_t)(b * S + jj) * lmax + t] = __uint_as_float(bits);
+        const uint32_t bin = bits >> kHistShift;
+        atomicAdd(&lhist[jj][bin >> 1], 1u << (16 * (bin & 1)));
+      }
+    }
+  };
+
+  // The last query's sum of tile k runs during tile k + 1 (before the first tile it is a
+  // masked no-op on zero accumulators); with one query there is nothing to overlap.
+  int t_prev = INT32_MAX / 2;
+  float sc_prev = 0.0f;
   for (int k0 = 0; k0 < kTilesPerWave; k0 += kRing) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
       const int k = k0 + u;
-      const int un = (u + kRing - 1) % kRing;
-      const int kn = min(k + kRing - 1, kTilesPerWave - 1);
-      load_key_tile<kFp8>(ring[un], tile_src(kn, ring_t0[un]), (kn & 1) * 32 + col, half);
       const int t = ring_t0[u] + col;
-      f32x16 acc[S];
+      const float sc = ring[u].scale;
+      asm volatile("" : "+v"(q_off), "+v"(w_off));
+      bf16x8 kb[8];
 #pragma unroll
-      for (int j = 0; j < S; ++j) acc[j] = f32x16{};
-      // Q fragments are read one k-step ahead of their MFMAs (bounded so that the reads do not
-      // all hoist and take the ring's registers)
-      bf16x8 qcur[S], qnext[S];
-#pragma unroll
-      for (int j = 0; j < S; ++j) qcur[j] = q_frag(j, 0);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        if (s < 7) {
-#pragma unroll
-          for (int j = 0; j < S; ++j) qnext[j] = q_frag(j, s + 1);
-        }
-        const bf16x8 kb = key_operand<kFp8>(ring[u], s);
-#pragma unroll
-        for (int j = 0; j < S; ++j) acc[j] = mfma32x32x16(qcur[j], kb, acc[j]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < S; ++j) qcur[j] = qnext[j];
-      }
-      // w * max(c, 0) == (w / 2) * (c + |c|): both factors are exact power-of-two
-      // rescalings, so the products round identically; c + |c| needs no NaN canonicalising
-      float part[S];
+      for (int s = 0; s < 8; ++s) kb[s] = key_operand<kFp8>(ring[u], s);
+      // refill the slot with tile k + kRing (the last round re-reads the final tile, masked
+      // by never being scored)
+      const int kn = min(k + kRing, kTilesPerWave - 1);
+      load_key_tile<kFp8>(ring[u], tile_src(kn, ring_t0[u]), (kn & 1) * 32 + col, half);
 #pragma unroll
       for (int j = 0; j < S; ++j) {
-        part[j] = 0.0f;
+        // A operand of k-step s for query j: Q[j][head = col][dims 64*half + 8*s .. +8]
+        f32x16 a = {};
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 wv = *reinterpret_cast<const f32x4*>(&lw[j][8 * g4 + 4 * half]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float c = acc[j][4 * g4 + i];
-            part[j] = __builtin_fmaf(wv[i], c + __builtin_fabsf(c), part[j]);
-          }
-        }
+        for (int s = 0; s < 8; ++s)
+          a = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(lq + q_off + j * kIdxHeads * kQRowBytes + 16 * s)),
+                           kb[s], a);
+        acc[j] = a;
+        if (S == 1) finish(0, t, sc);
+        else if (j > 0) finish(j - 1, t, sc);
+        else finish(S - 1, t_prev, sc_prev);
       }
-      // Add the other half's 16 heads of the same token (lane l ^ 32).  For a pair of queries
-      // the swap leaves the first one's total in lanes 0-31 and the second's in lanes 32-63,
-      // so one store and one histogram update serve both; an odd last query goes alone.
-#pragma unroll
-      for (int jp = 0; jp < S; jp += 2) {
-        const int jq = min(jp + 1, S - 1);
-        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[jp]),
-                                                   __float_as_uint(part[jq]), false, false);
-        const float total = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * ring[u].scale;
-        // scores are >= 0: clearing the sign bit maps -0 to +0
-        const uint32_t bits = __float_as_uint(total) & 0x7fffffffu;
-        const int j = jp + half;
-        if (j <= jq && (jq > jp || half == 0) && t < L - S + 1 + j) {
-          scores[(int64_t)(b * S + j) * lmax + t] = __uint_as_float(bits);
-          const uint32_t bin = bits >> kHistShift;
-          atomicAdd(&lhist[j][bin >> 1], 1u << (16 * (bin & 1)));
-        }
-      }
+      t_prev = t;
+      sc_prev = sc;
     }
   }
+  if (S > 1) finish(S - 1, t_prev, sc_prev);
   __syncthreads();
   for (int i = threadIdx.x; i < S * kHistBins / 2; i += kSweepThreads) {
     const uint32_t v = (&lhist[0][0])[i];

@@ -27,8 +27,9 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 
-# Sources each kernel is compiled from (its own file plus the shared headers).
-_SHARED = ["csrc/hs_device.h", "csrc/hs_internal.h", "../include/hisparse.h"]
+# Sources each kernel is compiled from (its own file, the shared headers, and the build script
+# that holds the compiler flags).
+_SHARED = ["csrc/hs_device.h", "csrc/hs_internal.h", "../include/hisparse.h", "build.py"]
 KERNEL_SOURCES = {
     "index_score_kernel": ["csrc/hs_index_topk.hip"] + _SHARED,
     "topk_select_kernel": ["csrc/hs_index_topk.hip"] + _SHARED,
