@@ -675,42 +675,53 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
 }
 
 // Combine the split partials of each query: M = max m_s, L = sum l_s 2^(m_s - M),
-// out = sum O_s 2^(m_s - M) / L, lse = (M + log2 L) ln 2.
+// out = sum O_s 2^(m_s - M) / L, lse = (M + log2 L) ln 2.  Workgroup = (query, 16 heads):
+// the factors go to LDS first, then consecutive threads stream consecutive 16-byte pieces.
+constexpr int kMergeHeads = 16;
+
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            int splits, uint16_t* __restrict__ out,
                                                            float* __restrict__ lse) {
-  const int bj = blockIdx.x;
-  const int h = threadIdx.x >> 2, qtr = threadIdx.x & 3;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) {
-    const float* ml = part_ml + (((int64_t)bj * splits + s) * kHeads + h) * 2;
-    if (ml[1] > 0.0f) M = fmaxf(M, ml[0]);
+  __shared__ float fac[kMaxSplits][kMergeHeads];  // 2^(m_s - M), 0 for an empty split
+  __shared__ float inv_l[kMergeHeads];
+  const int bj = blockIdx.x / (kHeads / kMergeHeads);
+  const int h0 = (blockIdx.x % (kHeads / kMergeHeads)) * kMergeHeads;
+  if (threadIdx.x < kMergeHeads) {
+    const int h = h0 + threadIdx.x;
+    float M = -INFINITY;
+    for (int s = 0; s < splits; ++s) {
+      const float* ml = part_ml + (((int64_t)bj * splits + s) * kHeads + h) * 2;
+      if (ml[1] > 0.0f) M = fmaxf(M, ml[0]);
+    }
+    float L = 0.0f;
+    for (int s = 0; s < splits; ++s) {
+      const float* ml = part_ml + (((int64_t)bj * splits + s) * kHeads + h) * 2;
+      const float f = ml[1] > 0.0f ? exp2f(ml[0] - M) : 0.0f;
+      fac[s][threadIdx.x] = f;
+      L += ml[1] * f;
+    }
+    inv_l[threadIdx.x] = L > 0.0f ? 1.0f / L : 0.0f;
+    if (lse) lse[(int64_t)bj * kHeads + h] = (M + log2f(L)) * 0.69314718055994531f;
   }
-  float L = 0.0f;
-  float f[kMaxSplits];
-  for (int s = 0; s < splits; ++s) {
-    const float* ml = part_ml + (((int64_t)bj * splits + s) * kHeads + h) * 2;
-    f[s] = ml[1] > 0.0f ? exp2f(ml[0] - M) : 0.0f;
-    L += ml[1] * f[s];
-  }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  uint16_t* op = out + ((int64_t)bj * kHeads + h) * kDv + 128 * qtr;
-  for (int d = 0; d < 128; d += 4) {
+  __syncthreads();
+  constexpr int kPieces = kMergeHeads * kDv / 4;  // f32x4 pieces of this workgroup's heads
+  for (int e = threadIdx.x; e < kPieces; e += 256) {
+    const int hl = e / (kDv / 4);
+    const int64_t off = ((int64_t)h0 + hl) * kDv + 4 * (e % (kDv / 4));
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < splits; ++s) {
-      if (f[s] == 0.0f) continue;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(
-          part_o + (((int64_t)bj * splits + s) * kHeads + h) * kDv + 128 * qtr + d);
-      acc += v * f[s];
+      const float f = fac[s][hl];
+      if (f == 0.0f) continue;
+      acc += *reinterpret_cast<const f32x4*>(part_o + ((int64_t)bj * splits + s) * kHeads * kDv + off) * f;
     }
+    const float inv = inv_l[hl];
     const __bf16 v0 = (__bf16)(acc[0] * inv), v1 = (__bf16)(acc[1] * inv);
     const __bf16 v2 = (__bf16)(acc[2] * inv), v3 = (__bf16)(acc[3] * inv);
     const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
     const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
-    *reinterpret_cast<u32x2*>(op + d) = u32x2{w0, w1};
+    *reinterpret_cast<u32x2*>(out + (int64_t)bj * kHeads * kDv + off) = u32x2{w0, w1};
   }
-  if (lse && qtr == 0) lse[(int64_t)bj * kHeads + h] = (M + log2f(L)) * 0.69314718055994531f;
 }
 
 }  // namespace
@@ -758,8 +769,8 @@ hipError_t hs_launch_decode(const hs_ctx* ctx, int layer, const void* q, const i
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   hs_timer_mark(ctx, HS_KERNEL_DECODE_MERGE, true, stream);
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(B * S)), dim3(256), 0, stream,
-                     ctx->ws.part_o, ctx->ws.part_ml, splits, static_cast<uint16_t*>(out), lse);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(B * S * (kHeads / kMergeHeads))), dim3(256), 0,
+                     stream, ctx->ws.part_o, ctx->ws.part_ml, splits, static_cast<uint16_t*>(out), lse);
   hs_timer_mark(ctx, HS_KERNEL_DECODE_MERGE, false, stream);
   return hipGetLastError();
 }
