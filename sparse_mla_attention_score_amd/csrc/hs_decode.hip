@@ -362,20 +362,24 @@ __global__ __launch_bounds__(kDecThreads) void sparse_mla_decode_kernel(
 //
 // A tile is fetched by direct global->LDS loads (16 bytes per lane; rows keep their stored
 // 656-byte pitch) one tile ahead of the tile being computed, so the gather's latency hides
-// behind the MFMAs and no registers hold rows in flight.  Operands are converted to bf16 exactly
-// as they are read: K with plain 8-byte reads (row-major), V^T with the transposing 8-byte read
-// (ds_read_b64_tr_b8: in each group of 16 lanes, lanes 2k and 2k+1 address the two halves of a
-// 16-byte segment of "row" k and lane r receives byte r of all eight segments), which hands a
-// lane the 8 rows of one value dim that its MFMA k-slots take.  The rows behind the k-slots are
+// behind the MFMAs and no registers hold rows in flight.  QK over the 512 nope dims runs on the
+// FP8 codes as stored (16x16x128 FP8 MFMAs, 32 bytes of a row per lane), the bf16 query carried
+// by two E4M3 parts with per-head power-of-two scales that together keep its 8 significant bits
+// (set up once per workgroup); the 64 rope dims stay bf16.  V^T is read with the transposing
+// 8-byte read (ds_read_b64_tr_b8: in each group of 16 lanes, lanes 2k and 2k+1 address the two
+// halves of a 16-byte segment of "row" k and lane r receives byte r of all eight segments), which
+// hands a lane the 8 rows of one value dim that its MFMA k-slots take, and converted to bf16
+// exactly for the PV product (the probabilities stay bf16: their FP8 parts would need scales per
+// 32 rows, which the output layout of QK does not group).  The rows behind the k-slots are
 // addressed in the order the probabilities come out of the QK result, so nothing is permuted in
 // memory.  Barriers between the waves wait for LDS traffic only, never for the prefetch.
 //
 // Work split: wave (hq, dh) holds Q for heads 16 hq .. +15 over half of the 576 QK dims (nope
 // 256 dh .. +255 and rope 32 dh .. +31) and accumulates O^T for those heads over value dims
-// 256 dh .. +255, on 16x16x32 bf16 MFMAs.  The two dim halves' partial scores are added through
-// LDS, after which both waves of a head group run the same softmax.  Holding a quarter of the
-// heads and half the dims keeps a wave under 256 registers, so two waves share each SIMD and
-// one's MFMAs overlap the other's conversions and softmax.
+// 256 dh .. +255.  The two dim halves' partial scores are added through LDS, after which both
+// waves of a head group run the same softmax.  Holding a quarter of the heads and half the dims
+// keeps a wave under 256 registers, so two waves share each SIMD and one's MFMAs overlap the
+// other's conversions and softmax.
 constexpr int kF8RowChunks = kFp8Row / 16;                   // 41 pieces of 16 bytes per row
 constexpr int kF8TileBytes = kTileRows * kFp8Row;            // 41,984
 constexpr int kF8TileLoads = kTileRows * kF8RowChunks / 64;  // 41 wave-wide loads per tile
@@ -425,6 +429,34 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const unsigned char* p) {
   const lds_i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
       (__attribute__((address_space(3))) lds_i32x2*)(p));
   return u32x2{(uint32_t)v[0], (uint32_t)v[1]};
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Four floats (|x| < 448) -> their OCP E4M3 codes, rounded to nearest even, one per byte
+// (element e in byte e); *v gets the values the codes stand for.
+__device__ __forceinline__ uint32_t pack_e4m3x4(const float* x, float* v) {
+  i16x2 w = {0, 0};
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x[0], x[1], 1.0f, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x[2], x[3], 1.0f, true);
+  const uint32_t code = (uint32_t)__builtin_bit_cast(int, w);
+  const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)code, 1.0f, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)code, 1.0f, true);
+  v[0] = lo[0];
+  v[1] = lo[1];
+  v[2] = hi[0];
+  v[3] = hi[1];
+  return code;
+}
+
+// C += A B^T-style 16x16x128 product of E4M3 operands, B scaled by 2^(scale_b - 127) (one
+// E8M0 scale per column of B).  Lane l holds A[l%16][32(l/16) .. +32] and B[32(l/16) .. +32][l%16],
+// byte j of its eight dwords being element j; c[i] = C[4(l/16)+i][l%16].
+__device__ __forceinline__ f32x4 mfma_f8_16x16x128(const i32x8& a, const i32x8& b, int scale_b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, scale_b);
 }
 
 constexpr int kF8Threads = 512;  // 8 waves: 4 groups of 16 heads x 2 halves of the dims
@@ -490,14 +522,54 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
     }
     rids[i] = v;
   }
-  // Q^T fragments (B operand): k-step s < 8 covers nope dims 256 dh + 32 s .. +31, s = 8 the
-  // rope dims 512 + 32 dh .. +31; lane group g holds 8 of the 32.
-  bf16x8 qf[9];
+  // Q^T for the nope dims, as the B operand of two FP8 k-steps of 128 dims (256 dh + 128 ks ..):
+  // lane group g holds dims 32 g .. +31 of the step for head `head`.  Each bf16 value q is
+  // carried by two E4M3 parts: q 2^E = hi + lo / 16, with one power of two E per head and
+  // k-step that puts the largest |q| in [128, 256).  hi keeps 4 significant bits, lo the next
+  // 4 of the remainder (|remainder| <= half a step of hi), so hi + lo / 16 carries bf16's 8; the
+  // MFMA's per-column E8M0 scales undo 2^E and the 16.  Rope dims 512 + 32 dh .. +31 stay
+  // bf16 (lane group g holds 8 of them).
+  i32x8 qh[2], ql[2];
+  int q_sh[2], q_sl[2];
+  bf16x8 q_rope;
   {
-    const uint16_t* qp = q + ((int64_t)bj * kHeads + head) * kDqk + 8 * g;
+    const uint16_t* qp = q + ((int64_t)bj * kHeads + head) * kDqk;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 256 * dh + 32 * s));
-    qf[8] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 512 + 32 * dh));
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint16_t* p = qp + 256 * dh + 128 * ks + 32 * g;
+      float x[32];
+      float m = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(p + 8 * v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[8 * v + 2 * e] = __uint_as_float(w[e] << 16);
+          x[8 * v + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 32; ++e) m = fmaxf(m, fabsf(x[e]));
+      m = fmaxf(m, __shfl_xor(m, 16));  // the head's maximum over the four lane groups
+      m = fmaxf(m, __shfl_xor(m, 32));
+      int E = 0;
+      if (m > 0.0f) E = 7 - ((int)((__float_as_uint(m) >> 23) & 255) - 127);
+      E = max(-120, min(E, 120));
+      const float sc = __builtin_ldexpf(1.0f, E);
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        float xs[4], hv[4], r[4], lv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xs[e] = x[4 * w + e] * sc;
+        qh[ks][w] = (int)pack_e4m3x4(xs, hv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = (xs[e] - hv[e]) * 16.0f;  // exact: |xs - hv| <= half a step
+        ql[ks][w] = (int)pack_e4m3x4(r, lv);
+      }
+      q_sh[ks] = 127 - E;
+      q_sl[ks] = 127 - E - 4;
+    }
+    q_rope = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 512 + 32 * dh + 8 * g));
   }
   f32x4 o[16];  // O^T for value dims 256 dh + 16 db + 4 g + i, head `head`
 #pragma unroll
@@ -507,7 +579,8 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
   // waits for them would otherwise sit inside the tile loop and also drain the prefetch.  (The
   // empty asm takes the fragments, so their loads cannot sink below this point.)
 #pragma unroll
-  for (int s = 0; s < 9; ++s) asm volatile("" : "+v"(qf[s]));
+  for (int ks = 0; ks < 2; ++ks) asm volatile("" : "+v"(qh[ks]), "+v"(ql[ks]));
+  asm volatile("" : "+v"(q_rope));
   wait_vmcnt<0>();
   asm volatile("" ::: "memory");
   __syncthreads();  // row ids staged
@@ -545,19 +618,23 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
       row_sc[tid] = *reinterpret_cast<const float*>(buf + tid * kFp8Row + 640);
       row_bias[tid] = (tid < nrows - t0 && rids[t0 + tid] >= 0) ? 0.0f : -INFINITY;
     }
-    // ---- partial S^T = K Q^T over this wave's dims: 4 blocks of 16 rows (mb), lane holds rows
-    // 16 mb + 4 g + i of head `head`
+    // ---- partial S^T = K Q^T over this wave's nope dims, on the FP8 codes as stored: 4 blocks
+    // of 16 rows (mb), lane holds rows 16 mb + 4 g + i of head `head`
     f32x4 c[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const unsigned char* kp = buf + (16 * mb + c16) * kFp8Row + 256 * dh + 8 * g;
+      const unsigned char* kp = buf + (16 * mb + c16) * kFp8Row + 256 * dh + 32 * g;
       c[mb] = f32x4{};
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        // rows of odd blocks have bit 4 set: their pieces 2s, 2s+1 sit at 2(s^4), 2(s^4)+1
-        const int ss = (mb & 1) ? (s ^ 4) : s;
-        const u32x2 raw = *reinterpret_cast<const u32x2*>(kp + 32 * ss);
-        c[mb] = mfma16x16x32(e4m3x8_to_bf16(raw[0], raw[1]), qf[s], c[mb]);
+      for (int ks = 0; ks < 2; ++ks) {
+        // rows of odd blocks have bit 4 set: their pieces 8 ks + 2 g (+1) sit 8 pieces away
+        const int kss = (mb & 1) ? (ks ^ 1) : ks;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(kp + 128 * kss);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(kp + 128 * kss + 16);
+        const i32x8 k8 = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        c[mb] = mfma_f8_16x16x128(k8, qh[ks], q_sh[ks], c[mb]);
+        c[mb] = mfma_f8_16x16x128(k8, ql[ks], q_sl[ks], c[mb]);
       }
     }
     lds_barrier();  // row_sc / row_bias written
@@ -568,7 +645,7 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
       bias4[mb] = *reinterpret_cast<const f32x4*>(&row_bias[16 * mb + 4 * g]);
       c[mb] *= sc4[mb];  // nope part times the row's scale; the rope part adds on top
       const unsigned char* rp = buf + (16 * mb + c16) * kFp8Row + 512 + 64 * dh + 16 * g;
-      c[mb] = mfma16x16x32(as_bf16x8(*reinterpret_cast<const u32x4*>(rp)), qf[8], c[mb]);
+      c[mb] = mfma16x16x32(as_bf16x8(*reinterpret_cast<const u32x4*>(rp)), q_rope, c[mb]);
       sx[wave][mb][lane] = c[mb];
     }
     lds_barrier();
@@ -589,8 +666,10 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
       auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
       tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
+    // (v_exp_f32: 2^-inf = 0, and results below 2^-126 flush to 0, far below what a sum of
+    // probabilities <= 2^kLazyRescale can notice)
     if (tmax > m_used + kLazyRescale) {
-      const float alpha = exp2f(m_used - tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_used - tmax);
       l_part *= alpha;
 #pragma unroll
       for (int db = 0; db < 16; ++db) o[db] *= alpha;
@@ -603,7 +682,7 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = c[mb][i] > -INFINITY ? exp2f(c[mb][i] - m_used) : 0.0f;
+        const float p = __builtin_amdgcn_exp2f(c[mb][i] - m_used);
         l_part += p;
         pb[mb >> 1][4 * (mb & 1) + i] = (__bf16)(p * sc4[mb][i]);
       }
