@@ -68,7 +68,9 @@ def main() -> int:
         return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    total_steps = args.warmup + args.steps
+    # warm-up, the timed steps, then as many steps again with per-kernel timing on (kept out of
+    # the timed region: its event pairs between launches would lengthen the step)
+    total_steps = args.warmup + 2 * args.steps
     wl = synth.config(args.config, scale=args.scale, steps=total_steps)
     lay = synth.make_layout(wl)
     B, S, K, NL = wl.batch, wl.queries, wl.topk, wl.n_layers
@@ -133,42 +135,51 @@ def main() -> int:
         log(f"device error word after warmup: {err:#x}")
         return 1
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    misses = []
-    # per-kernel HIP events, recorded by the library on the stream each kernel is launched on
-    ctx.kernel_timing(True)
+    # the timed region: K whole steps, nothing recorded between launches
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_host = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        run_step(args.warmup + i, events[i])
+        run_step(args.warmup + i)
     end.record(stream)
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
     elapsed_ms = start.elapsed_time(end)
+    timed_miss = int(stats[:, 2].sum())
+    err = ctx.device_error()
+    if err:
+        log(f"device error word after timed steps: {err:#x}")
+        return 1
+    # the next K steps with per-call events and per-kernel HIP events (recorded by the library
+    # on the stream each kernel is launched on): stage and kernel durations, the roofline
+    first_inst = args.warmup + args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ctx.kernel_timing(True)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        run_step(first_inst + i, events[i])
+    torch.cuda.synchronize()
     ktimes = ctx.kernel_times()
     ctx.kernel_timing(False)
     kernels_us = {k: round(ms * 1e3 / n, 1) for k, (ms, n) in ktimes.items() if n}
     kernel_launches = {k: n for k, (ms, n) in ktimes.items() if n}
     err = ctx.device_error()
     if err:
-        log(f"device error word after timed steps: {err:#x}")
+        log(f"device error word after instrumented steps: {err:#x}")
         return 1
-    # per-call durations (ms), averaged over the timed steps
+    # per-call durations (ms), averaged over the instrumented steps
     t_idx = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
     t_res = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
     t_dec = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
-    # misses of the timed steps (stats of the last step only are resident; rerun is not needed:
-    # count misses per step with a second identical pass is avoided, report the last step)
-    last_miss = int(stats[:, 2].sum())
+    last_miss = int(stats[:, 2].sum())  # misses of the last instrumented step
 
     ms_per_step = elapsed_ms / args.steps
     layer_steps_per_s = args.steps * NL / (elapsed_ms / 1e3)
-    # algorithmic work of the timed steps
+    # algorithmic work of the instrumented steps (the roofline's kernel times are theirs)
     idx_b = gat_b = att_f = sweep_b = sweep_f = 0
     for i in range(args.steps):
-        lens_i = wl.ctx_at(args.warmup + i)
+        lens_i = wl.ctx_at(first_inst + i)
         wk = acc.step_work(lens_i, S, K, NL, wl.kv_dtype, wl.idx_dtype)
         idx_b += wk["indexer_bytes"]
         gat_b += wk["gather_bytes"]
@@ -221,7 +232,8 @@ def main() -> int:
                    "frac_hbm_peak": round(gat_gbps / HBM_PEAK_GBPS, 4)},
         "attention": {"algorithmic_flops": int(att_f), "tflops": round(att_f / (t_dec * 1e-3) / 1e12, 2),
                       "mfma_util_bf16_dense": round(mfma_util, 4)},
-        "host_link": {"misses_last_step": last_miss, "misses_warmup_steps": misses_warm,
+        "host_link": {"misses_last_step": last_miss, "misses_last_timed_step": timed_miss,
+                      "misses_warmup_steps": misses_warm,
                       "gbps": round(host_gbps, 2)},
         "kernels_us": kernels_us,
         "kernel_launches": kernel_launches,

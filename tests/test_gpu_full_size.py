@@ -61,8 +61,9 @@ def run_sampled(wl: synth.Workload, steps: int, sample: list):
 
 
 def test_full_ctx128k_b64_mtp3():
-    # the benchmark's workload and context configuration (3 warm-up + 16 timed steps)
-    wl = synth.config(3, steps=19)
+    # the benchmark's workload and context configuration (3 warm-up, 16 timed and 16
+    # instrumented steps)
+    wl = synth.config(3, steps=35)
     run_sampled(wl, 3, [0, 37, 63])
 
 
