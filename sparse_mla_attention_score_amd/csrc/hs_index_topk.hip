@@ -18,9 +18,10 @@
 // digit (bits [30:19]) is counted in LDS and added to a global histogram.
 //
 // Select: one workgroup per (request, query).  The histogram gives the threshold bin; one
-// pass over the scores marks the tokens above it in a bitmap (wave ballots) and collects the
-// bin's tokens on chip, where a radix select over the key's remaining 19 bits and a token
-// order among equal keys pick the rest.  If the bin is too large for the chip, the same
+// pass over the scores (two rounds of loads in flight) marks the tokens above it in a bitmap
+// (wave ballots; in LDS up to 256 K tokens, else in the workspace) and collects the bin's
+// tokens on chip, where a radix select over the key's remaining 19 bits and a token order
+// among equal keys pick the rest.  If the bin is too large for the chip, the same
 // refinement runs over the scores in memory, with an index-ordered pass for exact ties.  The
 // bitmap is then emitted in order.
 #include "hs_device.h"
@@ -293,6 +294,11 @@ __device__ int find_threshold_bin(SelectShared& sh, int nbins, int need, int* ab
   return bin;
 }
 
+// The token bitmap of the selection lives in LDS when it fits (kLdsBitmap; it follows the
+// candidates in the dynamic LDS), else in the workspace.
+constexpr int kLdsBitmapMaxWords = 8192;
+
+template <bool kLdsBitmap>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const int32_t* __restrict__ ctx_lens, int B, int S, int K, int max_ctx,
     const float* __restrict__ scores, int64_t lmax, uint32_t* __restrict__ hist,
@@ -331,28 +337,36 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   const int need = K - above;  // tokens to take from bin beta
   const float* sc = scores + (int64_t)bj * lmax;
   // bm_words covers whole 1,024-token chunks, so the last chunk's ballot words stay inside
-  uint32_t* bm = bitmap + (int64_t)bj * bm_words;
+  uint32_t* bm;
+  if constexpr (kLdsBitmap) bm = reinterpret_cast<uint32_t*>(dyn + (size_t)cand_cap * sizeof(uint64_t));
+  else bm = bitmap + (int64_t)bj * bm_words;
   const int n_chunks = (Lj + kSelThreads - 1) / kSelThreads;
 
   if (beta >= 0 && cnt_beta <= cand_cap) {
     // ---- fast path: one pass, bin beta collected on chip
     if (tid == 0) sh.misc[2] = 0;
     __syncthreads();
-    // 16 chunks per round: all loads of a round are in flight together
-    constexpr int kPer = 16;
-    for (int c0 = 0; c0 < n_chunks; c0 += kPer) {
-      uint32_t keys[kPer];
+    // 8 chunks per round, all loaded together; two rounds' registers alternate, and the next
+    // round's loads are issued before this round is classified, so 16 loads per thread stay in
+    // flight and a round's memory latency hides behind the previous round's work.  Loads are
+    // unconditional (past the end they read the last visible token again) and masked
+    // afterwards: a load under a branch would make the compiler wait for every load in flight.
+    constexpr int kPer = 8;
+    auto load_round = [&](uint32_t (&k)[kPer], int c0) {
 #pragma unroll
       for (int e = 0; e < kPer; ++e) {
         const int t = (c0 + e) * kSelThreads + tid;
-        keys[e] = t < Lj ? __float_as_uint(__builtin_nontemporal_load(sc + t)) : 0u;
+        const uint32_t v = __float_as_uint(__builtin_nontemporal_load(sc + min(t, Lj - 1)));
+        k[e] = t < Lj ? v : 0u;
       }
+    };
+    auto classify_round = [&](const uint32_t (&k)[kPer], int c0) {
 #pragma unroll
       for (int e = 0; e < kPer; ++e) {
         const int c = c0 + e;
         if (c < n_chunks) {
           const int t = c * kSelThreads + tid;
-          const int bin = t < Lj ? (int)(keys[e] >> kHistShift) : -1;
+          const int bin = t < Lj ? (int)(k[e] >> kHistShift) : -1;
           const uint64_t m = __ballot(bin > beta);
           if (lane == 0) {
             const int word = (c * kSelThreads + wave * 64) / 32;
@@ -361,10 +375,18 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
           }
           if (bin == beta) {
             const int pos = atomicAdd(&sh.misc[2], 1);
-            if (pos < cand_cap) cand[pos] = ((uint64_t)keys[e] << 32) | (uint32_t)(~(uint32_t)t);
+            if (pos < cand_cap) cand[pos] = ((uint64_t)k[e] << 32) | (uint32_t)(~(uint32_t)t);
           }
         }
       }
+    };
+    uint32_t ka[kPer], kb[kPer];
+    load_round(ka, 0);
+    for (int c0 = 0; c0 < n_chunks; c0 += 2 * kPer) {
+      load_round(kb, c0 + kPer);
+      classify_round(ka, c0);
+      load_round(ka, c0 + 2 * kPer);
+      classify_round(kb, c0 + kPer);
     }
     // every reader is in this workgroup: the barrier's workgroup-scope release/acquire orders
     // the word stores before the atomics below (no device-scope fence, which would write
@@ -463,17 +485,21 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   }
   __syncthreads();
 
-  // ---- emission in ascending token order (words read at device scope: the atomics above
-  // were performed in L2)
+  // ---- emission in ascending token order (a global bitmap is read at device scope: the
+  // atomics above were performed in L2)
+  auto word_at = [&](int wd) -> uint32_t {
+    if constexpr (kLdsBitmap) return bm[wd];
+    else return load_agent(&bm[wd]);
+  };
   const int n_words = (Lj + 31) / 32;
   const int per = (n_words + kSelThreads - 1) / kSelThreads;
   const int w0 = tid * per, w1 = min(n_words, w0 + per);
   int cnt = 0;
-  for (int wd = w0; wd < w1; ++wd) cnt += __popc(load_agent(&bm[wd]));
+  for (int wd = w0; wd < w1; ++wd) cnt += __popc(word_at(wd));
   int total;
   int pos = block_exclusive_scan<kSelThreads>(cnt, sh.scan, &total);
   for (int wd = w0; wd < w1; ++wd) {
-    uint32_t v = load_agent(&bm[wd]);
+    uint32_t v = word_at(wd);
     while (v) {
       const int bit = __ffs(v) - 1;
       v &= v - 1;
@@ -506,6 +532,17 @@ hipError_t launch_scores(const hs_ctx* ctx, const void* q_idx, const float* w,
 
 using namespace hs;
 
+// Dynamic-LDS limit of the select: the candidates plus, with the LDS bitmap, the bitmap.
+hipError_t hs_select_set_attributes(const hs_config& c) {
+  const int lds = hs_select_cand_cap(c) * (int)sizeof(uint64_t) + kLdsBitmapMaxWords * 4;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_select_kernel<true>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_select_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  return e;
+}
+
 // On-chip candidate capacity of the select.
 int hs_select_cand_cap(const hs_config& c) {
   const int want = c.topk_lds_candidates > 0 ? c.topk_lds_candidates : kDefaultCandCap;
@@ -530,12 +567,19 @@ hipError_t hs_launch_index_topk(const hs_ctx* ctx, const void* q_idx, const floa
   }
   if (e != hipSuccess) return e;
   const int cap = hs_select_cand_cap(ctx->cfg);
-  const size_t dyn = (size_t)cap * sizeof(uint64_t);
+  const bool lds_bitmap = ctx->lay.bm_words <= kLdsBitmapMaxWords;
+  const size_t dyn = (size_t)cap * sizeof(uint64_t) + (lds_bitmap ? (size_t)ctx->lay.bm_words * 4 : 0);
   hs_timer_mark(ctx, HS_KERNEL_TOPK_SELECT, true, stream);
-  hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)(B * S)), dim3(kSelThreads), dyn, stream,
-                     ctx_lens, B, S, ctx->cfg.topk, ctx->cfg.max_pages_per_req * kBlock,
-                     ctx->ws.scores, ctx->lay.lmax, ctx->ws.hist, ctx->ws.bitmap,
-                     (int64_t)ctx->lay.bm_words, topk_out, cap, ctx->ws.err);
+  if (lds_bitmap)
+    hipLaunchKernelGGL(topk_select_kernel<true>, dim3((unsigned)(B * S)), dim3(kSelThreads), dyn, stream,
+                       ctx_lens, B, S, ctx->cfg.topk, ctx->cfg.max_pages_per_req * kBlock,
+                       ctx->ws.scores, ctx->lay.lmax, ctx->ws.hist, ctx->ws.bitmap,
+                       (int64_t)ctx->lay.bm_words, topk_out, cap, ctx->ws.err);
+  else
+    hipLaunchKernelGGL(topk_select_kernel<false>, dim3((unsigned)(B * S)), dim3(kSelThreads), dyn, stream,
+                       ctx_lens, B, S, ctx->cfg.topk, ctx->cfg.max_pages_per_req * kBlock,
+                       ctx->ws.scores, ctx->lay.lmax, ctx->ws.hist, ctx->ws.bitmap,
+                       (int64_t)ctx->lay.bm_words, topk_out, cap, ctx->ws.err);
   hs_timer_mark(ctx, HS_KERNEL_TOPK_SELECT, false, stream);
   return hipGetLastError();
 }
