@@ -91,32 +91,24 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     return;
   }
 
-  // ---- 1. sorted union of the S lists through a token bitmap of the request (workspace
-  // scratch): a bit per selected token, then the set bits read out in order.  Padding (-1)
-  // is skipped; tokens outside [0, Lb) are flagged and skipped.
+  // ---- 1. sorted union of the S lists through a token bitmap of the request: a bit per
+  // selected token, then the set bits read out in order.  The bitmap lives in LDS (over msrc
+  // and mdst, free until step 2) when the context fits, else in workspace scratch.  Padding
+  // (-1) is skipped; tokens outside [0, Lb) are flagged and skipped.
   const int n_in = S * K;
   const int n_words = (Lb + 31) >> 5;
-  uint32_t* ub = ubits + (int64_t)b * ubits_stride;
   if (tid < 8) cnt[tid] = 0;
-  for (int i = tid; i < n_words; i += kResThreads) ub[i] = 0u;
   for (int i = tid; i < H; i += kResThreads) flag[i] = 0;
-  __syncthreads();  // the zeroing stores have completed before any bit is set
-  for (int i = tid; i < n_in; i += kResThreads) {
-    const int32_t t = tk[i];
-    if (t >= Lb) raise_error(err, HS_DEVERR_BAD_ROW);
-    else if (t >= 0) atomicOr(&ub[t >> 5], 1u << (t & 31));
-  }
-  __syncthreads();  // the atomics were performed in L2; the words are read back at agent scope
   int nU;
-  {
+  auto read_out = [&](auto word_at) {
     const int per = (n_words + kResThreads - 1) / kResThreads;
     const int w0 = min(n_words, tid * per), w1 = min(n_words, w0 + per);
     int c = 0;
-    for (int wd = w0; wd < w1; ++wd) c += __popc(load_agent(&ub[wd]));
+    for (int wd = w0; wd < w1; ++wd) c += __popc(word_at(wd));
     int tot;
     int pos = block_exclusive_scan<kResThreads>(c, scan, &tot);
     for (int wd = w0; wd < w1; ++wd) {
-      uint32_t v = load_agent(&ub[wd]);
+      uint32_t v = word_at(wd);
       while (v) {
         const int bit = __ffs(v) - 1;
         v &= v - 1;
@@ -124,8 +116,31 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
       }
     }
     nU = tot;
+  };
+  if (n_words <= 2 * union_cap) {
+    uint32_t* lb = reinterpret_cast<uint32_t*>(msrc);
+    for (int i = tid; i < n_words; i += kResThreads) lb[i] = 0u;
     __syncthreads();
+    for (int i = tid; i < n_in; i += kResThreads) {
+      const int32_t t = tk[i];
+      if (t >= Lb) raise_error(err, HS_DEVERR_BAD_ROW);
+      else if (t >= 0) atomicOr(&lb[t >> 5], 1u << (t & 31));
+    }
+    __syncthreads();
+    read_out([&](int wd) { return lb[wd]; });
+  } else {
+    uint32_t* ub = ubits + (int64_t)b * ubits_stride;
+    for (int i = tid; i < n_words; i += kResThreads) ub[i] = 0u;
+    __syncthreads();  // the zeroing stores have completed before any bit is set
+    for (int i = tid; i < n_in; i += kResThreads) {
+      const int32_t t = tk[i];
+      if (t >= Lb) raise_error(err, HS_DEVERR_BAD_ROW);
+      else if (t >= 0) atomicOr(&ub[t >> 5], 1u << (t & 31));
+    }
+    __syncthreads();  // the atomics were performed in L2; the words are read back at agent scope
+    read_out([&](int wd) { return load_agent(&ub[wd]); });
   }
+  __syncthreads();
 
   // ---- 2. classify: resident / hot hit (stamped) / miss.  Thread owns a contiguous run.
   int n_miss;
@@ -134,24 +149,18 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     const int i0 = tid * per;
     int32_t u[kPerU], blk[kPerU], slot[kPerU], hb[kPerU];
     int n_res = 0, n_hit = 0, my_miss = 0;
+    // the three lookups of a token are independent loads, issued together (one round trip);
+    // only the one its class needs is used
 #pragma unroll
     for (int e = 0; e < kPerU; ++e) {
       u[e] = -1;
-      blk[e] = -1;
+      blk[e] = slot[e] = hb[e] = -1;
       if (e < per && i0 + e < nU) {
         u[e] = U[i0 + e];
         blk[e] = bt[u[e] >> 6];
+        slot[e] = t2s[u[e]];
+        hb[e] = hbt[u[e] >> 6];
       }
-    }
-#pragma unroll
-    for (int e = 0; e < kPerU; ++e) {
-      slot[e] = -1;
-      if (u[e] >= 0 && blk[e] < 0) slot[e] = t2s[u[e]];
-    }
-#pragma unroll
-    for (int e = 0; e < kPerU; ++e) {
-      hb[e] = -1;
-      if (u[e] >= 0 && blk[e] < 0 && !(slot[e] >= 0 && slot[e] < H)) hb[e] = hbt[u[e] >> 6];
     }
 #pragma unroll
     for (int e = 0; e < kPerU; ++e) {
