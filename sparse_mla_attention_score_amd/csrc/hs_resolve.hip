@@ -44,6 +44,13 @@ __device__ __forceinline__ int count_below(const int32_t* a, int n, int32_t x, b
   return lo;
 }
 
+// Sum of v over the block, added to *dst (one LDS atomic per wave).
+__device__ __forceinline__ void block_add(int v, int* dst) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0 && v) atomicAdd(dst, v);
+}
+
 __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     const int32_t* __restrict__ topk, const int32_t* __restrict__ ctx_lens, int S, int K,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ host_block_table,
@@ -56,14 +63,15 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     int32_t* __restrict__ stats, uint32_t* __restrict__ ubits, int64_t ubits_stride,
     int32_t* __restrict__ err) {
   extern __shared__ __align__(16) unsigned char dyn[];
-  // union_cap (a power of two, >= S*K and >= 1024) entries each: sorted union U, per-token
-  // row or miss code `cls` (also the staging area of the input lists), miss source row,
-  // miss destination (victim slot, then its row); then H slot flags.
+  // union_cap (a power of two, >= S*K and >= 1024) entries each: sorted union U, per-entry
+  // class `cls` (row id, -1, or -2 - miss rank), the token of each miss (then its host row),
+  // each miss's victim slot (then its row); then H slot flags.
   int32_t* U = reinterpret_cast<int32_t*>(dyn);
   int32_t* cls = U + union_cap;
   int32_t* msrc = cls + union_cap;
   int32_t* mdst = msrc + union_cap;
   uint8_t* flag = reinterpret_cast<uint8_t*>(mdst + union_cap);
+  __shared__ int32_t lhot[kMaxHot / kBlock];
   __shared__ int scan[kResThreads / 64 + 1];
   __shared__ int cnt[8];
 
@@ -91,11 +99,23 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     return;
   }
 
+  // Everything that depends only on the inputs is loaded up front and kept in registers: the
+  // thread's entries of the S lists (i = tid + 1024 e; used again for the row ids) and its
+  // run of the recency list.
+  const int n_in = S * K;
+  const int perH = (H + kResThreads - 1) / kResThreads;  // <= kPerH
+  const int h0 = tid * perH;
+  int32_t tkv[kPerU], ord[kPerH];
+#pragma unroll
+  for (int e = 0; e < kPerU; ++e) tkv[e] = tid + e * kResThreads < n_in ? tk[tid + e * kResThreads] : -1;
+#pragma unroll
+  for (int e = 0; e < kPerH; ++e) ord[e] = e < perH && h0 + e < H ? order_cur[h0 + e] : -1;
+  for (int i = tid; i < H / kBlock; i += kResThreads) lhot[i] = hot[i];
+
   // ---- 1. sorted union of the S lists through a token bitmap of the request: a bit per
   // selected token, then the set bits read out in order.  The bitmap lives in LDS (over msrc
   // and mdst, free until step 2) when the context fits, else in workspace scratch.  Padding
   // (-1) is skipped; tokens outside [0, Lb) are flagged and skipped.
-  const int n_in = S * K;
   const int n_words = (Lb + 31) >> 5;
   if (tid < 8) cnt[tid] = 0;
   for (int i = tid; i < H; i += kResThreads) flag[i] = 0;
@@ -117,26 +137,26 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     }
     nU = tot;
   };
+  auto mark = [&](uint32_t* words) {
+#pragma unroll
+    for (int e = 0; e < kPerU; ++e) {
+      const int32_t t = tkv[e];
+      if (t >= Lb) raise_error(err, HS_DEVERR_BAD_ROW);
+      else if (t >= 0) atomicOr(&words[t >> 5], 1u << (t & 31));
+    }
+  };
   if (n_words <= 2 * union_cap) {
     uint32_t* lb = reinterpret_cast<uint32_t*>(msrc);
     for (int i = tid; i < n_words; i += kResThreads) lb[i] = 0u;
     __syncthreads();
-    for (int i = tid; i < n_in; i += kResThreads) {
-      const int32_t t = tk[i];
-      if (t >= Lb) raise_error(err, HS_DEVERR_BAD_ROW);
-      else if (t >= 0) atomicOr(&lb[t >> 5], 1u << (t & 31));
-    }
+    mark(lb);
     __syncthreads();
     read_out([&](int wd) { return lb[wd]; });
   } else {
     uint32_t* ub = ubits + (int64_t)b * ubits_stride;
     for (int i = tid; i < n_words; i += kResThreads) ub[i] = 0u;
     __syncthreads();  // the zeroing stores have completed before any bit is set
-    for (int i = tid; i < n_in; i += kResThreads) {
-      const int32_t t = tk[i];
-      if (t >= Lb) raise_error(err, HS_DEVERR_BAD_ROW);
-      else if (t >= 0) atomicOr(&ub[t >> 5], 1u << (t & 31));
-    }
+    mark(ub);
     __syncthreads();  // the atomics were performed in L2; the words are read back at agent scope
     read_out([&](int wd) { return load_agent(&ub[wd]); });
   }
@@ -172,9 +192,8 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
         ++n_res;
       } else if (slot[e] >= 0 && slot[e] < H) {
         const int32_t s = slot[e];
-        flag[s] = 1;
-        st_stamp[s] = step;
-        const int32_t h = hot[s >> 6];
+        flag[s] = 1;  // stamped with the other touched slots in step 3
+        const int32_t h = lhot[s >> 6];
         if (h >= 0 && h < num_gpu_blocks) c = h * kBlock + (s & 63);
         else raise_error(err, HS_DEVERR_BAD_BLOCK);
         ++n_hit;
@@ -188,15 +207,15 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
       }
       cls[i0 + e] = c;
     }
-    atomicAdd(&cnt[0], n_res);
-    atomicAdd(&cnt[1], n_hit);
+    block_add(n_res, &cnt[0]);
+    block_add(n_hit, &cnt[1]);
     int tot;
     int rank = block_exclusive_scan<kResThreads>(my_miss, scan, &tot);
 #pragma unroll
     for (int e = 0; e < kPerU; ++e) {
       if (u[e] >= 0 && cls[i0 + e] == -2) {
         cls[i0 + e] = -2 - rank;  // miss code carries its rank (ascending token order)
-        msrc[rank] = hb[e] * kBlock + (u[e] & 63);
+        msrc[rank] = u[e];
         ++rank;
       }
     }
@@ -205,17 +224,9 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
 
   // ---- 3. victims: the first n_miss untouched slots of the recency list, then the new list
   // (untouched slots in old order, then every touched slot in ascending slot order)
-  const int perH = (H + kResThreads - 1) / kResThreads;  // <= kPerH
-  const int h0 = tid * perH;
-  int32_t ord[kPerH];
   int n_assign;
   {
     int my_cand = 0;
-#pragma unroll
-    for (int e = 0; e < kPerH; ++e) {
-      ord[e] = -1;
-      if (e < perH && h0 + e < H) ord[e] = order_cur[h0 + e];
-    }
 #pragma unroll
     for (int e = 0; e < kPerH; ++e)
       if (ord[e] >= 0 && ord[e] < H && !flag[ord[e]]) ++my_cand;
@@ -235,63 +246,84 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
   for (int r = tid; r < n_assign; r += kResThreads) flag[mdst[r]] = 1;
   __syncthreads();
   {
-    int keep = 0, touched = 0;
+    // both counts in one scan: kept slots in the low 16 bits, touched in the high 16 (each
+    // total is at most H <= 16,384, so the halves never carry into each other).  Every touched
+    // slot (hit or victim) takes this call's stamp here, in the thread's contiguous run.
+    int packed = 0;
 #pragma unroll
     for (int e = 0; e < kPerH; ++e) {
-      if (ord[e] >= 0 && ord[e] < H && !flag[ord[e]]) ++keep;
-      if (e < perH && h0 + e < H && flag[h0 + e]) ++touched;
+      if (ord[e] >= 0 && ord[e] < H && !flag[ord[e]]) packed += 1;
+      if (e < perH && h0 + e < H && flag[h0 + e]) {
+        packed += 1 << 16;
+        st_stamp[h0 + e] = step;
+      }
     }
-    int n_keep, n_touch;
-    int pk = block_exclusive_scan<kResThreads>(keep, scan, &n_keep);
-    int pt = block_exclusive_scan<kResThreads>(touched, scan, &n_touch);
+    int tot;
+    const int pre = block_exclusive_scan<kResThreads>(packed, scan, &tot);
+    const int n_keep = tot & 0xffff;
+    int pk = pre & 0xffff, pt = n_keep + (pre >> 16);
 #pragma unroll
     for (int e = 0; e < kPerH; ++e) {
       if (ord[e] >= 0 && ord[e] < H && !flag[ord[e]]) order_next[pk++] = ord[e];
-      if (e < perH && h0 + e < H && flag[h0 + e]) order_next[n_keep + pt++] = h0 + e;
+      if (e < perH && h0 + e < H && flag[h0 + e]) order_next[pt++] = h0 + e;
     }
   }
 
-  // ---- 4. assign victims to misses (rank order = ascending token order)
+  // ---- 4. fill the victims (rank order = ascending token order) and publish the miss list;
+  // the copy kernel moves the rows
   int fills = 0;
-  for (int i = tid; i < nU; i += kResThreads) {
-    const int32_t c = cls[i];
-    if (c > -2) continue;
-    const int r = -2 - c;
-    if (r >= n_assign) {
-      cls[i] = -1;
-      continue;
-    }
-    const int32_t u = U[i];
+  for (int r = tid; r < n_assign; r += kResThreads) {
+    const int32_t u = msrc[r];
     const int32_t v = mdst[r];
     const int32_t old = st_tok[v];
+    const int32_t hbk = hbt[u >> 6];  // checked in step 2
     if (old >= 0 && old < lmax) t2s[old] = -1;
     else ++fills;
     st_tok[v] = u;
-    st_stamp[v] = step;
     t2s[u] = v;
-    const int32_t h = hot[v >> 6];
+    const int32_t h = lhot[v >> 6];
     int32_t row = -1;
     if (h >= 0 && h < num_gpu_blocks) row = h * kBlock + (v & 63);
     else raise_error(err, HS_DEVERR_BAD_BLOCK);
-    cls[i] = row;
     mdst[r] = row;
+    miss_src[(int64_t)b * n_in + r] = hbk * kBlock + (u & 63);
+    miss_dst[(int64_t)b * n_in + r] = row;
   }
-  atomicAdd(&cnt[2], fills);
+  block_add(fills, &cnt[2]);
+  if (tid == 0) miss_cnt[b] = n_assign;
   __syncthreads();
 
-  // ---- 5. publish the miss list; the copy kernel moves the rows
-  for (int r2 = tid; r2 < n_assign; r2 += kResThreads) {
-    miss_src[(int64_t)b * n_in + r2] = msrc[r2];
-    miss_dst[(int64_t)b * n_in + r2] = mdst[r2];
-  }
-  if (tid == 0) miss_cnt[b] = n_assign;
-
-  // ---- 6. row ids, positionally
-  for (int i = tid; i < n_in; i += kResThreads) {
-    const int32_t t = tk[i];
-    int32_t r = -1;
-    if (t >= 0 && t < Lb && nU > 0) r = cls[count_below(U, nU, t, false)];
-    out[i] = r;
+  // ---- 5. row ids, positionally: each entry's place in U by binary search (the thread's
+  // searches advance together, one LDS round trip per halving step)
+  {
+    int lo[kPerU], hi[kPerU];
+#pragma unroll
+    for (int e = 0; e < kPerU; ++e) {
+      lo[e] = 0;
+      hi[e] = tkv[e] >= 0 && tkv[e] < Lb ? nU : 0;
+    }
+    for (int it = 0; (1 << it) <= nU; ++it) {
+#pragma unroll
+      for (int e = 0; e < kPerU; ++e) {
+        if (lo[e] < hi[e]) {
+          const int mid = (lo[e] + hi[e]) >> 1;
+          if (U[mid] < tkv[e]) lo[e] = mid + 1;
+          else hi[e] = mid;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kPerU; ++e) {
+      const int i = tid + e * kResThreads;
+      if (i >= n_in) continue;
+      int32_t r = -1;
+      if (tkv[e] >= 0 && tkv[e] < Lb && nU > 0) {
+        const int32_t c = cls[lo[e]];
+        if (c >= -1) r = c;
+        else if (-2 - c < n_assign) r = mdst[-2 - c];
+      }
+      out[i] = r;
+    }
   }
   if (tid == 0) {
     const int used = min(H, req_used[b] + cnt[2]);
