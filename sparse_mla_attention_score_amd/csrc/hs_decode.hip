@@ -372,14 +372,17 @@ __global__ __launch_bounds__(kDecThreads) void sparse_mla_decode_kernel(
 // exactly for the PV product (the probabilities stay bf16: their FP8 parts would need scales per
 // 32 rows, which the output layout of QK does not group).  The rows behind the k-slots are
 // addressed in the order the probabilities come out of the QK result, so nothing is permuted in
-// memory.  Barriers between the waves wait for LDS traffic only, never for the prefetch.
+// memory.  The barrier that opens a tile waits for that tile's loads; the next tile's loads are
+// issued right after it, so no barrier waits for them.
 //
-// Work split: wave (hq, dh) holds Q for heads 16 hq .. +15 over half of the 576 QK dims (nope
-// 256 dh .. +255 and rope 32 dh .. +31) and accumulates O^T for those heads over value dims
-// 256 dh .. +255.  The two dim halves' partial scores are added through LDS, after which both
-// waves of a head group run the same softmax.  Holding a quarter of the heads and half the dims
-// keeps a wave under 256 registers, so two waves share each SIMD and one's MFMAs overlap the
-// other's conversions and softmax.
+// Work split: for QK, wave (hb, rh) holds Q for heads 16 hb .. +15 over all 576 dims and scores
+// rows 32 rh .. +31 of the tile, so no partial scores cross waves; the two row halves of a head
+// group agree on the head's running maximum through LDS.  For PV, wave w accumulates O^T for
+// value dims 64 w .. +63 of all 64 heads, so each FP8 value of the tile is converted once; the
+// probabilities reach it through LDS, already in its B-operand layout (the QK result of lane
+// (head, g) is exactly the P fragment of that lane for that head block and row half).  Three
+// barriers per tile: tile landed (and the previous tile finished), maxima written,
+// probabilities written.  A wave stays under 256 registers, so two waves share each SIMD.
 constexpr int kF8RowChunks = kFp8Row / 16;                   // 41 pieces of 16 bytes per row
 constexpr int kF8TileBytes = kTileRows * kFp8Row;            // 41,984
 constexpr int kF8TileLoads = kTileRows * kF8RowChunks / 64;  // 41 wave-wide loads per tile
@@ -459,9 +462,9 @@ __device__ __forceinline__ f32x4 mfma_f8_16x16x128(const i32x8& a, const i32x8& 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, scale_b);
 }
 
-constexpr int kF8Threads = 512;  // 8 waves: 4 groups of 16 heads x 2 halves of the dims
+constexpr int kF8Threads = 512;  // 8 waves: QK 4 head groups x 2 row halves; PV 8 x 64 value dims
 constexpr int kF8Waves = kF8Threads / 64;
-constexpr int kF8LoadsMinW = kF8TileLoads / kF8Waves;  // tile loads every wave issues (5)
+constexpr float kNoMax = -1.0e30f;  // running maximum before any row (finite: exp2 of it is 0)
 
 __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ row_ids,
@@ -472,10 +475,10 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
   // two tiles of raw rows (distinct objects, one filled while the other is read)
   __shared__ __align__(16) unsigned char tile_a[kF8TileBytes];
   __shared__ __align__(16) unsigned char tile_b[kF8TileBytes];
-  __shared__ int32_t rids[kMaxTopk];               // this workgroup's row ids (-1: skipped)
-  __shared__ __align__(16) f32x4 sx[kF8Waves][4][64];  // partial scores, accumulator layout
-  __shared__ __align__(16) float row_sc[kTileRows];    // FP8 scale of each row of the tile
-  __shared__ __align__(16) float row_bias[kTileRows];  // 0, or -inf for a skipped row
+  __shared__ __align__(16) int32_t rids[kMaxTopk];  // this workgroup's row ids (-1: skipped)
+  __shared__ __align__(16) bf16x8 pls[2][4][64];    // P fragments: [row half][head group][lane]
+  __shared__ float smax[2][kHeads];                 // tile maximum per row half and head
+  __shared__ float lsum[2][kHeads];                 // row sums per row half and head
   // The tiles are written only by the asm loads: hand their addresses to asm so that the
   // compiler does not take them for never-written memory.
   asm volatile("" : : "v"(tile_a), "v"(tile_b) : "memory");
@@ -494,12 +497,12 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
   const int bj = b * S + j;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // hq: heads 16 hq .. +15.  dh: this wave's half of the QK dims (nope 256 dh .. +255, rope
-  // 32 dh .. +31) and of the value dims (256 dh .. +255).  In the 16x16 MFMA layouts lane l
-  // works on head 16 hq + l%16 and on rows / dims in groups of 4 selected by l/16.
-  const int hq = wave & 3, dh = wave >> 2;
+  // QK: heads 16 hb .. +15, tile rows 32 rh .. +31.  PV: value dims 64 wave .. +63.  In the
+  // 16x16 MFMA layouts lane l works on head (16 x block) + l%16 and on rows / dims in groups of
+  // 4 selected by l/16.
+  const int hb = wave & 3, rh = wave >> 2;
   const int c16 = lane & 15, g = lane >> 4;
-  const int head = 16 * hq + c16;
+  const int head = 16 * hb + c16;
 
   const int Lb = ctx_lens[b];
   int n = 0;
@@ -522,21 +525,21 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
     }
     rids[i] = v;
   }
-  // Q^T for the nope dims, as the B operand of two FP8 k-steps of 128 dims (256 dh + 128 ks ..):
-  // lane group g holds dims 32 g .. +31 of the step for head `head`.  Each bf16 value q is
-  // carried by two E4M3 parts: q 2^E = hi + lo / 16, with one power of two E per head and
-  // k-step that puts the largest |q| in [128, 256).  hi keeps 4 significant bits, lo the next
-  // 4 of the remainder (|remainder| <= half a step of hi), so hi + lo / 16 carries bf16's 8; the
-  // MFMA's per-column E8M0 scales undo 2^E and the 16.  Rope dims 512 + 32 dh .. +31 stay
-  // bf16 (lane group g holds 8 of them).
-  i32x8 qh[2], ql[2];
-  int q_sh[2], q_sl[2];
-  bf16x8 q_rope;
+  // Q^T for the nope dims, as the B operand of four FP8 k-steps of 128 dims (128 ks ..): lane
+  // group g holds dims 32 g .. +31 of the step for head `head`.  Each bf16 value q is carried by
+  // two E4M3 parts: q 2^E = hi + lo / 16, with one power of two E per head and k-step that puts
+  // the largest |q| in [128, 256).  hi keeps 4 significant bits, lo the next 4 of the remainder
+  // (|remainder| <= half a step of hi), so hi + lo / 16 carries bf16's 8; the MFMA's per-column
+  // E8M0 scales undo 2^E and the 16.  The rope dims stay bf16: two k-steps of 32, lane group g
+  // holding 8 of each.
+  i32x8 qh[4], ql[4];
+  int q_sh[4];
+  bf16x8 q_rope[2];
   {
     const uint16_t* qp = q + ((int64_t)bj * kHeads + head) * kDqk;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint16_t* p = qp + 256 * dh + 128 * ks + 32 * g;
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint16_t* p = qp + 128 * ks + 32 * g;
       float x[32];
       float m = 0.0f;
 #pragma unroll
@@ -558,29 +561,35 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
       const float sc = __builtin_ldexpf(1.0f, E);
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
-        float xs[4], hv[4], r[4], lv[4];
+        float xs[4], hv[4], rr[4], lv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) xs[e] = x[4 * w + e] * sc;
         qh[ks][w] = (int)pack_e4m3x4(xs, hv);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = (xs[e] - hv[e]) * 16.0f;  // exact: |xs - hv| <= half a step
-        ql[ks][w] = (int)pack_e4m3x4(r, lv);
+        for (int e = 0; e < 4; ++e) rr[e] = (xs[e] - hv[e]) * 16.0f;  // exact: |xs - hv| <= half a step
+        ql[ks][w] = (int)pack_e4m3x4(rr, lv);
       }
-      q_sh[ks] = 127 - E;
-      q_sl[ks] = 127 - E - 4;
+      q_sh[ks] = 127 - E;  // the lo part's scale is 2^-4 of it
     }
-    q_rope = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 512 + 32 * dh + 8 * g));
-  }
-  f32x4 o[16];  // O^T for value dims 256 dh + 16 db + 4 g + i, head `head`
 #pragma unroll
-  for (int db = 0; db < 16; ++db) o[db] = f32x4{};
-  float m_used = -INFINITY, l_part = 0.0f;
+    for (int kr = 0; kr < 2; ++kr)
+      q_rope[kr] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 512 + 32 * kr + 8 * g));
+  }
+  f32x4 o[4][4];  // O^T[value dim 64 wave + 16 db + 4 g + i][head 16 hg + c16] in o[db][hg][i]
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) o[db][hg] = f32x4{};
+  float m_pv[4];  // running maximum of head 16 hg + c16 (log2 units), as every wave keeps it
+#pragma unroll
+  for (int hg = 0; hg < 4; ++hg) m_pv[hg] = kNoMax;
+  float m_qk = kNoMax, l_part = 0.0f;  // the same for `head`, and its partial row sum
   // Q and the row ids are in before any tile load is issued, and the compiler knows it: its
   // waits for them would otherwise sit inside the tile loop and also drain the prefetch.  (The
   // empty asm takes the fragments, so their loads cannot sink below this point.)
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) asm volatile("" : "+v"(qh[ks]), "+v"(ql[ks]));
-  asm volatile("" : "+v"(q_rope));
+  for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(qh[ks]), "+v"(ql[ks]));
+  asm volatile("" : "+v"(q_rope[0]), "+v"(q_rope[1]));
   wait_vmcnt<0>();
   asm volatile("" ::: "memory");
   __syncthreads();  // row ids staged
@@ -605,28 +614,25 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
   };
 
   // Transposed V reads: lane group g takes the k-slots 8g .. 8g+7 of a 32-row k-step, which
-  // hold the rows the P operand puts there (rows 4g .. 4g+3 and 16+4g .. 16+4g+3 of the step).
-  // Rows 16+ of a step (kk8 >= 4) have their pieces swizzled: value dims 16 db .. +15 sit at
-  // piece db ^ 8, i.e. 128 bytes later for db < 8 and earlier for db >= 8.
+  // hold the rows the P fragments put there (rows 4g .. 4g+3 and 16+4g .. 16+4g+3 of the step).
+  // Rows 16+ of a step (kk8 >= 4) have their pieces swizzled: the wave's value dims 64 wave +
+  // 16 db .. +15 are piece 4 wave + db, found at piece (4 wave + db) ^ 8, i.e. 128 bytes later
+  // when bit 3 of the piece is clear (wave & 2 == 0) and 128 bytes earlier when it is set.
   const int kk8 = (lane & 15) >> 1;
-  const int v_lane_off = (kk8 < 4 ? 4 * g + kk8 : 16 + 4 * g + (kk8 - 4)) * kFp8Row + 256 * dh + 8 * (lane & 1);
-  const int v_sw = kk8 >= 4 ? 128 : 0;
+  const int v_lane_off = (kk8 < 4 ? 4 * g + kk8 : 16 + 4 * g + (kk8 - 4)) * kFp8Row + 64 * wave + 8 * (lane & 1);
+  const int v_sw = kk8 >= 4 ? ((wave & 2) ? -128 : 128) : 0;
 
   auto compute = [&](const unsigned char* buf, int t0) {
-    // ---- per-row scale and validity of the tile, in contiguous arrays
-    if (tid < kTileRows) {
-      row_sc[tid] = *reinterpret_cast<const float*>(buf + tid * kFp8Row + 640);
-      row_bias[tid] = (tid < nrows - t0 && rids[t0 + tid] >= 0) ? 0.0f : -INFINITY;
-    }
-    // ---- partial S^T = K Q^T over this wave's nope dims, on the FP8 codes as stored: 4 blocks
-    // of 16 rows (mb), lane holds rows 16 mb + 4 g + i of head `head`
-    f32x4 c[4];
+    // ---- S^T = K Q^T for rows 32 rh + 16 mb + 4 g + i, head `head`: the nope part on the FP8
+    // codes as stored, times the row's scale, plus the rope part
+    f32x4 c[2], rsc[2];
+    bool ok[2][4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const unsigned char* kp = buf + (16 * mb + c16) * kFp8Row + 256 * dh + 32 * g;
+    for (int mb = 0; mb < 2; ++mb) {
+      const unsigned char* kp = buf + (32 * rh + 16 * mb + c16) * kFp8Row + 32 * g;
       c[mb] = f32x4{};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < 4; ++ks) {
         // rows of odd blocks have bit 4 set: their pieces 8 ks + 2 g (+1) sit 8 pieces away
         const int kss = (mb & 1) ? (ks ^ 1) : ks;
         const u32x4 lo = *reinterpret_cast<const u32x4*>(kp + 128 * kss);
@@ -634,82 +640,98 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
         const i32x8 k8 = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         c[mb] = mfma_f8_16x16x128(k8, qh[ks], q_sh[ks], c[mb]);
-        c[mb] = mfma_f8_16x16x128(k8, ql[ks], q_sl[ks], c[mb]);
+        c[mb] = mfma_f8_16x16x128(k8, ql[ks], q_sh[ks] - 4, c[mb]);
       }
-    }
-    lds_barrier();  // row_sc / row_bias written
-    f32x4 sc4[4], bias4[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      sc4[mb] = *reinterpret_cast<const f32x4*>(&row_sc[16 * mb + 4 * g]);
-      bias4[mb] = *reinterpret_cast<const f32x4*>(&row_bias[16 * mb + 4 * g]);
-      c[mb] *= sc4[mb];  // nope part times the row's scale; the rope part adds on top
-      const unsigned char* rp = buf + (16 * mb + c16) * kFp8Row + 512 + 64 * dh + 16 * g;
-      c[mb] = mfma16x16x32(as_bf16x8(*reinterpret_cast<const u32x4*>(rp)), q_rope, c[mb]);
-      sx[wave][mb][lane] = c[mb];
-    }
-    lds_barrier();
-    // ---- add the other dim half's partial (wave ^ 4); both waves then hold the same scores
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      c[mb] += sx[wave ^ 4][mb][lane];
+      const int row0 = 32 * rh + 16 * mb + 4 * g;
+      const int4 rid4 = *reinterpret_cast<const int4*>(&rids[t0 + row0]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        c[mb][i] = __builtin_fmaf(c[mb][i], qk_scale_log2, bias4[mb][i]);
-        tmax = fmaxf(tmax, c[mb][i]);
+        rsc[mb][i] = *reinterpret_cast<const float*>(buf + (row0 + i) * kFp8Row + 640);
+        ok[mb][i] = row0 + i < nrows - t0 && (i == 0 ? rid4.x : i == 1 ? rid4.y : i == 2 ? rid4.z : rid4.w) >= 0;
+      }
+      c[mb] *= rsc[mb];
+#pragma unroll
+      for (int kr = 0; kr < 2; ++kr) {
+        const unsigned char* rp = buf + (32 * rh + 16 * mb + c16) * kFp8Row + 512 + 64 * kr + 16 * g;
+        c[mb] = mfma16x16x32(as_bf16x8(*reinterpret_cast<const u32x4*>(rp)), q_rope[kr], c[mb]);
       }
     }
-    // the head's maximum over the 4 lane groups
+    // ---- logits (log2 units; skipped rows -inf) and this row half's maximum of the head
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[mb][i] = ok[mb][i] ? c[mb][i] * qk_scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, c[mb][i]);
+      }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     {
       auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
       tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    // (v_exp_f32: 2^-inf = 0, and results below 2^-126 flush to 0, far below what a sum of
-    // probabilities <= 2^kLazyRescale can notice)
-    if (tmax > m_used + kLazyRescale) {
-      const float alpha = __builtin_amdgcn_exp2f(m_used - tmax);
-      l_part *= alpha;
+    if (g == 0) smax[rh][head] = tmax;
+    lds_barrier();
+    // ---- the running maximum only moves when it grows by more than 2^kLazyRescale; every wave
+    // applies the same rule to the same values, so all agree on each head's maximum
+    // (v_exp_f32: results below 2^-126 flush to 0, far below what a sum of probabilities
+    // <= 2^kLazyRescale can notice)
 #pragma unroll
-      for (int db = 0; db < 16; ++db) o[db] *= alpha;
-      m_used = tmax;
+    for (int hg = 0; hg < 4; ++hg) {
+      const float t = fmaxf(smax[0][16 * hg + c16], smax[1][16 * hg + c16]);
+      if (t > m_pv[hg] + kLazyRescale) {
+        const float alpha = __builtin_amdgcn_exp2f(m_pv[hg] - t);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db][hg] *= alpha;
+        m_pv[hg] = t;
+      }
     }
-    // P (times the row scale) as the B operand of two 32-row k-steps: k-slot 8g + e holds row
-    // 4g + e (e < 4) or 16 + 4g + e - 4 of the step
-    bf16x8 pb[2];
+    {
+      const float t = fmaxf(smax[0][head], smax[1][head]);
+      if (t > m_qk + kLazyRescale) {
+        l_part *= __builtin_amdgcn_exp2f(m_qk - t);
+        m_qk = t;
+      }
+    }
+    // ---- P (times the row scale) as the B operand of PV k-step rh, head group hb: k-slot 8g + e
+    // holds row 4g + e (e < 4) or 16 + 4g + e - 4 of the step, which is what this lane has
+    bf16x8 pb;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(c[mb][i] - m_used);
+        const float p = __builtin_amdgcn_exp2f(c[mb][i] - m_qk);
         l_part += p;
-        pb[mb >> 1][4 * (mb & 1) + i] = (__bf16)(p * sc4[mb][i]);
+        pb[4 * mb + i] = (__bf16)(p * rsc[mb][i]);
       }
-    // ---- O^T += V^T P^T: 16 blocks of 16 value dims x 2 k-steps of 32 rows
+    pls[rh][hb][lane] = pb;
+    lds_barrier();
+    // ---- O^T += V^T P^T: 4 blocks of 16 value dims x 4 head groups x 2 k-steps of 32 rows
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const unsigned char* vp = buf + 32 * kk * kFp8Row + v_lane_off;
+      const unsigned char* vp = buf + 32 * kk * kFp8Row + v_lane_off + v_sw;
+      bf16x8 pv[4];
 #pragma unroll
-      for (int db = 0; db < 16; ++db) {
-        const u32x2 raw = lds_read_tr8(vp + 16 * db + (db < 8 ? v_sw : -v_sw));
-        o[db] = mfma16x16x32(e4m3x8_to_bf16(raw[0], raw[1]), pb[kk], o[db]);
+      for (int hg = 0; hg < 4; ++hg) pv[hg] = pls[kk][hg][lane];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const u32x2 raw = lds_read_tr8(vp + 16 * db);
+        const bf16x8 va = e4m3x8_to_bf16(raw[0], raw[1]);
+#pragma unroll
+        for (int hg = 0; hg < 4; ++hg) o[db][hg] = mfma16x16x32(va, pv[hg], o[db][hg]);
       }
     }
   };
 
-  // tile i of the range lives in tile_a (even i) or tile_b (odd i); tile i+1 loads while
-  // tile i is computed
+  // Tile i of the range lives in tile_a (even i) or tile_b (odd i).  Once every wave has seen
+  // tile i land (and so has finished tile i - 1), tile i + 1 is loaded into the buffer tile
+  // i - 1 used, while tile i is computed.  (A third buffer, keeping two tiles in flight, was
+  // measured slower.)
   auto step = [&](const unsigned char* cur, const unsigned char* nxt, int t0) {
-    if (t0 + kTileRows < nrows) {
-      issue(lds_address(nxt), t0 + kTileRows);
-      wait_vmcnt<kF8LoadsMinW>();  // this wave's loads of `cur` have landed
-    } else {
-      wait_vmcnt<0>();
-    }
-    lds_barrier();  // ... and every other wave's
+    wait_vmcnt<0>();  // this wave's loads of `cur` have landed
+    lds_barrier();    // ... and every other wave's; `nxt`, P and the maxima are free again
+    if (t0 + kTileRows < nrows) issue(lds_address(nxt), t0 + kTileRows);
     compute(cur, t0);
-    lds_barrier();  // `cur`, the exchange buffer and the row arrays are free again
   };
   if (nrows > 0) issue(lds_address(tile_a), 0);
   for (int t0 = 0; t0 < nrows; t0 += 2 * kTileRows) {
@@ -718,37 +740,49 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
     step(tile_b, tile_a, t0 + kTileRows);
   }
 
-  // ---- finish: the head's row sum over the 4 lane groups (both dim halves hold the same)
-  float l_tot = l_part + __shfl_xor(l_part, 16);
+  // ---- finish: the head's row sum over the 4 lane groups and the 2 row halves
+  float l_half = l_part + __shfl_xor(l_part, 16);
   {
-    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_tot), __float_as_uint(l_tot), false, false);
-    l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_half), __float_as_uint(l_half), false, false);
+    l_half = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
-  if (splits == 1) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    uint16_t* op = out + ((int64_t)bj * kHeads + head) * kDv + 256 * dh + 4 * g;
+  if (g == 0) lsum[rh][head] = l_half;
+  __syncthreads();
+  float l_tot[4];
 #pragma unroll
-    for (int db = 0; db < 16; ++db) {
-      const __bf16 v0 = (__bf16)(o[db][0] * inv), v1 = (__bf16)(o[db][1] * inv);
-      const __bf16 v2 = (__bf16)(o[db][2] * inv), v3 = (__bf16)(o[db][3] * inv);
-      const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
-      const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, v2) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
-      *reinterpret_cast<u32x2*>(op + 16 * db) = u32x2{w0, w1};
+  for (int hg = 0; hg < 4; ++hg) l_tot[hg] = lsum[0][16 * hg + c16] + lsum[1][16 * hg + c16];
+  if (splits == 1) {
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) {
+      const float inv = l_tot[hg] > 0.0f ? 1.0f / l_tot[hg] : 0.0f;
+      uint16_t* op = out + ((int64_t)bj * kHeads + 16 * hg + c16) * kDv + 64 * wave + 4 * g;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const __bf16 v0 = (__bf16)(o[db][hg][0] * inv), v1 = (__bf16)(o[db][hg][1] * inv);
+        const __bf16 v2 = (__bf16)(o[db][hg][2] * inv), v3 = (__bf16)(o[db][hg][3] * inv);
+        const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
+        const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, v2) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
+        *reinterpret_cast<u32x2*>(op + 16 * db) = u32x2{w0, w1};
+      }
+      if (lse && g == 0 && wave == 0)
+        lse[(int64_t)bj * kHeads + 16 * hg + c16] = (m_pv[hg] + log2f(l_tot[hg])) * 0.69314718055994531f;
     }
-    if (lse && g == 0 && dh == 0)
-      lse[(int64_t)bj * kHeads + head] = (m_used + log2f(l_tot)) * 0.69314718055994531f;
   } else {
     const int64_t part = (int64_t)bj * splits + sp;
-    if (g == 0 && dh == 0) {
-      part_ml[(part * kHeads + head) * 2 + 0] = m_used;
-      part_ml[(part * kHeads + head) * 2 + 1] = l_tot;
-    }
-    if (nrows > 0) {
-      float* pp = part_o + (part * kHeads + head) * kDv + 256 * dh + 4 * g;
 #pragma unroll
-      for (int db = 0; db < 16; ++db) *reinterpret_cast<f32x4*>(pp + 16 * db) = o[db];
+    for (int hg = 0; hg < 4; ++hg) {
+      const int h = 16 * hg + c16;
+      if (g == 0 && wave == 0) {
+        part_ml[(part * kHeads + h) * 2 + 0] = m_pv[hg];
+        part_ml[(part * kHeads + h) * 2 + 1] = l_tot[hg];
+      }
+      if (nrows > 0) {
+        float* pp = part_o + (part * kHeads + h) * kDv + 64 * wave + 4 * g;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) *reinterpret_cast<f32x4*>(pp + 16 * db) = o[db][hg];
+      }
     }
   }
 }
