@@ -164,6 +164,7 @@ def main() -> int:
     ctx.kernel_timing(False)
     kernels_us = {k: round(ms * 1e3 / n, 1) for k, (ms, n) in ktimes.items() if n}
     kernel_launches = {k: n for k, (ms, n) in ktimes.items() if n}
+    sel_list, sel_scores = ctx.select_paths()  # over every step since the context was reset
     err = ctx.device_error()
     if err:
         log(f"device error word after instrumented steps: {err:#x}")
@@ -227,7 +228,8 @@ def main() -> int:
         "stages_ms": {"index_topk": round(t_idx, 4), "resolve": round(t_res, 4),
                       "sparse_mla_decode": round(t_dec, 4)},
         "indexer": {"algorithmic_bytes": int(idx_b), "gbps": round(idx_gbps, 1),
-                    "frac_hbm_peak": round(idx_gbps / HBM_PEAK_GBPS, 4)},
+                    "frac_hbm_peak": round(idx_gbps / HBM_PEAK_GBPS, 4),
+                    "selections_from_candidate_list": sel_list, "selections_from_scores": sel_scores},
         "gather": {"algorithmic_bytes": int(gat_b), "gbps": round(gat_gbps, 1),
                    "frac_hbm_peak": round(gat_gbps / HBM_PEAK_GBPS, 4)},
         "attention": {"algorithmic_flops": int(att_f), "tflops": round(att_f / (t_dec * 1e-3) / 1e12, 2),

@@ -159,6 +159,11 @@ hs_status hs_hot_reset(hs_ctx* ctx, void* stream);
  *             largest score s(t) = sum_h w_h * max(0, q_h . k_t), ties to the lower token
  *             index, written in ascending token order and padded with -1.
  * The score formula is not printed on the pages; this is the reading the library takes.
+ * Between calls the library keeps, per request slot and query, a guess of where the next
+ * call's selection threshold lies (from this call's score histogram); the sweep then also
+ * lists the tokens scoring above the guess, and the select reads that short list instead of
+ * every score whenever the histogram proves it complete.  The result is the same either way;
+ * hs_hot_reset clears the guesses.
  */
 hs_status hisparse_index_topk(hs_ctx* ctx, const void* q_idx, const float* w,
                               const int32_t* ctx_lens, int32_t B, int32_t S, int32_t* topk_out,
@@ -215,6 +220,12 @@ typedef struct hs_hot_state_ptrs {
 } hs_hot_state_ptrs;
 
 hs_status hs_hot_state(const hs_ctx* ctx, hs_hot_state_ptrs* out);
+
+/* Synchronise the context's device and read how many (request, query) selections of
+ * hisparse_index_topk were made from the sweep's candidate list and how many from all the
+ * scores, since the last hs_hot_reset (selections of L <= K or of invalid contexts are not
+ * counted).  For measurement and tests; never on the hot path. */
+hs_status hs_select_paths(hs_ctx* ctx, int64_t* from_candidates, int64_t* from_scores);
 
 /* Number of split-K partitions sparse_mla_decode uses for a (B, S) batch. */
 hs_status hs_decode_splits(const hs_ctx* ctx, int32_t B, int32_t S, int32_t* splits);

@@ -168,6 +168,11 @@ hs_status hs::compute_layout(const hs_config& c, Layout* L) {
   L->off_miss_cnt = take(B * 4);
   L->off_part_o = take(B * S * cap * kHeads * kDv * 4);
   L->off_part_ml = take(B * S * cap * kHeads * 2 * 4);
+  L->n_seg = (int32_t)((c.max_pages_per_req + kPagesPerItem - 1) / kPagesPerItem * kSweepWaves);
+  L->off_guess = take(B * S * 4);
+  L->off_seg_count = take(B * S * L->n_seg * 4);
+  L->off_cands = take(B * S * L->n_seg * kSegCap * 8);
+  L->off_path_count = take(2 * 8);
   L->total = off;
   return HS_OK;
 }
@@ -354,6 +359,10 @@ hs_status hs_bind(hs_ctx* ctx, const hs_buffers* b) {
   ctx->ws.miss_cnt = reinterpret_cast<int32_t*>(w + L.off_miss_cnt);
   ctx->ws.part_o = reinterpret_cast<float*>(w + L.off_part_o);
   ctx->ws.part_ml = reinterpret_cast<float*>(w + L.off_part_ml);
+  ctx->ws.guess = reinterpret_cast<uint32_t*>(w + L.off_guess);
+  ctx->ws.seg_count = reinterpret_cast<uint32_t*>(w + L.off_seg_count);
+  ctx->ws.cands = reinterpret_cast<uint64_t*>(w + L.off_cands);
+  ctx->ws.path_count = reinterpret_cast<unsigned long long*>(w + L.off_path_count);
   ctx->bound = true;
   return ok();
 }
@@ -450,6 +459,19 @@ hs_status hs_read_device_error(hs_ctx* ctx, int32_t* code) {
     e = hipMemcpy(ctx->ws.err, &zero, 4, hipMemcpyHostToDevice);
   }
   return e == hipSuccess ? ok() : hip_fail(e, "hs_read_device_error");
+}
+
+hs_status hs_select_paths(hs_ctx* ctx, int64_t* from_candidates, int64_t* from_scores) {
+  if (!ctx || !from_candidates || !from_scores) return fail(HS_ERR_INVALID_ARG, "NULL argument");
+  if (!ctx->bound) return fail(HS_ERR_STATE, "context is not bound");
+  unsigned long long v[2] = {0, 0};
+  hipError_t e = hipSetDevice(ctx->device);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(v, ctx->ws.path_count, sizeof(v), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hs_select_paths");
+  *from_candidates = (int64_t)v[0];
+  *from_scores = (int64_t)v[1];
+  return ok();
 }
 
 }  // extern "C"

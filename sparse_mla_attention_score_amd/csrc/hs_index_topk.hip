@@ -79,7 +79,8 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
     const int32_t* __restrict__ ctx_lens, const uint8_t* __restrict__ idx_pool,
     const int32_t* __restrict__ idx_block_table, int max_pages, int64_t num_idx_blocks, int B,
     float* __restrict__ scores, int64_t lmax, uint32_t* __restrict__ hist,
-    int32_t* __restrict__ err) {
+    const uint32_t* __restrict__ guess, uint32_t* __restrict__ seg_count,
+    uint64_t* __restrict__ cands, int n_seg, int32_t* __restrict__ err) {
   constexpr int kBlkBytes = kFp8 ? kIdxFp8Block : kIdxBf16Block;
   constexpr int kRing = 2;  // tile slots per wave
   constexpr int kTilesPerWave = 2 * kPagesPerItem / 4;
@@ -127,6 +128,16 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
+  // candidate list: this wave's segment of each query's list, and the keys from which a token
+  // is listed (kGuessOff: none)
+  const int seg = item * kSweepWaves + wave;
+  uint32_t gq[S];
+  int cq[S];
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    gq[j] = guess[b * S + j];
+    cq[j] = 0;
+  }
   __syncthreads();
 
   // Tile k of this wave is half (k & 1) of page p_begin + wave + 4 * (k >> 1).  Tiles past the
@@ -196,10 +207,26 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
       // scores are >= 0: clearing the sign bit maps -0 to +0
       const uint32_t bits = __float_as_uint(total) & 0x7fffffffu;
       const int jj = jp + half;
-      if (jj <= jq && (jq > jp || half == 0) && t < L - S + 1 + jj) {
+      const bool vis = jj <= jq && (jq > jp || half == 0) && t < L - S + 1 + jj;
+      if (vis) {
         scores[(int64_t)(b * S + jj) * lmax + t] = __uint_as_float(bits);
         const uint32_t bin = bits >> kHistShift;
         atomicAdd(&lhist[jj][bin >> 1], 1u << (16 * (bin & 1)));
+      }
+      // list the token for the next select if its key reaches the query's guess: lanes 0-31
+      // serve query jp, lanes 32-63 query jq; a lane's place is the number of listed lanes
+      // below it in its half
+      const bool cand = vis && bits >= (half ? gq[jq] : gq[jp]);
+      const uint64_t m = __ballot(cand);
+      if (m) {
+        const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+        const int pos = (half ? cq[jq] : cq[jp]) +
+                        (int)(half ? __builtin_amdgcn_mbcnt_hi(mhi, 0u) : __builtin_amdgcn_mbcnt_lo(mlo, 0u));
+        if (cand && pos < kSegCap)
+          cands[((int64_t)(b * S + jj) * n_seg + seg) * kSegCap + pos] =
+              ((uint64_t)bits << 32) | (uint32_t)(~(uint32_t)t);
+        cq[jp] += __popc(mlo);
+        if (jq > jp) cq[jq] += __popc(mhi);
       }
     }
   };
@@ -240,6 +267,10 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
     }
   }
   if (S > 1) finish(S - 1, t_prev, sc_prev);
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < S; ++j) seg_count[(int64_t)(b * S + j) * n_seg + seg] = (uint32_t)cq[j];
+  }
   __syncthreads();
   for (int i = threadIdx.x; i < S * kHistBins / 2; i += kSweepThreads) {
     const uint32_t v = (&lhist[0][0])[i];
@@ -303,7 +334,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const int32_t* __restrict__ ctx_lens, int B, int S, int K, int max_ctx,
     const float* __restrict__ scores, int64_t lmax, uint32_t* __restrict__ hist,
     uint32_t* __restrict__ bitmap, int64_t bm_words, int32_t* __restrict__ topk_out,
-    int cand_cap, int32_t* __restrict__ err) {
+    int cand_cap, uint32_t* __restrict__ guess, const uint32_t* __restrict__ seg_count,
+    const uint64_t* __restrict__ cands, int n_seg_max, unsigned long long* __restrict__ path_count,
+    int32_t* __restrict__ err) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ SelectShared sh;
   uint64_t* cand = reinterpret_cast<uint64_t*>(dyn);  // (key << 32) | ~token
@@ -314,15 +347,18 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   const int Lb = ctx_lens[b];
   int32_t* out = topk_out + (int64_t)bj * K;
   uint32_t* gh = hist + (int64_t)bj * kHistBins;
+  const uint32_t g_used = guess[bj];  // the guess the sweep listed candidates from
   if (Lb < S || Lb > max_ctx) {
     for (int i = tid; i < kHistBins; i += kSelThreads) gh[i] = 0;
     for (int i = tid; i < K; i += kSelThreads) out[i] = -1;
+    if (tid == 0) guess[bj] = kGuessOff;
     return;
   }
   const int Lj = Lb - S + 1 + j;
   if (Lj <= K) {  // everything is selected; keep the histogram zero for the next call
     for (int i = tid; i < kHistBins; i += kSelThreads) gh[i] = 0;
     for (int i = tid; i < K; i += kSelThreads) out[i] = i < Lj ? i : -1;
+    if (tid == 0) guess[bj] = kGuessOff;
     return;
   }
 
@@ -335,6 +371,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   const int beta = find_threshold_bin(sh, kHistBins, K, &above);
   const int cnt_beta = beta >= 0 ? (int)sh.hist[beta] : 0;
   const int need = K - above;  // tokens to take from bin beta
+  {
+    // the next call's guess: the lowest key of the bin that holds the 2K-th largest score, so
+    // that a slowly moving threshold stays above it (off when there is no such bin)
+    int above2;
+    const int gbin = find_threshold_bin(sh, kHistBins, 2 * K, &above2);
+    if (tid == 0) guess[bj] = gbin > 0 ? (uint32_t)gbin << kHistShift : kGuessOff;
+  }
   const float* sc = scores + (int64_t)bj * lmax;
   // bm_words covers whole 1,024-token chunks, so the last chunk's ballot words stay inside
   uint32_t* bm;
@@ -343,7 +386,67 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   const int n_chunks = (Lj + kSelThreads - 1) / kSelThreads;
 
   if (beta >= 0 && cnt_beta <= cand_cap) {
-    // ---- fast path: one pass, bin beta collected on chip
+    // ---- fast path: bin beta collected on chip, the tokens above it marked in the bitmap.
+    // From the sweep's candidate list when it is complete: every token of bin beta and above
+    // was listed if the guess is at most bin beta's lowest key and no wave's segment
+    // overflowed; the counts found must then equal the histogram's.  Otherwise, or if they
+    // do not, one pass over all the scores.
+    bool from_list = false;
+    const int n_seg = (((Lb + kBlock - 1) / kBlock + kPagesPerItem - 1) / kPagesPerItem) * kSweepWaves;
+    if (g_used != kGuessOff && g_used <= ((uint32_t)beta << kHistShift) && n_seg <= min(n_seg_max, kHistBins)) {
+      // segment counts into sh.hist (free until the refinement below)
+      const uint32_t* cnt_p = seg_count + (int64_t)bj * n_seg_max;
+      int over = 0;
+      for (int i = tid; i < n_seg; i += kSelThreads) {
+        const uint32_t c = cnt_p[i];
+        sh.hist[i] = c;
+        over |= c > (uint32_t)kSegCap ? 1 : 0;
+      }
+      const int n_words = (Lj + 31) / 32;
+      for (int i = tid; i < n_words; i += kSelThreads) bm[i] = 0u;
+      if (tid == 0) {
+        sh.misc[2] = 0;
+        sh.misc[4] = 0;
+      }
+      if (!__syncthreads_or(over)) {  // (the barrier also orders the zeroing before the bits)
+        const uint64_t* lst = cands + (int64_t)bj * n_seg_max * kSegCap;
+        const int n_slots = n_seg * kSegCap;
+        int my_above = 0;
+        constexpr int kPer = 8;
+        for (int e0 = 0; e0 < n_slots; e0 += kPer * kSelThreads) {
+          uint64_t v[kPer];
+          bool ok[kPer];
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) {
+            const int slot = e0 + e * kSelThreads + tid;
+            const int sg = slot / kSegCap;
+            ok[e] = slot < n_slots && (uint32_t)(slot - sg * kSegCap) < sh.hist[min(sg, n_seg - 1)];
+            v[e] = lst[min(slot, n_slots - 1)];  // unconditional; masked by ok
+          }
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) {
+            if (!ok[e]) continue;
+            const uint32_t key = (uint32_t)(v[e] >> 32), t = ~(uint32_t)v[e];
+            if ((int)t >= Lj) continue;
+            const int bin = (int)(key >> kHistShift);
+            if (bin > beta) {
+              atomicOr(&bm[t >> 5], 1u << (t & 31));
+              ++my_above;
+            } else if (bin == beta) {
+              const int pos = atomicAdd(&sh.misc[2], 1);
+              if (pos < cand_cap) cand[pos] = v[e];
+            }
+          }
+        }
+        if (my_above) atomicAdd(&sh.misc[4], my_above);
+        __syncthreads();
+        from_list = sh.misc[4] == above && sh.misc[2] == cnt_beta;
+        __syncthreads();
+      }
+    }
+    if (tid == 0) atomicAdd(&path_count[from_list ? 0 : 1], 1ull);
+    if (!from_list) {
+    // one pass over the scores; every bitmap word is written
     if (tid == 0) sh.misc[2] = 0;
     __syncthreads();
     // 8 chunks per round, all loaded together; two rounds' registers alternate, and the next
@@ -387,6 +490,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
       classify_round(ka, c0);
       load_round(ka, c0 + 2 * kPer);
       classify_round(kb, c0 + kPer);
+    }
     }
     // every reader is in this workgroup: the barrier's workgroup-scope release/acquire orders
     // the word stores before the atomics below (no device-scope fence, which would write
@@ -439,6 +543,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
       if (rank < need_left) atomicOr(&bm[t >> 5], 1u << (t & 31));
     }
   } else {
+    if (tid == 0) atomicAdd(&path_count[1], 1ull);
     // ---- general path: refine the threshold over the remaining 19 bits, then an ordered
     // pass that takes the lowest-index ties.
     uint32_t prefix = (uint32_t)max(beta, 0);
@@ -522,7 +627,8 @@ hipError_t launch_scores(const hs_ctx* ctx, const void* q_idx, const float* w,
                      static_cast<const uint16_t*>(q_idx), w, ctx_lens,
                      static_cast<const uint8_t*>(ctx->buf.idx_pool), ctx->buf.idx_block_table,
                      c.max_pages_per_req, (int64_t)c.num_idx_blocks, B, ctx->ws.scores,
-                     ctx->lay.lmax, ctx->ws.hist, ctx->ws.err);
+                     ctx->lay.lmax, ctx->ws.hist, ctx->ws.guess, ctx->ws.seg_count, ctx->ws.cands,
+                     ctx->lay.n_seg, ctx->ws.err);
   hs_timer_mark(ctx, HS_KERNEL_INDEX_SCORE, false, stream);
   return hipGetLastError();
 }
@@ -574,12 +680,14 @@ hipError_t hs_launch_index_topk(const hs_ctx* ctx, const void* q_idx, const floa
     hipLaunchKernelGGL(topk_select_kernel<true>, dim3((unsigned)(B * S)), dim3(kSelThreads), dyn, stream,
                        ctx_lens, B, S, ctx->cfg.topk, ctx->cfg.max_pages_per_req * kBlock,
                        ctx->ws.scores, ctx->lay.lmax, ctx->ws.hist, ctx->ws.bitmap,
-                       (int64_t)ctx->lay.bm_words, topk_out, cap, ctx->ws.err);
+                       (int64_t)ctx->lay.bm_words, topk_out, cap, ctx->ws.guess, ctx->ws.seg_count,
+                       ctx->ws.cands, ctx->lay.n_seg, ctx->ws.path_count, ctx->ws.err);
   else
     hipLaunchKernelGGL(topk_select_kernel<false>, dim3((unsigned)(B * S)), dim3(kSelThreads), dyn, stream,
                        ctx_lens, B, S, ctx->cfg.topk, ctx->cfg.max_pages_per_req * kBlock,
                        ctx->ws.scores, ctx->lay.lmax, ctx->ws.hist, ctx->ws.bitmap,
-                       (int64_t)ctx->lay.bm_words, topk_out, cap, ctx->ws.err);
+                       (int64_t)ctx->lay.bm_words, topk_out, cap, ctx->ws.guess, ctx->ws.seg_count,
+                       ctx->ws.cands, ctx->lay.n_seg, ctx->ws.path_count, ctx->ws.err);
   hs_timer_mark(ctx, HS_KERNEL_TOPK_SELECT, false, stream);
   return hipGetLastError();
 }

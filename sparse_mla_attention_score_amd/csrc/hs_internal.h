@@ -30,6 +30,11 @@ constexpr int kHistBins = 4096;
 constexpr int kHistShift = 19;
 constexpr int kPagesPerItem = 64;      // pages scored by one sweep workgroup (4,096 tokens)
 constexpr int kDefaultCandCap = 4096;  // on-chip candidates of the threshold bin
+// Candidate list of the select: each sweep wave writes the tokens whose score key reaches the
+// query's guess into its own segment (96 entries) of the query's list.
+constexpr int kSegCap = 96;
+constexpr int kSweepWaves = 4;
+constexpr uint32_t kGuessOff = 0xFFFFFFFFu;  // no guess: no candidates are written
 
 // Decode split-K.
 constexpr int kTileRows = 64;
@@ -53,16 +58,21 @@ struct Workspace {
   int32_t* miss_cnt;     // [Bmax] misses of the last resolve
   float* part_o;         // [Bmax*Smax*splits_cap][64][512] split-K partial outputs
   float* part_ml;        // [Bmax*Smax*splits_cap][64][2] split-K (max, sum) in log2 units
+  uint32_t* guess;       // [Bmax][Smax]       score key from which the sweep lists candidates
+  uint32_t* seg_count;   // [Bmax][Smax][n_seg] candidates each sweep wave found (> kSegCap: overflow)
+  uint64_t* cands;       // [Bmax][Smax][n_seg][kSegCap] (key << 32) | ~token
+  unsigned long long* path_count;  // [2] selections made from the candidate list / the scores
 };
 
 struct Layout {
   size_t off_slot_token, off_slot_stamp, off_lru_order, off_tok2slot, off_req_step, off_req_used,
       off_err, off_scores, off_hist, off_bitmap, off_miss_src, off_miss_dst, off_miss_cnt,
-      off_part_o, off_part_ml, total;
+      off_part_o, off_part_ml, off_guess, off_seg_count, off_cands, off_path_count, total;
   int32_t hot_rows;
   int64_t lmax;       // max_pages_per_req * 64
   int64_t bm_words;   // bitmap words per (request, query): lmax rounded up to 1,024, / 32
   int32_t splits_cap;
+  int32_t n_seg;      // candidate segments per (request, query): sweep workgroups x waves
 };
 
 hs_status compute_layout(const hs_config& c, Layout* out);

@@ -406,7 +406,8 @@ __global__ __launch_bounds__(kCopyThreads) void miss_copy_kernel(
 __global__ void hot_reset_kernel(int32_t* slot_token, int32_t* slot_stamp, int32_t* lru_order,
                                  int64_t n_slots, int H, int32_t* tok2slot, int64_t n_tok,
                                  int32_t* req_step, int32_t* req_used, int max_batch,
-                                 uint32_t* hist, int64_t n_hist, int64_t n_all, int32_t* err) {
+                                 uint32_t* hist, int64_t n_hist, uint32_t* guess, int n_guess,
+                                 unsigned long long* path_count, int64_t n_all, int32_t* err) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_all; i += stride) {
     if (i < n_tok) tok2slot[i] = -1;
@@ -417,6 +418,8 @@ __global__ void hot_reset_kernel(int32_t* slot_token, int32_t* slot_stamp, int32
       lru_order[n_slots + i] = (int32_t)(i % H);
     }
     if (i < n_hist) hist[i] = 0;
+    if (i < n_guess) guess[i] = kGuessOff;
+    if (i < 2) path_count[i] = 0;
     if (i < max_batch) {
       req_step[i] = 0;
       req_used[i] = 0;
@@ -482,7 +485,8 @@ hipError_t hs_launch_hot_reset(const hs_ctx* ctx, hipStream_t stream) {
   hipLaunchKernelGGL(hot_reset_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      ctx->ws.slot_token, ctx->ws.slot_stamp, ctx->ws.lru_order, n_slots,
                      ctx->lay.hot_rows, ctx->ws.tok2slot, n_tok, ctx->ws.req_step, ctx->ws.req_used,
-                     c.max_batch, ctx->ws.hist, n_hist, n, ctx->ws.err);
+                     c.max_batch, ctx->ws.hist, n_hist, ctx->ws.guess, c.max_batch * c.max_queries,
+                     ctx->ws.path_count, n, ctx->ws.err);
   hs_timer_mark(ctx, HS_KERNEL_HOT_RESET, false, stream);
   return hipGetLastError();
 }

@@ -31,8 +31,8 @@ HS_KERNEL_COUNT = len(KERNEL_NAMES)
 EXPORTED = ["hs_create", "hs_destroy", "hs_workspace_bytes", "hs_host_pool_bytes",
             "hs_host_pool_alloc", "hs_bind", "hs_hot_reset", "hisparse_index_topk",
             "hisparse_resolve", "sparse_mla_decode", "hs_read_device_error", "hs_decode_splits",
-            "hs_hot_state", "hs_kernel_timing", "hs_kernel_times", "hs_status_string",
-            "hs_last_error"]
+            "hs_hot_state", "hs_kernel_timing", "hs_kernel_times", "hs_select_paths",
+            "hs_status_string", "hs_last_error"]
 
 
 class hs_config(ctypes.Structure):
@@ -91,6 +91,7 @@ def lib() -> ctypes.CDLL:
             "sparse_mla_decode": [P, i32, P, P, P, i32, i32, f32, P, P, P],
             "hs_read_device_error": [P, ctypes.POINTER(i32)],
             "hs_decode_splits": [P, i32, i32, ctypes.POINTER(i32)],
+            "hs_select_paths": [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)],
             "hs_hot_state": [P, ctypes.POINTER(hs_hot_state_ptrs)],
             "hs_kernel_timing": [P, i32],
             "hs_kernel_times": [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
@@ -187,6 +188,13 @@ def hs_decode_splits(ctx: int, B: int, S: int) -> int:
     n = ctypes.c_int32()
     _check(lib().hs_decode_splits(ctx, B, S, ctypes.byref(n)), "hs_decode_splits")
     return n.value
+
+
+def hs_select_paths(ctx: int) -> tuple:
+    """(selections made from the sweep's candidate list, selections made from all scores)."""
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().hs_select_paths(ctx, ctypes.byref(a), ctypes.byref(b)), "hs_select_paths")
+    return a.value, b.value
 
 
 def hs_hot_state(ctx: int) -> hs_hot_state_ptrs:
@@ -289,6 +297,9 @@ class Context:
 
     def device_error(self) -> int:
         return hs_read_device_error(self.ctx)
+
+    def select_paths(self) -> tuple:
+        return hs_select_paths(self.ctx)
 
     def kernel_timing(self, enable: bool) -> None:
         hs_kernel_timing(self.ctx, enable)

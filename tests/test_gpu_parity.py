@@ -104,6 +104,22 @@ def test_select_multipass_path():
     gw.close()
 
 
+def test_select_from_candidate_list():
+    # From the second call on, the sweep lists the tokens above each query's guess and the
+    # select works from that list whenever the histogram proves it complete; every call's
+    # top-K is still checked against the oracle.  The first call has no guess.
+    wl = synth.toy(seed=7, batch=3, queries=2, ctx=(9000, 6000, 12000), topk=256, steps=5)
+    gw = GpuWorkload(wl)
+    run_isolated(gw, 5)
+    from_list, from_scores = gw.ctx.select_paths()
+    per_call = wl.batch * wl.queries
+    print(f"selections from the candidate list {from_list}, from all scores {from_scores}")
+    assert from_list + from_scores == 5 * per_call
+    assert from_scores >= per_call  # the first call reads every score
+    assert from_list >= 3 * per_call
+    gw.close()
+
+
 def test_config1_bf16_8k():
     wl = synth.config(1)
     gw = GpuWorkload(wl)
