@@ -110,6 +110,10 @@ __device__ __forceinline__ void raise_error(int32_t* err, int32_t bit) {
   atomicOr(reinterpret_cast<int*>(err), bit);
 }
 
+// Word 3 of a raw buffer resource on gfx950 (32-bit data format, no swizzle, no index
+// stride): offsets at or past num_records read as zero.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 __device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -290,6 +290,52 @@ struct SelectShared {
   int misc[8];
 };
 
+// Bins (of `nbins`) holding the need1-th and the need2-th largest element given per-bin
+// counts in sh.hist, counted from the top (-1 where there are fewer elements), from one scan;
+// *above1 = number of elements in bins above bin 1.
+__device__ void find_threshold_bins2(SelectShared& sh, int nbins, int need1, int need2, int* bin1,
+                                     int* above1, int* bin2) {
+  const int per = nbins / kSelThreads > 0 ? nbins / kSelThreads : 1;
+  const int tid = threadIdx.x;
+  int local = 0;
+  const int hi = nbins - per * tid, lo = hi - per;
+  if (lo >= 0)
+    for (int bin = lo; bin < hi; ++bin) local += sh.hist[bin];
+  if (tid == 0) {  // ordered before the writes below by the scan's barriers
+    sh.misc[0] = -1;
+    sh.misc[1] = 0;
+    sh.misc[5] = -1;
+  }
+  int total;
+  const int before = block_exclusive_scan<kSelThreads>(local, sh.scan, &total);
+  if (lo >= 0 && before < need1 && before + local >= need1) {
+    int acc = before;
+    for (int bin = hi - 1; bin >= lo; --bin) {
+      if (acc + (int)sh.hist[bin] >= need1) {
+        sh.misc[0] = bin;
+        sh.misc[1] = acc;
+        break;
+      }
+      acc += sh.hist[bin];
+    }
+  }
+  if (lo >= 0 && before < need2 && before + local >= need2) {
+    int acc = before;
+    for (int bin = hi - 1; bin >= lo; --bin) {
+      if (acc + (int)sh.hist[bin] >= need2) {
+        sh.misc[5] = bin;
+        break;
+      }
+      acc += sh.hist[bin];
+    }
+  }
+  __syncthreads();
+  *bin1 = sh.misc[0];
+  *above1 = sh.misc[1];
+  *bin2 = sh.misc[5];
+  __syncthreads();
+}
+
 // Bin (of `nbins`) holding the K-th largest element given per-bin counts in sh.hist, counted
 // from the top.  Returns the bin; *above = number of elements in higher bins.
 __device__ int find_threshold_bin(SelectShared& sh, int nbins, int need, int* above) {
@@ -362,22 +408,38 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     return;
   }
 
+  // The sweep's candidate list of this query (see the fast path below): the segments' counts
+  // are loaded now, with the histogram, on the chance that it is used.
+  const int n_seg = (((Lb + kBlock - 1) / kBlock + kPagesPerItem - 1) / kPagesPerItem) * kSweepWaves;
+  const int n_slots = n_seg * kSegCap;
+  const bool try_list = g_used != kGuessOff && n_seg <= min(n_seg_max, kHistBins);
+  const uint64_t* lst = cands + (int64_t)bj * n_seg_max * kSegCap;
+  constexpr int kSegPerThread = kHistBins / kSelThreads;
+  uint32_t segc[kSegPerThread];
+  if (try_list) {
+    const uint32_t* cnt_p = seg_count + (int64_t)bj * n_seg_max;
+#pragma unroll
+    for (int r = 0; r < kSegPerThread; ++r) {
+      const int i = tid + r * kSelThreads;
+      segc[r] = i < n_seg ? cnt_p[i] : 0u;
+    }
+  }
   for (int i = tid; i < kHistBins; i += kSelThreads) {
     sh.hist[i] = gh[i];
     gh[i] = 0;
   }
   __syncthreads();
-  int above;
-  const int beta = find_threshold_bin(sh, kHistBins, K, &above);
+  // the K-th largest score's bin, and the next call's guess: the lowest key of the bin that
+  // holds the n2-th largest score, so that a slowly moving threshold stays above it.  n2 is 4K,
+  // or a quarter of the list's slots if that is less, so that the segments (a wave's share of
+  // the listed tokens) do not overflow; no guess when that leaves no margin over K, or when
+  // there is no such bin.
+  const int n2 = min(4 * K, n_slots / 4);
+  int above, beta, gbin;
+  find_threshold_bins2(sh, kHistBins, K, n2 > K ? n2 : 4 * K, &beta, &above, &gbin);
+  if (tid == 0) guess[bj] = n2 > K && gbin > 0 ? (uint32_t)gbin << kHistShift : kGuessOff;
   const int cnt_beta = beta >= 0 ? (int)sh.hist[beta] : 0;
   const int need = K - above;  // tokens to take from bin beta
-  {
-    // the next call's guess: the lowest key of the bin that holds the 2K-th largest score, so
-    // that a slowly moving threshold stays above it (off when there is no such bin)
-    int above2;
-    const int gbin = find_threshold_bin(sh, kHistBins, 2 * K, &above2);
-    if (tid == 0) guess[bj] = gbin > 0 ? (uint32_t)gbin << kHistShift : kGuessOff;
-  }
   const float* sc = scores + (int64_t)bj * lmax;
   // bm_words covers whole 1,024-token chunks, so the last chunk's ballot words stay inside
   uint32_t* bm;
@@ -392,15 +454,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     // overflowed; the counts found must then equal the histogram's.  Otherwise, or if they
     // do not, one pass over all the scores.
     bool from_list = false;
-    const int n_seg = (((Lb + kBlock - 1) / kBlock + kPagesPerItem - 1) / kPagesPerItem) * kSweepWaves;
-    if (g_used != kGuessOff && g_used <= ((uint32_t)beta << kHistShift) && n_seg <= min(n_seg_max, kHistBins)) {
+    if (try_list && g_used <= ((uint32_t)beta << kHistShift)) {
       // segment counts into sh.hist (free until the refinement below)
-      const uint32_t* cnt_p = seg_count + (int64_t)bj * n_seg_max;
       int over = 0;
-      for (int i = tid; i < n_seg; i += kSelThreads) {
-        const uint32_t c = cnt_p[i];
-        sh.hist[i] = c;
-        over |= c > (uint32_t)kSegCap ? 1 : 0;
+#pragma unroll
+      for (int r = 0; r < kSegPerThread; ++r) {
+        const int i = tid + r * kSelThreads;
+        if (i < n_seg) sh.hist[i] = segc[r];
+        over |= segc[r] > (uint32_t)kSegCap ? 1 : 0;
       }
       const int n_words = (Lj + 31) / 32;
       for (int i = tid; i < n_words; i += kSelThreads) bm[i] = 0u;
@@ -409,34 +470,56 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
         sh.misc[4] = 0;
       }
       if (!__syncthreads_or(over)) {  // (the barrier also orders the zeroing before the bits)
-        const uint64_t* lst = cands + (int64_t)bj * n_seg_max * kSegCap;
-        const int n_slots = n_seg * kSegCap;
+        // Each wave reads whole segments (w, w + 16, ...), only their filled entries: lane l
+        // takes entries l, l + 64 and l + 128.  Nine segments' loads are issued together.
         int my_above = 0;
-        constexpr int kPer = 8;
-        for (int e0 = 0; e0 < n_slots; e0 += kPer * kSelThreads) {
-          uint64_t v[kPer];
-          bool ok[kPer];
-#pragma unroll
-          for (int e = 0; e < kPer; ++e) {
-            const int slot = e0 + e * kSelThreads + tid;
-            const int sg = slot / kSegCap;
-            ok[e] = slot < n_slots && (uint32_t)(slot - sg * kSegCap) < sh.hist[min(sg, n_seg - 1)];
-            v[e] = lst[min(slot, n_slots - 1)];  // unconditional; masked by ok
+        auto take = [&](uint64_t v) {
+          const uint32_t key = (uint32_t)(v >> 32), t = ~(uint32_t)v;
+          if ((int)t >= Lj) return;
+          const int bin = (int)(key >> kHistShift);
+          if (bin > beta) {
+            atomicOr(&bm[t >> 5], 1u << (t & 31));
+            ++my_above;
+          } else if (bin == beta) {
+            const int pos = atomicAdd(&sh.misc[2], 1);
+            if (pos < cand_cap) cand[pos] = v;
           }
+        };
+        // The loads are buffer loads: an empty entry's lane asks for an offset past the end,
+        // which returns zero without touching memory, so no load sits under a branch (where
+        // the compiler would issue it only when its value is used, one round trip each).
+        constexpr int kSegsAtOnce = 9, kPerSeg = kSegCap / 64;
+        static_assert(kSegCap % 64 == 0, "whole wave rows per segment");
+        const int n_waves = kSelThreads / 64;
+        const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint64_t*>(lst), (short)0, n_slots * (int)sizeof(uint64_t), kBufferRsrcWord3);
+        for (int s0 = wave; s0 < n_seg; s0 += kSegsAtOnce * n_waves) {
+          uint64_t v[kSegsAtOnce][kPerSeg];
+          int c[kSegsAtOnce];  // the segment's count: the same in every lane, so rows of 64
+                               // entries past it are skipped by a scalar branch
 #pragma unroll
-          for (int e = 0; e < kPer; ++e) {
-            if (!ok[e]) continue;
-            const uint32_t key = (uint32_t)(v[e] >> 32), t = ~(uint32_t)v[e];
-            if ((int)t >= Lj) continue;
-            const int bin = (int)(key >> kHistShift);
-            if (bin > beta) {
-              atomicOr(&bm[t >> 5], 1u << (t & 31));
-              ++my_above;
-            } else if (bin == beta) {
-              const int pos = atomicAdd(&sh.misc[2], 1);
-              if (pos < cand_cap) cand[pos] = v[e];
+          for (int a = 0; a < kSegsAtOnce; ++a) {
+            const int sg = s0 + a * n_waves;
+            c[a] = __builtin_amdgcn_readfirstlane(sg < n_seg ? (int)sh.hist[sg] : 0);
+#pragma unroll
+            for (int r = 0; r < kPerSeg; ++r) {
+              v[a][r] = 0;
+              if (c[a] > 64 * r) {
+                const int idx = lane + 64 * r;
+                const uint32_t off = idx < c[a] ? (uint32_t)(sg * kSegCap + idx) * (uint32_t)sizeof(uint64_t) : 0x80000000u;
+                const auto w = __builtin_amdgcn_raw_buffer_load_b64(lrs, off, 0, 0);
+                v[a][r] = ((uint64_t)(uint32_t)w[1] << 32) | (uint32_t)w[0];
+              }
             }
           }
+#pragma unroll
+          for (int a = 0; a < kSegsAtOnce; ++a)
+#pragma unroll
+            for (int r = 0; r < kPerSeg; ++r) {
+              if (c[a] <= 64 * r) continue;
+              asm volatile("" : "+v"(v[a][r]));  // every load above is issued before the first wait
+              if (lane + 64 * r < c[a]) take(v[a][r]);
+            }
         }
         if (my_above) atomicAdd(&sh.misc[4], my_above);
         __syncthreads();

@@ -31,8 +31,8 @@ constexpr int kHistShift = 19;
 constexpr int kPagesPerItem = 64;      // pages scored by one sweep workgroup (4,096 tokens)
 constexpr int kDefaultCandCap = 4096;  // on-chip candidates of the threshold bin
 // Candidate list of the select: each sweep wave writes the tokens whose score key reaches the
-// query's guess into its own segment (96 entries) of the query's list.
-constexpr int kSegCap = 96;
+// query's guess into its own segment (192 entries) of the query's list.
+constexpr int kSegCap = 192;
 constexpr int kSweepWaves = 4;
 constexpr uint32_t kGuessOff = 0xFFFFFFFFu;  // no guess: no candidates are written
 
