@@ -120,6 +120,36 @@ def test_select_from_candidate_list():
     gw.close()
 
 
+def test_select_falls_back_when_the_guess_misses():
+    # The head weights are scaled by a power of two between calls.  The top-K is unchanged in
+    # exact arithmetic, but every score moves by that factor, so the guess the previous call
+    # left is too high (x0.25: too few tokens are listed) or far too low (x4 after x0.25: the
+    # list's segments overflow).  The select must then read every score, and still match the
+    # oracle; the call after each miss uses the list again.
+    wl = synth.toy(seed=8, batch=2, queries=2, ctx=(9000, 12000), topk=256, steps=5)
+    gw = GpuWorkload(wl)
+    base = gw.w_np.copy()
+    factors = [1.0, 0.25, 0.25, 4.0, 4.0]
+    for step, f in enumerate(factors):
+        gw.w_np = base * f
+        gw.w = torch.from_numpy(gw.w_np).to(gw.dev)
+        qidx, _, ctx_lens = gw.inputs(step)
+        print(f"[guess misses] step {step} weights x{f}", flush=True)
+        tk = gw.gpu_topk(qidx, ctx_lens).cpu().numpy()
+        for b in range(wl.batch):
+            _, sc = gw.oracle_topk(b, qidx, int(ctx_lens[b]))
+            for j in range(wl.queries):
+                check_topk(tk[b, j], sc[j], wl.topk)
+    from_list, from_scores = gw.ctx.select_paths()
+    per_call = wl.batch * wl.queries
+    print(f"selections from the candidate list {from_list}, from all scores {from_scores}")
+    assert from_list + from_scores == len(factors) * per_call
+    assert from_scores >= 3 * per_call  # the first call and the two misses
+    assert from_list >= per_call
+    assert gw.ctx.device_error() == 0
+    gw.close()
+
+
 def test_config1_bf16_8k():
     wl = synth.config(1)
     gw = GpuWorkload(wl)
