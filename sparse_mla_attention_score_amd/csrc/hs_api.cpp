@@ -68,7 +68,7 @@ static void timer_free(hs_ctx* ctx) {
 hipError_t hs_set_kernel_attributes();
 hipError_t hs_resolve_set_attributes(size_t lds_bytes);
 hipError_t hs_select_set_attributes(const hs_config& c);
-size_t hs_resolve_lds_bytes(int S, int K, int H);
+size_t hs_resolve_lds_bytes(int S, int K, int H, int max_pages);
 
 namespace {
 
@@ -286,7 +286,7 @@ hs_status hs_create(const hs_config* cfg, hs_ctx** out) {
   hipError_t e = hipGetDevice(&ctx->device);
   if (e == hipSuccess) e = hs_set_kernel_attributes();
   if (e == hipSuccess)
-    e = hs_resolve_set_attributes(hs_resolve_lds_bytes(cfg->max_queries, cfg->topk, ctx->lay.hot_rows));
+    e = hs_resolve_set_attributes(hs_resolve_lds_bytes(cfg->max_queries, cfg->topk, ctx->lay.hot_rows, cfg->max_pages_per_req));
   if (e == hipSuccess) e = hs_select_set_attributes(*cfg);
   if (e != hipSuccess) {
     delete ctx;

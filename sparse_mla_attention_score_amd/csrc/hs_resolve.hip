@@ -61,11 +61,12 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     int32_t* __restrict__ req_used, int32_t* __restrict__ miss_src, int32_t* __restrict__ miss_dst,
     int32_t* __restrict__ miss_cnt, int union_cap, int32_t* __restrict__ row_ids,
     int32_t* __restrict__ stats, uint32_t* __restrict__ ubits, int64_t ubits_stride,
-    int32_t* __restrict__ err) {
+    int tables_off, int32_t* __restrict__ err) {
   extern __shared__ __align__(16) unsigned char dyn[];
   // union_cap (a power of two, >= S*K and >= 1024) entries each: sorted union U, per-entry
   // class `cls` (row id, -1, or -2 - miss rank), the token of each miss (then its host row),
-  // each miss's victim slot (then its row); then H slot flags.
+  // each miss's victim slot (then its row); then H slot flags; then, when they fit
+  // (tables_off > 0), copies of the request's block table and host block table.
   int32_t* U = reinterpret_cast<int32_t*>(dyn);
   int32_t* cls = U + union_cap;
   int32_t* msrc = cls + union_cap;
@@ -111,6 +112,19 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
 #pragma unroll
   for (int e = 0; e < kPerH; ++e) ord[e] = e < perH && h0 + e < H ? order_cur[h0 + e] : -1;
   for (int i = tid; i < H / kBlock; i += kResThreads) lhot[i] = hot[i];
+  // The page tables are read per union entry (up to 8 per thread, at random pages): from LDS
+  // when they fit, staged here with coalesced loads.
+  const int n_pages = (Lb + kBlock - 1) / kBlock;
+  int32_t* lbt = tables_off > 0 ? reinterpret_cast<int32_t*>(dyn + tables_off) : nullptr;
+  int32_t* lhbt = lbt ? lbt + max_pages : nullptr;
+  if (lbt) {
+    for (int i = tid; i < n_pages; i += kResThreads) {
+      lbt[i] = bt[i];
+      lhbt[i] = hbt[i];
+    }
+  }
+  const int32_t* pbt = lbt ? lbt : bt;
+  const int32_t* phbt = lbt ? lhbt : hbt;
 
   // ---- 1. sorted union of the S lists through a token bitmap of the request: a bit per
   // selected token, then the set bits read out in order.  The bitmap lives in LDS (over msrc
@@ -177,9 +191,9 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
       blk[e] = slot[e] = hb[e] = -1;
       if (e < per && i0 + e < nU) {
         u[e] = U[i0 + e];
-        blk[e] = bt[u[e] >> 6];
+        blk[e] = pbt[u[e] >> 6];
         slot[e] = t2s[u[e]];
-        hb[e] = hbt[u[e] >> 6];
+        hb[e] = phbt[u[e] >> 6];
       }
     }
 #pragma unroll
@@ -276,7 +290,7 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     const int32_t u = msrc[r];
     const int32_t v = mdst[r];
     const int32_t old = st_tok[v];
-    const int32_t hbk = hbt[u >> 6];  // checked in step 2
+    const int32_t hbk = phbt[u >> 6];  // checked in step 2
     if (old >= 0 && old < lmax) t2s[old] = -1;
     else ++fills;
     st_tok[v] = u;
@@ -439,8 +453,20 @@ static int union_cap_for(int S, int K) {
   return n < 1024 ? 1024 : n;
 }
 
-size_t hs_resolve_lds_bytes(int S, int K, int H) {
+// Dynamic LDS of the resolver: the union arrays and the slot flags, plus both page tables of
+// a request when everything fits a CU's 160 KiB (less a margin for the static arrays).
+static size_t resolve_lds_base(int S, int K, int H) {
   return (size_t)union_cap_for(S, K) * 16 + (size_t)((H + 15) / 16) * 16;
+}
+
+static size_t resolve_lds_with_tables(int S, int K, int H, int max_pages) {
+  const size_t base = resolve_lds_base(S, K, H);
+  const size_t with = base + (size_t)max_pages * 8;
+  return with <= 160 * 1024 - 2048 ? with : base;
+}
+
+size_t hs_resolve_lds_bytes(int S, int K, int H, int max_pages) {
+  return resolve_lds_with_tables(S, K, H, max_pages);
 }
 
 hipError_t hs_launch_resolve(const hs_ctx* ctx, const int32_t* topk, const int32_t* ctx_lens, int B,
@@ -448,7 +474,9 @@ hipError_t hs_launch_resolve(const hs_ctx* ctx, const int32_t* topk, const int32
   const hs_config& c = ctx->cfg;
   const int H = ctx->lay.hot_rows;
   const int cap = union_cap_for(S, c.topk);
-  const size_t lds = hs_resolve_lds_bytes(S, c.topk, H);
+  const size_t base = resolve_lds_base(S, c.topk, H);
+  const size_t lds = resolve_lds_with_tables(S, c.topk, H, c.max_pages_per_req);
+  const int tables_off = lds > base ? (int)base : 0;
   hs_timer_mark(ctx, HS_KERNEL_RESOLVE, true, stream);
   hipLaunchKernelGGL(resolve_kernel, dim3((unsigned)B), dim3(kResThreads), lds, stream, topk,
                      ctx_lens, S, c.topk, ctx->buf.block_table, ctx->buf.host_block_table,
@@ -457,7 +485,7 @@ hipError_t hs_launch_resolve(const hs_ctx* ctx, const int32_t* topk, const int32
                      ctx->ws.slot_stamp, ctx->ws.lru_order, ctx->ws.tok2slot, ctx->lay.lmax,
                      ctx->ws.req_step, ctx->ws.req_used, ctx->ws.miss_src, ctx->ws.miss_dst,
                      ctx->ws.miss_cnt, cap, row_ids, stats, ctx->ws.bitmap,
-                     (int64_t)c.max_queries * ctx->lay.bm_words, ctx->ws.err);
+                     (int64_t)c.max_queries * ctx->lay.bm_words, tables_off, ctx->ws.err);
   hs_timer_mark(ctx, HS_KERNEL_RESOLVE, false, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || c.num_host_blocks == 0) return e;
