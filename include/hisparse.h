@@ -69,6 +69,7 @@ typedef enum { HS_BF16 = 0, HS_FP8_E4M3 = 1 } hs_dtype;
 #define HS_DEVERR_SHORT_CONTEXT  0x8  /* context < number of queries, or > max pages */
 #define HS_DEVERR_TOPK_COUNT     0x10 /* internal: selection did not produce min(K, L) tokens */
 #define HS_DEVERR_HOT_FULL       0x20 /* more misses than untouched hot slots */
+#define HS_DEVERR_TAIL_PAGE      0x40 /* release of the tail page or of a page past the context */
 
 /*
  * Static configuration.  Fixed kernel shapes must be given as listed; the rest size the
@@ -111,8 +112,9 @@ typedef struct hs_buffers {
   void* kv_pool;                   /* [n_layers][num_gpu_blocks][64][row bytes] */
   const void* idx_pool;            /* [num_idx_blocks][indexer block bytes] */
   const int32_t* idx_block_table;  /* [max_batch][max_pages_per_req] indexer block per page */
-  const int32_t* block_table;      /* [max_batch][max_pages_per_req] GPU block, or -1 for a
-                                      placeholder whose rows live only in host memory */
+  int32_t* block_table;            /* [max_batch][max_pages_per_req] GPU block, or -1 for a
+                                      placeholder whose rows live only in host memory
+                                      (hisparse_release_pages writes placeholders into it) */
   const int32_t* host_block_table; /* [max_batch][max_pages_per_req] host block or -1 */
   const int32_t* hot_blocks;       /* [max_batch][hot_rows/64] GPU blocks leased as hot pages */
   void* workspace;                 /* hs_workspace_bytes() bytes, 256-byte aligned */
@@ -221,6 +223,31 @@ typedef struct hs_hot_state_ptrs {
 
 hs_status hs_hot_state(const hs_ctx* ctx, hs_hot_state_ptrs* out);
 
+/*
+ * Write side of the host pool (part-1 page, "How it works", the paragraphs after the three
+ * residency states: a completed cacheable prefix page is copied to host memory while the GPU
+ * keeps serving it, all sparse-MLA layers in one launch after the forward pass, ordered on the
+ * model's stream; under pressure the page later gives up its GPU block without a second copy).
+ *
+ * hisparse_materialize_pages: for each of the n entries (request b, page p) of `pages`
+ *   (device [n][2] int32), copy the page's 64 rows of every layer from its GPU block
+ *   (block_table[b][p]) into its host block (host_block_table[b][p], which the caller assigns
+ *   beforehand).  The copy is issued by the GPU on `stream`; the pinned pool holds the rows once
+ *   the stream has reached the end of the call.  An entry with no GPU block or no host block
+ *   sets a device error bit and is skipped.
+ * hisparse_release_pages: for each entry, if the page has a host block, set
+ *   block_table[b][p] = -1 (the page becomes host-only: later selections of its tokens resolve
+ *   through the hot buffer, copying from the host copy) and write the GPU block it held to
+ *   freed_out[i] (device [n] int32); -1 where nothing was given up (already host-only, or a
+ *   page listed twice).  The tail page, the one holding token ctx_lens[b] - 1, and pages past
+ *   it are refused (HS_DEVERR_TAIL_PAGE), as is a resident page with no host block
+ *   (HS_DEVERR_NO_HOST_COPY).  Materialise before releasing, on the same stream.
+ * Both calls allocate nothing and never synchronise (graph-capturable like the step calls).
+ */
+hs_status hisparse_materialize_pages(hs_ctx* ctx, const int32_t* pages, int32_t n, void* stream);
+hs_status hisparse_release_pages(hs_ctx* ctx, const int32_t* pages, int32_t n,
+                                 const int32_t* ctx_lens, int32_t* freed_out, void* stream);
+
 /* Synchronise the context's device and read how many (request, query) selections of
  * hisparse_index_topk were made from the sweep's candidate list and how many from all the
  * scores, since the last hs_hot_reset (selections of L <= K or of invalid contexts are not
@@ -246,7 +273,9 @@ typedef enum {
   HS_KERNEL_DECODE = 4,       /* sparse MLA decode attention */
   HS_KERNEL_DECODE_MERGE = 5, /* split-K merge of the decode */
   HS_KERNEL_HOT_RESET = 6,    /* hot-buffer reset */
-  HS_KERNEL_COUNT = 7
+  HS_KERNEL_MATERIALIZE = 7,  /* device-to-host copy of completed pages */
+  HS_KERNEL_RELEASE = 8,      /* pages giving up their GPU blocks */
+  HS_KERNEL_COUNT = 9
 } hs_kernel_id;
 
 hs_status hs_kernel_timing(hs_ctx* ctx, int32_t enable);

@@ -17,6 +17,9 @@ pages it follows:
   scores every earlier token and keeps 2,048; 64 heads share the latent),
   the "Try it" section (short prompts stay on the sparse-MLA MQA kernel),
   and footnote 1 (656-byte FP8 rows; QK over 576 dims, PV over 512).
+* Part 1, "How it works", the paragraphs after the three residency states: the
+  write side of the host pool (completed pages copied to host memory, then
+  giving up their GPU blocks without a second copy).
 
 Where the pages are silent the reading taken is stated at the function.
 Parity status: every function below is pinned by tests under
@@ -35,6 +38,8 @@ from .hisparse_oracle import (  # noqa: F401
     e4m3_decode,
     E4M3_VALUES,
     indexer_scores,
+    materialize_pages,
+    release_pages,
     resolve,
     topk_select,
 )

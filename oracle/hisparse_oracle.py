@@ -240,3 +240,44 @@ def attention(q_bits: np.ndarray, latent: np.ndarray, sm_scale: float):
     out = np.matmul(p, latent[:, :512]) / l
     lse = (m + np.log(l))[:, 0]
     return out, lse
+
+
+# ------------------------------------------------------- host pool write side
+
+def materialize_pages(gpu_rows: np.ndarray, host_rows: np.ndarray, block_table: np.ndarray,
+                      host_block_table: np.ndarray, pages, n_layers: int) -> None:
+    """Copy completed pages to host memory (Part 1, "How it works", the paragraph after the
+    three residency states: a completed cacheable prefix page is queued for a copy to CPU
+    memory while the GPU keeps serving it; all sparse-MLA layers are copied together).
+
+    gpu_rows  [n_layers][gpu blocks * 64][row bytes] uint8 (rows as stored on the GPU)
+    host_rows [n_layers][host blocks * 64][row bytes] uint8, written in place
+    pages     (request, page) pairs.  A page with no GPU block or no host block is skipped.
+    """
+    for b, p in pages:
+        g, h = int(block_table[b, p]), int(host_block_table[b, p])
+        if g < 0 or h < 0:
+            continue
+        for layer in range(n_layers):
+            host_rows[layer, h * BLOCK:(h + 1) * BLOCK] = gpu_rows[layer, g * BLOCK:(g + 1) * BLOCK]
+
+
+def release_pages(block_table: np.ndarray, host_block_table: np.ndarray, pages, ctx_lens) -> list:
+    """A page gives up its GPU block without a second copy (Part 1, "How it works": once its
+    host copy exists, the page can release its GPU slot when the pool fills; the tail is never
+    evicted).  Returns the freed GPU block per entry (-1 where nothing was given up) and writes
+    the placeholder -1 into block_table in place.
+
+    Reading: a page whose host block is missing keeps its GPU block; so do the tail page
+    (holding token ctx_len - 1) and pages past it; a page listed twice is given up once.
+    """
+    freed = []
+    for b, p in pages:
+        tail = (int(ctx_lens[b]) - 1) // BLOCK
+        g, h = int(block_table[b, p]), int(host_block_table[b, p])
+        if p >= tail or h < 0 or g < 0:
+            freed.append(-1)
+            continue
+        block_table[b, p] = -1
+        freed.append(g)
+    return freed

@@ -461,6 +461,33 @@ hs_status hs_read_device_error(hs_ctx* ctx, int32_t* code) {
   return e == hipSuccess ? ok() : hip_fail(e, "hs_read_device_error");
 }
 
+static hs_status check_pages(const hs_ctx* ctx, const int32_t* pages, int32_t n, const char* what) {
+  if (!ctx) return fail(HS_ERR_INVALID_ARG, "%s: ctx is NULL", what);
+  if (!ctx->bound) return fail(HS_ERR_STATE, "%s: context is not bound", what);
+  if (n < 0) return fail(HS_ERR_INVALID_ARG, "%s: n=%d is negative", what, n);
+  if (n > 0 && !pages) return fail(HS_ERR_INVALID_ARG, "%s: pages is NULL", what);
+  if (n > 0 && (ctx->cfg.num_host_blocks == 0 || !ctx->host_pool_dev))
+    return fail(HS_ERR_STATE, "%s: no host pool", what);
+  return HS_OK;
+}
+
+hs_status hisparse_materialize_pages(hs_ctx* ctx, const int32_t* pages, int32_t n, void* stream) {
+  hs_status s = check_pages(ctx, pages, n, "hisparse_materialize_pages");
+  if (s != HS_OK || n == 0) return s;
+  hipError_t e = hs_launch_materialize(ctx, pages, n, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "hisparse_materialize_pages launch");
+}
+
+hs_status hisparse_release_pages(hs_ctx* ctx, const int32_t* pages, int32_t n,
+                                 const int32_t* ctx_lens, int32_t* freed_out, void* stream) {
+  hs_status s = check_pages(ctx, pages, n, "hisparse_release_pages");
+  if (s != HS_OK || n == 0) return s;
+  if (!ctx_lens || !freed_out)
+    return fail(HS_ERR_INVALID_ARG, "hisparse_release_pages: ctx_lens or freed_out is NULL");
+  hipError_t e = hs_launch_release(ctx, pages, n, ctx_lens, freed_out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "hisparse_release_pages launch");
+}
+
 hs_status hs_select_paths(hs_ctx* ctx, int64_t* from_candidates, int64_t* from_scores) {
   if (!ctx || !from_candidates || !from_scores) return fail(HS_ERR_INVALID_ARG, "NULL argument");
   if (!ctx->bound) return fail(HS_ERR_STATE, "context is not bound");

@@ -113,4 +113,7 @@ hipError_t hs_launch_decode(const hs_ctx* ctx, int layer, const void* q, const i
                             const int32_t* ctx_lens, int B, int S, float sm_scale, void* out,
                             float* lse, int splits, hipStream_t stream);
 int hs_choose_splits(const hs_ctx* ctx, int B, int S);
+hipError_t hs_launch_materialize(const hs_ctx* ctx, const int32_t* pages, int n, hipStream_t stream);
+hipError_t hs_launch_release(const hs_ctx* ctx, const int32_t* pages, int n, const int32_t* ctx_lens,
+                             int32_t* freed, hipStream_t stream);
 int hs_select_cand_cap(const hs_config& c);

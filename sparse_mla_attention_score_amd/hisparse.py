@@ -22,17 +22,19 @@ HS_DEVERR_BAD_ROW = 0x4
 HS_DEVERR_SHORT_CONTEXT = 0x8
 HS_DEVERR_TOPK_COUNT = 0x10
 HS_DEVERR_HOT_FULL = 0x20
+HS_DEVERR_TAIL_PAGE = 0x40
 
 # hs_kernel_id
 KERNEL_NAMES = ["index_score", "topk_select", "resolve", "miss_copy", "decode", "decode_merge",
-                "hot_reset"]
+                "hot_reset", "materialize", "release"]
 HS_KERNEL_COUNT = len(KERNEL_NAMES)
 
 EXPORTED = ["hs_create", "hs_destroy", "hs_workspace_bytes", "hs_host_pool_bytes",
             "hs_host_pool_alloc", "hs_bind", "hs_hot_reset", "hisparse_index_topk",
             "hisparse_resolve", "sparse_mla_decode", "hs_read_device_error", "hs_decode_splits",
             "hs_hot_state", "hs_kernel_timing", "hs_kernel_times", "hs_select_paths",
-            "hs_status_string", "hs_last_error"]
+            "hisparse_materialize_pages", "hisparse_release_pages", "hs_status_string",
+            "hs_last_error"]
 
 
 class hs_config(ctypes.Structure):
@@ -92,6 +94,8 @@ def lib() -> ctypes.CDLL:
             "hs_read_device_error": [P, ctypes.POINTER(i32)],
             "hs_decode_splits": [P, i32, i32, ctypes.POINTER(i32)],
             "hs_select_paths": [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)],
+            "hisparse_materialize_pages": [P, P, i32, P],
+            "hisparse_release_pages": [P, P, i32, P, P, P],
             "hs_hot_state": [P, ctypes.POINTER(hs_hot_state_ptrs)],
             "hs_kernel_timing": [P, i32],
             "hs_kernel_times": [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
@@ -188,6 +192,14 @@ def hs_decode_splits(ctx: int, B: int, S: int) -> int:
     n = ctypes.c_int32()
     _check(lib().hs_decode_splits(ctx, B, S, ctypes.byref(n)), "hs_decode_splits")
     return n.value
+
+
+def hisparse_materialize_pages(ctx: int, pages: int, n: int, stream: int) -> None:
+    _check(lib().hisparse_materialize_pages(ctx, pages, n, stream), "hisparse_materialize_pages")
+
+
+def hisparse_release_pages(ctx: int, pages: int, n: int, ctx_lens: int, freed_out: int, stream: int) -> None:
+    _check(lib().hisparse_release_pages(ctx, pages, n, ctx_lens, freed_out, stream), "hisparse_release_pages")
 
 
 def hs_select_paths(ctx: int) -> tuple:
@@ -300,6 +312,14 @@ class Context:
 
     def select_paths(self) -> tuple:
         return hs_select_paths(self.ctx)
+
+    def materialize_pages(self, pages) -> None:
+        """pages: device int32 [n][2] of (request, page)."""
+        hisparse_materialize_pages(self.ctx, pages.data_ptr(), pages.shape[0], self.stream())
+
+    def release_pages(self, pages, ctx_lens, freed_out) -> None:
+        hisparse_release_pages(self.ctx, pages.data_ptr(), pages.shape[0], ctx_lens.data_ptr(),
+                               freed_out.data_ptr(), self.stream())
 
     def kernel_timing(self, enable: bool) -> None:
         hs_kernel_timing(self.ctx, enable)
