@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse-MLA decode layer-steps/s + achieved HBM GB/s (indexer+gather) at 128K ctx"
 HBM_PEAK_GBPS = 8000.0
 BF16_DENSE_TFLOPS = 2500.0
+MAT_PAGES_PER_REQ = 16  # pages per request whose materialisation (device -> host) is timed
 
 
 def log(msg: str) -> None:
@@ -74,6 +75,16 @@ def main() -> int:
     wl = synth.config(args.config, scale=args.scale, steps=total_steps)
     lay = synth.make_layout(wl)
     B, S, K, NL = wl.batch, wl.queries, wl.topk, wl.n_layers
+    # the write side of the host pool is measured after the steps: complete resident pages
+    # (not the tail) of every request get a spare host block each, to be materialised into
+    mat_pages = []
+    for b in range(B):
+        tail = (int(wl.ctx[b]) - 1) // synth.BLOCK
+        res = [int(p) for p in np.nonzero(lay.block_table[b] >= 0)[0] if p < tail]
+        mat_pages += [(b, p) for p in res[:MAT_PAGES_PER_REQ]]
+    for k, (b, p) in enumerate(mat_pages):
+        lay.host_block_table[b, p] = lay.num_host_blocks + k
+    lay.num_host_blocks += len(mat_pages)
     log(f"workload {wl.name}: B={B} S={S} ctx={wl.ctx[0]} layers={NL} gpu_blocks={lay.num_gpu_blocks} "
         f"host_blocks={lay.num_host_blocks} idx_blocks={lay.num_idx_blocks}")
 
@@ -165,6 +176,24 @@ def main() -> int:
     kernels_us = {k: round(ms * 1e3 / n, 1) for k, (ms, n) in ktimes.items() if n}
     kernel_launches = {k: n for k, (ms, n) in ktimes.items() if n}
     sel_list, sel_scores = ctx.select_paths()  # over every step since the context was reset
+    # write side of the host pool: materialise the chosen pages (every layer, one launch);
+    # one untimed launch, then MAT_REPS timed ones
+    mat = None
+    if mat_pages:
+        pages_d = torch.tensor(mat_pages, dtype=torch.int32, device=dev)
+        ctx.materialize_pages(pages_d)
+        torch.cuda.synchronize()
+        MAT_REPS = 5
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(MAT_REPS):
+            ctx.materialize_pages(pages_d)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        mat_us = e0.elapsed_time(e1) * 1e3 / MAT_REPS
+        mat_bytes = len(mat_pages) * synth.BLOCK * wl.row_bytes * NL
+        mat = {"pages": len(mat_pages), "bytes": mat_bytes, "us": round(mat_us, 1),
+               "gbps": round(mat_bytes / (mat_us * 1e-6) / 1e9, 2)}
     err = ctx.device_error()
     if err:
         log(f"device error word after instrumented steps: {err:#x}")
@@ -234,6 +263,7 @@ def main() -> int:
                    "frac_hbm_peak": round(gat_gbps / HBM_PEAK_GBPS, 4)},
         "attention": {"algorithmic_flops": int(att_f), "tflops": round(att_f / (t_dec * 1e-3) / 1e12, 2),
                       "mfma_util_bf16_dense": round(mfma_util, 4)},
+        "materialize": mat,
         "host_link": {"misses_last_step": last_miss, "misses_last_timed_step": timed_miss,
                       "misses_warmup_steps": misses_warm,
                       "gbps": round(host_gbps, 2)},
