@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse-MLA decode layer-steps/s + achieved HBM GB/s (indexer+gather) at 128K ctx"
 HBM_PEAK_GBPS = 8000.0
 BF16_DENSE_TFLOPS = 2500.0
+PCIE_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction, nominal (the host link of the misses)
 MAT_PAGES_PER_REQ = 16  # pages per request whose materialisation (device -> host) is timed
 
 
@@ -167,9 +168,11 @@ def main() -> int:
     first_inst = args.warmup + args.steps
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     ctx.kernel_timing(True)
+    miss_acc = torch.zeros((), dtype=torch.int64, device=dev)  # misses of the instrumented steps
     torch.cuda.synchronize()
     for i in range(args.steps):
         run_step(first_inst + i, events[i])
+        miss_acc += stats[:, 2].sum()  # after the step's last event: not inside any timing
     torch.cuda.synchronize()
     ktimes = ctx.kernel_times()
     ctx.kernel_timing(False)
@@ -192,8 +195,9 @@ def main() -> int:
         torch.cuda.synchronize()
         mat_us = e0.elapsed_time(e1) * 1e3 / MAT_REPS
         mat_bytes = len(mat_pages) * synth.BLOCK * wl.row_bytes * NL
+        mat_gbps = mat_bytes / (mat_us * 1e-6) / 1e9
         mat = {"pages": len(mat_pages), "bytes": mat_bytes, "us": round(mat_us, 1),
-               "gbps": round(mat_bytes / (mat_us * 1e-6) / 1e9, 2)}
+               "gbps": round(mat_gbps, 2), "peak": PCIE_PEAK_GBPS, "frac": round(mat_gbps / PCIE_PEAK_GBPS, 4)}
     err = ctx.device_error()
     if err:
         log(f"device error word after instrumented steps: {err:#x}")
@@ -229,7 +233,12 @@ def main() -> int:
     gat_gbps = gat_b / (t_dec * 1e-3) / 1e9
     both_gbps = (idx_b + gat_b) / ((t_idx + t_dec) * 1e-3) / 1e9
     mfma_util = att_f / (t_dec * 1e-3) / (BF16_DENSE_TFLOPS * 1e12)
-    host_gbps = last_miss * NL * wl.row_bytes / (t_res * 1e-3) / 1e9
+    # host link: the copy kernel's rate over the instrumented steps' misses, and the rate over
+    # the whole resolve stage (resolver + copy)
+    inst_misses = int(miss_acc.item()) / args.steps
+    copy_bytes = inst_misses * NL * wl.row_bytes
+    copy_gbps = copy_bytes / (ktimes["miss_copy"][0] / ktimes["miss_copy"][1] * 1e-3) / 1e9 if ktimes["miss_copy"][1] else 0.0
+    host_gbps = copy_bytes / (t_res * 1e-3) / 1e9
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -266,7 +275,9 @@ def main() -> int:
         "materialize": mat,
         "host_link": {"misses_last_step": last_miss, "misses_last_timed_step": timed_miss,
                       "misses_warmup_steps": misses_warm,
-                      "gbps": round(host_gbps, 2)},
+                      "misses_per_instrumented_step": round(inst_misses, 1),
+                      "copy_kernel_gbps": round(copy_gbps, 2), "resolve_stage_gbps": round(host_gbps, 2),
+                      "peak": PCIE_PEAK_GBPS, "frac": round(copy_gbps / PCIE_PEAK_GBPS, 4)},
         "kernels_us": kernels_us,
         "kernel_launches": kernel_launches,
         "roofline": {"kernel": "index_score_kernel (indexer score sweep)",
