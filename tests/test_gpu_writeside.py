@@ -16,9 +16,10 @@ pytestmark = pytest.mark.gpu
 BLOCK = 64
 
 
-def test_materialize_release_then_decode():
+@pytest.mark.parametrize("kv_dtype", [1, 0], ids=["fp8_rows", "bf16_rows"])
+def test_materialize_release_then_decode(kv_dtype):
     wl = synth.toy(seed=41, batch=2, queries=2, ctx=(3000, 4100), topk=64, n_layers=2, steps=3,
-                   residency=[(synth.RES_HYBRID, 0.6)] * 2)
+                   residency=[(synth.RES_HYBRID, 0.6)] * 2, kv_dtype=kv_dtype)
     lay0 = synth.make_layout(wl)
     # complete resident pages (not the tail) to materialise: three per request
     pages = []
