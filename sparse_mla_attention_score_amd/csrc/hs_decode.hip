@@ -788,53 +788,83 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
 }
 
 // Combine the split partials of each query: M = max m_s, L = sum l_s 2^(m_s - M),
-// out = sum O_s 2^(m_s - M) / L, lse = (M + log2 L) ln 2.  Workgroup = (query, 16 heads):
-// the factors go to LDS first, then consecutive threads stream consecutive 16-byte pieces.
-constexpr int kMergeHeads = 16;
+// out = sum O_s 2^(m_s - M) / L, lse = (M + log2 L) ln 2.  Workgroup = (query, kH heads), 512
+// threads: each of a head's 128 pieces of 4 value dims is summed by kG threads, each over its
+// share of the splits (at most kPer), with all of a thread's loads issued before the first use;
+// the kG sums meet in LDS.  Many splits (few queries): one head per workgroup and 4 groups, so
+// that a lone query still spreads over 64 workgroups; few splits: 4 heads and one group, so
+// that a large batch does not launch a workgroup per head.
+constexpr int kMergeThreads = 512;
+constexpr int kMergePieces = kDv / 4;  // 128
 
-__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_ml,
-                                                           int splits, uint16_t* __restrict__ out,
-                                                           float* __restrict__ lse) {
-  __shared__ float fac[kMaxSplits][kMergeHeads];  // 2^(m_s - M), 0 for an empty split
-  __shared__ float inv_l[kMergeHeads];
-  const int bj = blockIdx.x / (kHeads / kMergeHeads);
-  const int h0 = (blockIdx.x % (kHeads / kMergeHeads)) * kMergeHeads;
-  if (threadIdx.x < kMergeHeads) {
-    const int h = h0 + threadIdx.x;
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) {
-      const float* ml = part_ml + (((int64_t)bj * splits + s) * kHeads + h) * 2;
-      if (ml[1] > 0.0f) M = fmaxf(M, ml[0]);
+template <int kH, int kG, int kPer>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float* __restrict__ part_o,
+                                                                     const float* __restrict__ part_ml,
+                                                                     int splits, uint16_t* __restrict__ out,
+                                                                     float* __restrict__ lse) {
+  static_assert(kH * kG * kMergePieces == kMergeThreads && kG * kPer >= 1 && kG * kPer <= 64, "shape");
+  __shared__ float fac[kH][kG * kPer];  // 2^(m_s - M), 0 for an empty split
+  __shared__ float inv_l[kH];
+  __shared__ f32x4 gsum[kG > 1 ? kG - 1 : 1][kH][kMergePieces];
+  const int bj = blockIdx.x / (kHeads / kH), h0 = (blockIdx.x % (kHeads / kH)) * kH;
+  const int tid = threadIdx.x;
+  if (tid < 64) {  // wave 0: the factors of each head, one split per lane
+#pragma unroll
+    for (int hl = 0; hl < kH; ++hl) {
+      float m = -INFINITY, l = 0.0f;
+      if (tid < splits) {
+        const float* ml = part_ml + (((int64_t)bj * splits + tid) * kHeads + h0 + hl) * 2;
+        m = ml[0];
+        l = ml[1];
+      }
+      const float M = wave_max(l > 0.0f ? m : -INFINITY);
+      const float f = l > 0.0f ? exp2f(m - M) : 0.0f;
+      float L = l * f;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+      if (tid < kG * kPer) fac[hl][tid] = f;
+      if (tid == 0) {
+        inv_l[hl] = L > 0.0f ? 1.0f / L : 0.0f;
+        if (lse) lse[(int64_t)bj * kHeads + h0 + hl] = (M + log2f(L)) * 0.69314718055994531f;
+      }
     }
-    float L = 0.0f;
-    for (int s = 0; s < splits; ++s) {
-      const float* ml = part_ml + (((int64_t)bj * splits + s) * kHeads + h) * 2;
-      const float f = ml[1] > 0.0f ? exp2f(ml[0] - M) : 0.0f;
-      fac[s][threadIdx.x] = f;
-      L += ml[1] * f;
-    }
-    inv_l[threadIdx.x] = L > 0.0f ? 1.0f / L : 0.0f;
-    if (lse) lse[(int64_t)bj * kHeads + h] = (M + log2f(L)) * 0.69314718055994531f;
   }
   __syncthreads();
-  constexpr int kPieces = kMergeHeads * kDv / 4;  // f32x4 pieces of this workgroup's heads
-  for (int e = threadIdx.x; e < kPieces; e += 256) {
-    const int hl = e / (kDv / 4);
-    const int64_t off = ((int64_t)h0 + hl) * kDv + 4 * (e % (kDv / 4));
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < splits; ++s) {
-      const float f = fac[s][hl];
-      if (f == 0.0f) continue;
-      acc += *reinterpret_cast<const f32x4*>(part_o + ((int64_t)bj * splits + s) * kHeads * kDv + off) * f;
-    }
-    const float inv = inv_l[hl];
-    const __bf16 v0 = (__bf16)(acc[0] * inv), v1 = (__bf16)(acc[1] * inv);
-    const __bf16 v2 = (__bf16)(acc[2] * inv), v3 = (__bf16)(acc[3] * inv);
-    const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
-    const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
-    *reinterpret_cast<u32x2*>(out + (int64_t)bj * kHeads * kDv + off) = u32x2{w0, w1};
+  const int piece = tid % kMergePieces, hl = (tid / kMergePieces) % kH, grp = tid / (kMergePieces * kH);
+  // Buffer loads relative to this query's partials: a split past the last gets an offset past
+  // the end, which reads zero without a memory access, so every load is an unconditional
+  // instruction and all of them are issued before the first use.
+  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(part_o + (int64_t)bj * splits * kHeads * kDv), (short)0,
+      splits * kHeads * kDv * (int)sizeof(float), kBufferRsrcWord3);
+  f32x4 v[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int sp = grp + kG * k;
+    const int off = sp < splits ? ((sp * kHeads + h0 + hl) * kDv + 4 * piece) * (int)sizeof(float) : (int)0x80000000;
+    v[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, 0));
   }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int sp = grp + kG * k;  // < kG * kPer
+    // an empty split's partial was never written: dropped by the select, not scaled by 0
+    const float f = sp < splits ? fac[hl][sp] : 0.0f;
+    acc += f != 0.0f ? v[k] * f : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if constexpr (kG > 1) {
+    if (grp > 0) gsum[grp - 1][hl][piece] = acc;
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int g = 0; g < kG - 1; ++g) acc += gsum[g][hl][piece];
+  }
+  const float inv = inv_l[hl];
+  const __bf16 v0 = (__bf16)(acc[0] * inv), v1 = (__bf16)(acc[1] * inv);
+  const __bf16 v2 = (__bf16)(acc[2] * inv), v3 = (__bf16)(acc[3] * inv);
+  const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
+  const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
+  *reinterpret_cast<u32x2*>(out + ((int64_t)bj * kHeads + h0 + hl) * kDv + 4 * piece) = u32x2{w0, w1};
 }
 
 }  // namespace
@@ -882,8 +912,16 @@ hipError_t hs_launch_decode(const hs_ctx* ctx, int layer, const void* q, const i
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   hs_timer_mark(ctx, HS_KERNEL_DECODE_MERGE, true, stream);
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(B * S * (kHeads / kMergeHeads))), dim3(256), 0,
-                     stream, ctx->ws.part_o, ctx->ws.part_ml, splits, static_cast<uint16_t*>(out), lse);
+  static_assert(kMaxSplits == 32, "merge shapes below cover up to 32 splits");
+  if (splits > 8)
+    hipLaunchKernelGGL((decode_merge_kernel<1, 4, 8>), dim3((unsigned)(B * S * kHeads)), dim3(kMergeThreads), 0,
+                       stream, ctx->ws.part_o, ctx->ws.part_ml, splits, static_cast<uint16_t*>(out), lse);
+  else if (splits > 2)
+    hipLaunchKernelGGL((decode_merge_kernel<4, 1, 8>), dim3((unsigned)(B * S * kHeads / 4)), dim3(kMergeThreads), 0,
+                       stream, ctx->ws.part_o, ctx->ws.part_ml, splits, static_cast<uint16_t*>(out), lse);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<4, 1, 2>), dim3((unsigned)(B * S * kHeads / 4)), dim3(kMergeThreads), 0,
+                       stream, ctx->ws.part_o, ctx->ws.part_ml, splits, static_cast<uint16_t*>(out), lse);
   hs_timer_mark(ctx, HS_KERNEL_DECODE_MERGE, false, stream);
   return hipGetLastError();
 }
