@@ -682,17 +682,44 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   const int n_words = (Lj + 31) / 32;
   const int per = (n_words + kSelThreads - 1) / kSelThreads;
   const int w0 = tid * per, w1 = min(n_words, w0 + per);
-  int cnt = 0;
-  for (int wd = w0; wd < w1; ++wd) cnt += __popc(word_at(wd));
   int total;
-  int pos = block_exclusive_scan<kSelThreads>(cnt, sh.scan, &total);
-  for (int wd = w0; wd < w1; ++wd) {
-    uint32_t v = word_at(wd);
-    while (v) {
-      const int bit = __ffs(v) - 1;
-      v &= v - 1;
-      if (pos < K) out[pos] = wd * 32 + bit;
-      ++pos;
+  constexpr int kWordsInRegs = 32;  // a thread's words up to 1 M tokens (32 K words)
+  if (!kLdsBitmap && per <= kWordsInRegs) {
+    // the thread's words from the global bitmap (read at device scope, as below), loaded once
+    // and together: every load is unconditional (past the thread's run it re-reads the last
+    // word, and the value is dropped), so none waits behind a branch
+    uint32_t wv[kWordsInRegs];
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < kWordsInRegs; ++e) wv[e] = load_agent(&bm[min(w0 + e, n_words - 1)]);
+#pragma unroll
+    for (int e = 0; e < kWordsInRegs; ++e) {
+      wv[e] = w0 + e < w1 ? wv[e] : 0u;
+      cnt += __popc(wv[e]);
+    }
+    int pos = block_exclusive_scan<kSelThreads>(cnt, sh.scan, &total);
+#pragma unroll
+    for (int e = 0; e < kWordsInRegs; ++e) {
+      uint32_t v = wv[e];
+      while (v) {
+        const int bit = __ffs(v) - 1;
+        v &= v - 1;
+        if (pos < K) out[pos] = (w0 + e) * 32 + bit;
+        ++pos;
+      }
+    }
+  } else {
+    int cnt = 0;
+    for (int wd = w0; wd < w1; ++wd) cnt += __popc(word_at(wd));
+    int pos = block_exclusive_scan<kSelThreads>(cnt, sh.scan, &total);
+    for (int wd = w0; wd < w1; ++wd) {
+      uint32_t v = word_at(wd);
+      while (v) {
+        const int bit = __ffs(v) - 1;
+        v &= v - 1;
+        if (pos < K) out[pos] = wd * 32 + bit;
+        ++pos;
+      }
     }
   }
   for (int i = total + tid; i < K; i += kSelThreads) out[i] = -1;
