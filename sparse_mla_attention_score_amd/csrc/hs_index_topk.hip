@@ -486,40 +486,56 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
           }
         };
         // The loads are buffer loads: an empty entry's lane asks for an offset past the end,
-        // which returns zero without touching memory, so no load sits under a branch (where
-        // the compiler would issue it only when its value is used, one round trip each).
-        constexpr int kSegsAtOnce = 9, kPerSeg = kSegCap / 64;
+        // which returns zero without a memory access, so no load sits under a per-lane branch
+        // (where the compiler would issue it only when its value is used, one round trip
+        // each).  Segments are read kSegsAtOnce at a time, their first kFirstRows rows of 64
+        // entries together (rows past a segment's count skipped by a scalar branch); any
+        // further rows follow behind a scalar branch.  Contexts up to 256 K tokens (the LDS
+        // bitmap; at most 256 segments, around 48 entries each at 128 K): 9 segments of 3 rows.
+        // Longer ones (up to 1,028 segments, a few entries each at 1 M): 16 segments of 1 row.
+        constexpr int kRows = kSegCap / 64;
+        constexpr int kSegsAtOnce = kLdsBitmap ? 9 : 16, kFirstRows = kLdsBitmap ? kRows : 1;
         static_assert(kSegCap % 64 == 0, "whole wave rows per segment");
         const int n_waves = kSelThreads / 64;
         const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint64_t*>(lst), (short)0, n_slots * (int)sizeof(uint64_t), kBufferRsrcWord3);
+        auto load_entry = [&](int sg, int idx, int c) -> uint64_t {
+          const uint32_t off = idx < c ? (uint32_t)(sg * kSegCap + idx) * (uint32_t)sizeof(uint64_t) : 0x80000000u;
+          const auto w = __builtin_amdgcn_raw_buffer_load_b64(lrs, off, 0, 0);
+          return ((uint64_t)(uint32_t)w[1] << 32) | (uint32_t)w[0];
+        };
         for (int s0 = wave; s0 < n_seg; s0 += kSegsAtOnce * n_waves) {
-          uint64_t v[kSegsAtOnce][kPerSeg];
-          int c[kSegsAtOnce];  // the segment's count: the same in every lane, so rows of 64
-                               // entries past it are skipped by a scalar branch
+          uint64_t v[kSegsAtOnce][kFirstRows];
+          int c[kSegsAtOnce];  // the segment's count: the same in every lane
 #pragma unroll
           for (int a = 0; a < kSegsAtOnce; ++a) {
             const int sg = s0 + a * n_waves;
             c[a] = __builtin_amdgcn_readfirstlane(sg < n_seg ? (int)sh.hist[sg] : 0);
 #pragma unroll
-            for (int r = 0; r < kPerSeg; ++r) {
+            for (int r = 0; r < kFirstRows; ++r) {
+              // the first row is loaded unconditionally (a branch would make the compiler
+              // wait for it at the join); later rows only when the segment reaches them
               v[a][r] = 0;
-              if (c[a] > 64 * r) {
-                const int idx = lane + 64 * r;
-                const uint32_t off = idx < c[a] ? (uint32_t)(sg * kSegCap + idx) * (uint32_t)sizeof(uint64_t) : 0x80000000u;
-                const auto w = __builtin_amdgcn_raw_buffer_load_b64(lrs, off, 0, 0);
-                v[a][r] = ((uint64_t)(uint32_t)w[1] << 32) | (uint32_t)w[0];
-              }
+              if (r == 0 || c[a] > 64 * r) v[a][r] = load_entry(sg, lane + 64 * r, c[a]);
             }
           }
 #pragma unroll
           for (int a = 0; a < kSegsAtOnce; ++a)
 #pragma unroll
-            for (int r = 0; r < kPerSeg; ++r) {
+            for (int r = 0; r < kFirstRows; ++r) {
               if (c[a] <= 64 * r) continue;
               asm volatile("" : "+v"(v[a][r]));  // every load above is issued before the first wait
               if (lane + 64 * r < c[a]) take(v[a][r]);
             }
+          for (int a = 0; a < kSegsAtOnce; ++a) {
+            if (c[a] <= 64 * kFirstRows) continue;
+            const int sg = s0 + a * n_waves;
+            for (int r = kFirstRows; r < kRows; ++r) {
+              if (c[a] <= 64 * r) break;
+              const uint64_t w = load_entry(sg, lane + 64 * r, c[a]);
+              if (lane + 64 * r < c[a]) take(w);
+            }
+          }
         }
         if (my_above) atomicAdd(&sh.misc[4], my_above);
         __syncthreads();
