@@ -159,7 +159,41 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
       else if (t >= 0) atomicOr(&words[t >> 5], 1u << (t & 31));
     }
   };
-  if (n_words <= 2 * union_cap) {
+  // One list (S = 1): if its valid tokens are strictly ascending and its padding comes only at
+  // the end (as the top-K call emits it), the list is already the sorted union, and the bitmap
+  // is skipped.  Any other list takes the bitmap below.
+  bool direct = false;
+  if (S == 1) {
+#pragma unroll
+    for (int e = 0; e < kPerU; ++e) {
+      const int i = tid + e * kResThreads;
+      if (i < n_in) U[i] = tkv[e];
+    }
+    __syncthreads();
+    int bad = 0, valid = 0;
+#pragma unroll
+    for (int e = 0; e < kPerU; ++e) {
+      const int i = tid + e * kResThreads;
+      if (i >= n_in) continue;
+      const int32_t t = tkv[e], prev = i > 0 ? U[i - 1] : -1;
+      if (t >= 0) {
+        valid += 1;
+        if (t >= Lb || (i > 0 && prev >= t) || (i > 0 && prev < 0)) bad = 1;  // out of range, unordered, or after padding
+      }
+    }
+    __shared__ int n_valid;
+    if (tid == 0) n_valid = 0;
+    bad = __syncthreads_or(bad);
+    block_add(valid, &n_valid);
+    __syncthreads();
+    if (!bad) {
+      direct = true;
+      nU = n_valid;
+    }
+  }
+  if (direct) {
+    // U holds the list
+  } else if (n_words <= 2 * union_cap) {
     uint32_t* lb = reinterpret_cast<uint32_t*>(msrc);
     for (int i = tid; i < n_words; i += kResThreads) lb[i] = 0u;
     __syncthreads();
