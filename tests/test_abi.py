@@ -96,3 +96,17 @@ def test_kernel_ids_match_header():
     assert ids["HS_KERNEL_COUNT"] == hsb.HS_KERNEL_COUNT
     for i, name in enumerate(hsb.KERNEL_NAMES):
         assert ids[f"HS_KERNEL_{name.upper()}"] == i
+
+
+def test_write_side_argument_checks():
+    # a NULL context is refused on the host, before any HIP call
+    lib = hsb.lib()
+    pages = (ctypes.c_int32 * 2)(0, 0)
+    lens = (ctypes.c_int32 * 1)(65)
+    freed = (ctypes.c_int32 * 1)()
+    assert lib.hisparse_materialize_pages(None, pages, 1, None) == hsb.HS_ERR_INVALID_ARG
+    assert "ctx is NULL" in hsb.hs_last_error()
+    assert lib.hisparse_release_pages(None, pages, 1, lens, freed, None) == hsb.HS_ERR_INVALID_ARG
+    assert "ctx is NULL" in hsb.hs_last_error()
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.hs_select_paths(None, ctypes.byref(a), ctypes.byref(b)) == hsb.HS_ERR_INVALID_ARG
