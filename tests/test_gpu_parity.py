@@ -96,6 +96,16 @@ def test_topk2048_ragged_and_short_contexts():
     gw.close()
 
 
+def test_minimum_and_page_boundary_contexts():
+    # MTP3 over a context of exactly S tokens (the first query sees a single token, so its
+    # top-K is one token and 15 padding entries), contexts that end on a page boundary (64, 128)
+    # and one with a single token on its second page (65); each grows by S per step
+    wl = synth.toy(seed=9, batch=4, queries=4, ctx=(4, 64, 65, 128), topk=16, steps=3)
+    gw = GpuWorkload(wl)
+    run_isolated(gw, 3)
+    gw.close()
+
+
 def test_select_multipass_path():
     # a one-entry on-chip candidate cap forces the general radix path of the select
     wl = synth.toy(seed=6, batch=2, queries=2, ctx=(5000, 2600), topk=256, steps=2)
