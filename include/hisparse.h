@@ -243,6 +243,8 @@ hs_status hs_hot_state(const hs_ctx* ctx, hs_hot_state_ptrs* out);
  *   it are refused (HS_DEVERR_TAIL_PAGE), as is a resident page with no host block
  *   (HS_DEVERR_NO_HOST_COPY).  Materialise before releasing, on the same stream.
  * Both calls allocate nothing and never synchronise (graph-capturable like the step calls).
+ * n = 0 is a no-op.  Host errors: HS_ERR_INVALID_ARG (NULL ctx, n < 0, NULL pages with n > 0,
+ * NULL ctx_lens or freed_out), HS_ERR_STATE (context not bound, or no host pool).
  */
 hs_status hisparse_materialize_pages(hs_ctx* ctx, const int32_t* pages, int32_t n, void* stream);
 hs_status hisparse_release_pages(hs_ctx* ctx, const int32_t* pages, int32_t n,
