@@ -430,13 +430,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   }
   __syncthreads();
   // the K-th largest score's bin, and the next call's guess: the lowest key of the bin that
-  // holds the n2-th largest score, so that a slowly moving threshold stays above it.  n2 is 4K,
+  // holds the n2-th largest score, so that a slowly moving threshold stays above it.  n2 is 8K,
   // or a quarter of the list's slots if that is less, so that the segments (a wave's share of
   // the listed tokens) do not overflow; no guess when that leaves no margin over K, or when
-  // there is no such bin.
-  const int n2 = min(4 * K, n_slots / 4);
+  // there is no such bin.  (At 4K, a drifting query over a million tokens pushed its K-th
+  // score below the guess about one step in six.)
+  const int n2 = min(8 * K, n_slots / 4);
   int above, beta, gbin;
-  find_threshold_bins2(sh, kHistBins, K, n2 > K ? n2 : 4 * K, &beta, &above, &gbin);
+  find_threshold_bins2(sh, kHistBins, K, n2 > K ? n2 : 8 * K, &beta, &above, &gbin);
   if (tid == 0) guess[bj] = n2 > K && gbin > 0 ? (uint32_t)gbin << kHistShift : kGuessOff;
   const int cnt_beta = beta >= 0 ? (int)sh.hist[beta] : 0;
   const int need = K - above;  // tokens to take from bin beta
