@@ -699,9 +699,87 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   const int n_words = (Lj + 31) / 32;
   const int per = (n_words + kSelThreads - 1) / kSelThreads;
   const int w0 = tid * per, w1 = min(n_words, w0 + per);
-  int total;
+  int total = 0;
+  bool emitted = false;
+  if constexpr (!kLdsBitmap) {
+    // Global bitmap: coalesced reads.  Wave w owns words [w * rounds * 64, (w + 1) * rounds * 64)
+    // and lane l reads word base + 64 r + l of round r, so every load covers 256 contiguous
+    // bytes.  Pass 1 counts each wave's nonzero words; pass 2 reads the words again (from L2)
+    // and compacts the nonzero ones, in word order, into sh.hist (free by now: word indices in
+    // its first half, values in the second).  At most K words are nonzero.  Loads past the end
+    // re-read the last word and are masked, so none waits behind a branch.
+    constexpr int kWaves = kSelThreads / 64, kBatch = 16, kMaxNz = kHistBins / 2;
+    const int rounds = (n_words + kWaves * 64 - 1) / (kWaves * 64);
+    const int wbase = wave * rounds * 64;
+    uint32_t* nz_idx = sh.hist;
+    uint32_t* nz_val = sh.hist + kMaxNz;
+    int nz = 0;
+    for (int r0 = 0; r0 < rounds; r0 += kBatch) {
+      uint32_t v[kBatch];
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) v[e] = load_agent(&bm[min(wbase + (r0 + e) * 64 + lane, n_words - 1)]);
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        const bool ok = r0 + e < rounds && wbase + (r0 + e) * 64 + lane < n_words;
+        nz += __popcll(__ballot(ok && v[e] != 0u));
+      }
+    }
+    __syncthreads();  // every earlier reader of sh.hist and sh.scan is done
+    if (lane == 0) sh.scan[wave] = nz;
+    __syncthreads();
+    int off = 0, n_nz = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = sh.scan[w];
+      off += w < wave ? c : 0;
+      n_nz += c;
+    }
+    __syncthreads();  // sh.scan is read; the scans below write it
+    if (n_nz <= kMaxNz) {  // uniform
+      for (int r0 = 0; r0 < rounds; r0 += kBatch) {
+        uint32_t v[kBatch];
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e) v[e] = load_agent(&bm[min(wbase + (r0 + e) * 64 + lane, n_words - 1)]);
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e) {
+          const int wd = wbase + (r0 + e) * 64 + lane;
+          const bool keep = r0 + e < rounds && wd < n_words && v[e] != 0u;
+          const uint64_t m = __ballot(keep);
+          if (keep) {
+            const int p = off + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            nz_idx[p] = (uint32_t)wd;
+            nz_val[p] = v[e];
+          }
+          off += __popcll(m);
+        }
+      }
+      __syncthreads();
+      // thread t emits compacted entries 2t and 2t + 1
+      const int i0 = 2 * tid;
+      const uint32_t va = i0 < n_nz ? nz_val[i0] : 0u, vb = i0 + 1 < n_nz ? nz_val[i0 + 1] : 0u;
+      const int wa = i0 < n_nz ? (int)nz_idx[i0] : 0, wb = i0 + 1 < n_nz ? (int)nz_idx[i0 + 1] : 0;
+      int pos = block_exclusive_scan<kSelThreads>(__popc(va) + __popc(vb), sh.scan, &total);
+      uint32_t v = va;
+      while (v) {
+        const int bit = __ffs(v) - 1;
+        v &= v - 1;
+        if (pos < K) out[pos] = wa * 32 + bit;
+        ++pos;
+      }
+      v = vb;
+      while (v) {
+        const int bit = __ffs(v) - 1;
+        v &= v - 1;
+        if (pos < K) out[pos] = wb * 32 + bit;
+        ++pos;
+      }
+      emitted = true;
+    }
+  }
   constexpr int kWordsInRegs = 32;  // a thread's words up to 1 M tokens (32 K words)
-  if (!kLdsBitmap && per <= kWordsInRegs) {
+  if (emitted) {
+  } else if (!kLdsBitmap && per <= kWordsInRegs) {
     // the thread's words from the global bitmap (read at device scope, as below), loaded once
     // and together: every load is unconditional (past the thread's run it re-reads the last
     // word, and the value is dropped), so none waits behind a branch
