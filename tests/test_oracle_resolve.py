@@ -54,13 +54,16 @@ def test_single_access_equals_textbook_lru():
 
 def _ordered_list_model(calls, H, resident):
     """Recency list of slots; every slot touched in one call is used 'at the same time'
-    and ranks after untouched slots, ties by slot index."""
+    and ranks after untouched slots, ties by slot index.  Per call: the slot contents and the
+    counts (resident tokens, hot hits, misses, 64-slot pages holding a token) counted here by
+    hand from the model's own state."""
     order = list(range(H))
     slot_token = [-1] * H
     where = {}
     out = []
     for U in calls:
         U = sorted(set(U))
+        n_res = sum(1 for t in U if t in resident)
         hits = {where[t] for t in U if t not in resident and t in where}
         misses = [t for t in U if t not in resident and t not in where]
         free = [s for s in order if s not in hits]
@@ -72,7 +75,9 @@ def _ordered_list_model(calls, H, resident):
             where[t] = s
         touched = hits | set(victims)
         order = [s for s in order if s not in touched] + sorted(touched)
-        out.append(list(slot_token))
+        # pages of the hot buffer in use: a page counts once any of its 64 slots holds a token
+        pages_in_use = len({s // BLOCK for s in range(H) if slot_token[s] != -1})
+        out.append((list(slot_token), (n_res, len(hits), len(misses), pages_in_use)))
     return out
 
 
@@ -89,14 +94,18 @@ def test_multi_token_calls_match_ordered_list_model(H):
         n = int(rng.integers(1, H // 2))
         calls.append(list(rng.choice(n_pages * BLOCK, n, replace=False)))
     model = _ordered_list_model(calls, H, resident)
-    for U, expect in zip(calls, model):
+    partial_pages = 0
+    for U, (expect, counts) in zip(calls, model):
         S = 2
         topk = np.full((S, len(U)), -1, np.int32)
         half = len(U) // 2
         topk[0, :len(U) - half] = np.sort(U[half:])
         topk[1, :half] = np.sort(U[:half])
-        oracle.resolve(topk, bt, hbt, hot, st)
+        _, _, stats = oracle.resolve(topk, bt, hbt, hot, st)
         assert list(st.slot_token) == expect
+        assert stats == counts
+        partial_pages += int(sum(s != -1 for s in expect) % BLOCK != 0)
+    assert partial_pages > 0  # some calls leave a hot page partly filled
 
 
 def test_invariants_over_steps_and_content():
@@ -121,6 +130,13 @@ def test_invariants_over_steps_and_content():
         row_ids, copies, stats = oracle.resolve(topk, bt, hbt, hot, st)
         U = np.unique(topk)
         non_res = [t for t in U if bt[t // BLOCK] < 0]
+        # counts by hand: resident union tokens (pages 14 and 15), hits, misses, and the hot
+        # pages holding at least one token
+        assert stats[0] == sum(1 for t in U if t // BLOCK in (14, 15))
+        assert stats[1] == sum(1 for t in non_res if before.tok2slot[t] != -1)
+        assert stats[2] == len(copies) == len(non_res) - stats[1]
+        filled = [s for s in range(H) if st.slot_token[s] != -1]
+        assert stats[3] == len({s // BLOCK for s in filled})
         if cold_before:
             assert stats[2] == len(non_res) and stats[1] == 0
         if prev is not None and np.array_equal(prev, topk):

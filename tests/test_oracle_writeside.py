@@ -31,13 +31,22 @@ def workload(kv_dtype=1, n_layers=2):
     return wl, synth.make_layout(wl)
 
 
-def pools(wl, lay):
+def pools(wl, lay, empty_host_blocks=()):
+    """GPU and host pools filled by the generator.  The host blocks listed in
+    `empty_host_blocks` are then zeroed: blocks newly assigned to resident pages hold nothing
+    until the pages are materialised (the generator writes every host block of the table)."""
     rb = wl.row_bytes
     gpu = np.zeros(wl.n_layers * lay.num_gpu_blocks * BLOCK * rb, np.uint8)
     host = np.zeros(wl.n_layers * lay.num_host_blocks * BLOCK * rb, np.uint8)
     synth.fill_kv(wl, lay, gpu, host if host.size else None)
-    return (gpu.reshape(wl.n_layers, lay.num_gpu_blocks * BLOCK, rb),
-            host.reshape(wl.n_layers, lay.num_host_blocks * BLOCK, rb))
+    host = host.reshape(wl.n_layers, lay.num_host_blocks * BLOCK, rb)
+    for h in empty_host_blocks:
+        host[:, h * BLOCK:(h + 1) * BLOCK] = 0
+    return gpu.reshape(wl.n_layers, lay.num_gpu_blocks * BLOCK, rb), host
+
+
+def new_host_blocks(lay, pages):
+    return [int(lay.host_block_table[b, p]) for b, p in pages]
 
 
 @pytest.mark.parametrize("kv_dtype", [0, 1])
@@ -50,8 +59,11 @@ def test_materialized_rows_are_the_tokens_rows(kv_dtype):
         res = [p for p in np.nonzero(lay0.block_table[b] >= 0)[0] if p < tail]
         pages += [(b, int(res[0])), (b, int(res[-1]))]
     lay = spare_host_blocks(lay0, pages)
-    gpu, host = pools(wl, lay)
+    gpu, host = pools(wl, lay, new_host_blocks(lay, pages))
     before = host.copy()
+    for b, p in pages:  # the new host blocks start empty
+        h = lay.host_block_table[b, p]
+        assert not host[:, h * BLOCK:(h + 1) * BLOCK].any()
     oracle.materialize_pages(gpu, host, lay.block_table, lay.host_block_table, pages, wl.n_layers)
     touched = np.zeros(host.shape[1], bool)
     for b, p in pages:
@@ -102,7 +114,7 @@ def test_released_page_resolves_to_its_rows_from_the_host_copy():
     tail = (int(wl.ctx[b]) - 1) // BLOCK
     p = int([q for q in np.nonzero(lay0.block_table[b] >= 0)[0] if q < tail][0])
     lay = spare_host_blocks(lay0, [(b, p)])
-    gpu, host = pools(wl, lay)
+    gpu, host = pools(wl, lay, new_host_blocks(lay, [(b, p)]))
     oracle.materialize_pages(gpu, host, lay.block_table, lay.host_block_table, [(b, p)], wl.n_layers)
     g = int(lay.block_table[b, p])
     assert oracle.release_pages(lay.block_table, lay.host_block_table, [(b, p)], wl.ctx) == [g]
