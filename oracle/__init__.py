@@ -19,7 +19,10 @@ pages it follows:
   and footnote 1 (656-byte FP8 rows; QK over 576 dims, PV over 512).
 * Part 1, "How it works", the paragraphs after the three residency states: the
   write side of the host pool (completed pages copied to host memory, then
-  giving up their GPU blocks without a second copy).
+  giving up their GPU blocks without a second copy), and hot pages leased from
+  the shared block pool and given back.
+* Part 1, "Composing with the rest of vLLM": per-step resolver plans that can
+  be replayed and share the request's hot state (speculative decoding).
 
 Where the pages are silent the reading taken is stated at the function.
 Parity status: every function below is pinned by tests under
@@ -30,6 +33,7 @@ in the tests.
 """
 from .hisparse_oracle import (  # noqa: F401
     BLOCK,
+    HotPool,
     HotState,
     attention,
     bf16_decode,
@@ -39,6 +43,7 @@ from .hisparse_oracle import (  # noqa: F401
     E4M3_VALUES,
     indexer_scores,
     materialize_pages,
+    release_hot,
     release_pages,
     resolve,
     topk_select,

@@ -147,8 +147,30 @@ class ResolveError(RuntimeError):
     pass
 
 
+class HotPool:
+    """The shared pool that hot pages are leased from (Part 1, "How it works": hot-buffer pages
+    are ordinary KV blocks leased from the same pool as resident pages, taken when a request
+    first needs them and given back when it no longer does; one request's freed blocks become
+    another's hot capacity).
+
+    Reading taken (the pages give no order): a first-in first-out list of free GPU blocks.  A
+    lease takes the block at the front; a returned block goes to the back."""
+
+    def __init__(self, blocks=()):
+        self.free = [int(x) for x in blocks]
+
+    def give_back(self, blocks) -> None:
+        self.free.extend(int(x) for x in blocks)
+
+    def lease(self) -> int:
+        if not self.free:
+            raise ResolveError("no free block left in the hot pool")
+        return self.free.pop(0)
+
+
 def resolve(topk: np.ndarray, block_table: np.ndarray, host_block_table: np.ndarray,
-            hot_blocks: np.ndarray, st: HotState):
+            hot_blocks: np.ndarray, st: HotState, pool: HotPool | None = None,
+            window_start: int | None = None):
     """Fused top-K resolver of one request, one call (Part 1, "How it works":
     a resident token is read where it is, a hot token is read and its LRU
     entry refreshed, a miss copies its single row from pinned host memory into
@@ -157,22 +179,35 @@ def resolve(topk: np.ndarray, block_table: np.ndarray, host_block_table: np.ndar
     topk              [S][K] int32, ascending, -1 padded (one list per query)
     block_table       [pages] int32, GPU block or -1 (placeholder)
     host_block_table  [pages] int32, host block or -1
-    hot_blocks        [H/64] int32, GPU blocks holding the hot slots
+    hot_blocks        [H/64] int32, GPU blocks holding the hot slots; with a `pool`, -1 marks a
+                      hot page not leased yet, and leases are written into it in place
     st                hot state, updated in place
+    pool              the shared pool hot pages are leased from, or None when every hot page
+                      has its block from the start
+    window_start      the call counter at which the request's current plan window began (None:
+                      this call begins one).  Part 1, "Composing with the rest of vLLM":
+                      speculative decoding runs on per-step plans that can be replayed and share
+                      the request's hot state.  Reading taken: a plan is the row ids one call
+                      emits; no slot touched by a call of the current window is given to a miss,
+                      so every plan of the window keeps reading its rows until a later call
+                      begins a new window (for instance once drafts are rejected).
 
     Readings taken where the pages are silent:
       * the LRU clock is the call counter; a hit and a fill both stamp it;
       * resident pages take precedence and never touch the LRU;
-      * victims are the slots not touched in this call, in (stamp, slot)
-        order, empty slots (stamp -1) first; the i-th miss in ascending token
-        order takes the i-th victim;
+      * victims are the slots not touched in this window (this call, when it
+        begins one), in (stamp, slot) order, empty slots (stamp -1) first; the
+        i-th miss in ascending token order takes the i-th victim;
+      * a miss whose victim slot lies on a hot page without a block leases one
+        from the pool (empty slots fill in ascending order, so pages are leased
+        in ascending order, as the request first needs them);
       * a placeholder page without a host copy is an error.
     Returns (row_ids [S][K] int32, copies, stats) where copies lists
     (token, slot, host_row, dst_row) and stats = (resident, hit, miss, pages
     of hot slots in use).
     """
     step = st.step
-    H = st.slot_token.shape[0]
+    protect = step if window_start is None else int(window_start)
     U = np.unique(topk[topk >= 0])                                   # sorted union
     page = U // BLOCK
     resident = block_table[page] >= 0
@@ -182,7 +217,7 @@ def resolve(topk: np.ndarray, block_table: np.ndarray, host_block_table: np.ndar
     for t in U[hot]:                                                 # refresh hits
         st.slot_stamp[st.tok2slot[t]] = step
 
-    cand = np.nonzero(st.slot_stamp < step)[0]                       # untouched slots
+    cand = np.nonzero(st.slot_stamp < protect)[0]                    # untouched in the window
     cand = cand[np.lexsort((cand, st.slot_stamp[cand]))]             # (stamp, slot) order
     misses = U[miss]
     if misses.shape[0] > cand.shape[0]:
@@ -199,6 +234,10 @@ def resolve(topk: np.ndarray, block_table: np.ndarray, host_block_table: np.ndar
         hb = int(host_block_table[t // BLOCK])
         if hb < 0:
             raise ResolveError(f"token {t}: placeholder page without a host copy")
+        if hot_blocks[s // BLOCK] < 0:
+            if pool is None:
+                raise ResolveError(f"hot page {s // BLOCK} has no block")
+            hot_blocks[s // BLOCK] = pool.lease()
         dst = int(hot_blocks[s // BLOCK]) * BLOCK + s % BLOCK
         copies.append((int(t), s, hb * BLOCK + int(t) % BLOCK, dst))
 
@@ -218,6 +257,24 @@ def resolve(topk: np.ndarray, block_table: np.ndarray, host_block_table: np.ndar
     stats = (int(resident.sum()), int(hot.sum()), int(miss.sum()), -(-used // BLOCK))
     st.step = step + 1
     return row_ids, copies, stats
+
+
+def release_hot(st: HotState, hot_blocks: np.ndarray, pool: HotPool | None = None) -> list:
+    """A request gives up its hot buffer (Part 1, "How it works": hot pages go back to the pool
+    when no longer needed; a freed block can become another request's hot capacity).  Its hot
+    state becomes cold, as for a new request in that slot; with a pool, its leased blocks go
+    back to the pool in page order and its hot-page table is cleared to -1.  Returns the blocks
+    given back."""
+    back = []
+    if pool is not None:
+        back = [int(x) for x in hot_blocks if x >= 0]
+        pool.give_back(back)
+        hot_blocks[:] = -1
+    st.slot_token[:] = -1
+    st.slot_stamp[:] = -1
+    st.tok2slot[:] = -1
+    st.step = 0
+    return back
 
 
 # ----------------------------------------------------------------- attention

@@ -66,9 +66,8 @@ static void timer_free(hs_ctx* ctx) {
 }
 
 hipError_t hs_set_kernel_attributes();
-hipError_t hs_resolve_set_attributes(size_t lds_bytes);
-hipError_t hs_select_set_attributes(const hs_config& c);
-size_t hs_resolve_lds_bytes(int S, int K, int H, int max_pages);
+hipError_t hs_resolve_set_attributes();
+hipError_t hs_select_set_attributes();
 
 namespace {
 
@@ -118,6 +117,9 @@ hs_status validate(const hs_config* c) {
     return fail(HS_ERR_UNSUPPORTED, "max_queries must be in [1, 4]");
   if (c->max_pages_per_req < 1 || (int64_t)c->max_pages_per_req * hs::kBlock > (1ll << 30))
     return fail(HS_ERR_INVALID_ARG, "max_pages_per_req out of range");
+  // the sweep addresses one request's score rows (S x tokens x 4 bytes) with 31-bit offsets
+  if ((int64_t)c->max_queries * c->max_pages_per_req * hs::kBlock * 4 >= (1ll << 31))
+    return fail(HS_ERR_INVALID_ARG, "max_queries x max_pages_per_req too large (score rows over 2 GiB)");
   const int H = c->hot_rows_per_req ? c->hot_rows_per_req : default_hot_rows(*c);
   if (H % hs::kBlock != 0 || H > hs::kMaxHot)
     return fail(HS_ERR_INVALID_ARG, "hot_rows_per_req must be a multiple of 64 and <= 16384 (got %d)", H);
@@ -173,6 +175,7 @@ hs_status hs::compute_layout(const hs_config& c, Layout* L) {
   L->off_seg_count = take(B * S * L->n_seg * 4);
   L->off_cands = take(B * S * L->n_seg * kSegCap * 8);
   L->off_path_count = take(2 * 8);
+  L->off_zero_row = take(kZeroRowBytes);
   L->total = off;
   return HS_OK;
 }
@@ -285,9 +288,8 @@ hs_status hs_create(const hs_config* cfg, hs_ctx** out) {
   std::memset(&ctx->ws, 0, sizeof(ctx->ws));
   hipError_t e = hipGetDevice(&ctx->device);
   if (e == hipSuccess) e = hs_set_kernel_attributes();
-  if (e == hipSuccess)
-    e = hs_resolve_set_attributes(hs_resolve_lds_bytes(cfg->max_queries, cfg->topk, ctx->lay.hot_rows, cfg->max_pages_per_req));
-  if (e == hipSuccess) e = hs_select_set_attributes(*cfg);
+  if (e == hipSuccess) e = hs_resolve_set_attributes();
+  if (e == hipSuccess) e = hs_select_set_attributes();
   if (e != hipSuccess) {
     delete ctx;
     return hip_fail(e, "hs_create");
@@ -363,6 +365,12 @@ hs_status hs_bind(hs_ctx* ctx, const hs_buffers* b) {
   ctx->ws.seg_count = reinterpret_cast<uint32_t*>(w + L.off_seg_count);
   ctx->ws.cands = reinterpret_cast<uint64_t*>(w + L.off_cands);
   ctx->ws.path_count = reinterpret_cast<unsigned long long*>(w + L.off_path_count);
+  ctx->ws.zero_row = w + L.off_zero_row;
+  // the row of zeros the decode reads for skipped rows: written once here, read-only for
+  // every kernel
+  hipError_t e = hipSetDevice(ctx->device);
+  if (e == hipSuccess) e = hipMemset(ctx->ws.zero_row, 0, hs::kZeroRowBytes);
+  if (e != hipSuccess) return hip_fail(e, "hs_bind: clearing the zero row");
   ctx->bound = true;
   return ok();
 }

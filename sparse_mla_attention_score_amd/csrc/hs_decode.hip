@@ -263,7 +263,8 @@ __global__ __launch_bounds__(kDecThreads) void sparse_mla_decode_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int rr = 32 * dh + 8 * (i >> 2) + 4 * hf + (i & 3);
-      c[i] = rr < n_tile ? c[i] * qk_scale_log2 : -INFINITY;
+      // rows past the range and skipped rows (id -1) are left out of the softmax
+      c[i] = rr < n_tile && rid_next[rr] >= 0 ? c[i] * qk_scale_log2 : -INFINITY;
       tmax = fmaxf(tmax, c[i]);
     }
     {
@@ -471,7 +472,7 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
     const int32_t* __restrict__ ctx_lens, int B, int S, int K, int max_ctx,
     const uint8_t* __restrict__ kv, int64_t n_rows_pool, float qk_scale_log2, int splits,
     int xcd_map, uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float* __restrict__ part_ml, int32_t* __restrict__ err) {
+    float* __restrict__ part_ml, const uint8_t* __restrict__ zero_row, int32_t* __restrict__ err) {
   // two tiles of raw rows (distinct objects, one filled while the other is read)
   __shared__ __align__(16) unsigned char tile_a[kF8TileBytes];
   __shared__ __align__(16) unsigned char tile_b[kF8TileBytes];
@@ -607,8 +608,12 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
         asm volatile("" : "+v"(c));
         const int row = (c * 1599) >> 16;  // c / 41 for c < 2,688
         const int piece = c - row * kF8RowChunks;
-        const int32_t rid = max(rids[t0 + row], 0);  // a skipped row reads row 0, masked later
-        lds_load16(kv + (int64_t)rid * kFp8Row + 16 * nope_swizzle(piece, row), buf + ins * 1024);
+        // a skipped row (id -1: past the range, or flagged) reads a row of zeros, so whatever
+        // the pool holds elsewhere cannot reach the products; its logit is masked as well
+        const int32_t rid = rids[t0 + row];
+        const uint8_t* src = rid >= 0 ? kv + (int64_t)rid * kFp8Row + 16 * nope_swizzle(piece, row)
+                                      : zero_row + 16 * piece;
+        lds_load16(src, buf + ins * 1024);
       }
     }
   };
@@ -700,9 +705,9 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(c[mb][i] - m_qk);
+        const float p = ok[mb][i] ? __builtin_amdgcn_exp2f(c[mb][i] - m_qk) : 0.0f;
         l_part += p;
-        pb[4 * mb + i] = (__bf16)(p * rsc[mb][i]);
+        pb[4 * mb + i] = (__bf16)(ok[mb][i] ? p * rsc[mb][i] : 0.0f);
       }
     pls[rh][hb][lane] = pb;
     lds_barrier();
@@ -901,7 +906,7 @@ hipError_t hs_launch_decode(const hs_ctx* ctx, int layer, const void* q, const i
                        static_cast<const uint16_t*>(q), row_ids, ctx_lens, B, S, c.topk,
                        c.max_pages_per_req * kBlock, kv, n_rows_pool, qk_scale_log2, splits,
                        xcd_map, static_cast<uint16_t*>(out), lse, ctx->ws.part_o, ctx->ws.part_ml,
-                       ctx->ws.err);
+                       ctx->ws.zero_row, ctx->ws.err);
   else
     hipLaunchKernelGGL(sparse_mla_decode_kernel<false>, grid, dim3(kDecThreads), DecLds::kTotal, stream,
                        static_cast<const uint16_t*>(q), row_ids, ctx_lens, B, S, c.topk,

@@ -40,18 +40,28 @@ struct KeyTile {
 };
 
 template <bool kFp8>
-__device__ __forceinline__ void load_key_tile(KeyTile<kFp8>& kt, const uint8_t* base, int o, int half) {
+__device__ __forceinline__ void load_key_codes(KeyTile<kFp8>& kt, const uint8_t* base, int o, int half) {
   if constexpr (kFp8) {
     const u32x4* kp = reinterpret_cast<const u32x4*>(base + o * 128 + 64 * half);
 #pragma unroll
     for (int v = 0; v < 4; ++v) kt.v[v] = kp[v];
-    kt.scale = *reinterpret_cast<const float*>(base + 8192 + o * 4);
   } else {
     const u32x4* kp = reinterpret_cast<const u32x4*>(base + o * 256 + 128 * half);
 #pragma unroll
     for (int v = 0; v < 8; ++v) kt.v[v] = kp[v];
-    kt.scale = 1.0f;
   }
+}
+
+template <bool kFp8>
+__device__ __forceinline__ void load_key_scale(KeyTile<kFp8>& kt, const uint8_t* base, int o) {
+  if constexpr (kFp8) kt.scale = *reinterpret_cast<const float*>(base + 8192 + o * 4);
+  else kt.scale = 1.0f;
+}
+
+template <bool kFp8>
+__device__ __forceinline__ void load_key_tile(KeyTile<kFp8>& kt, const uint8_t* base, int o, int half) {
+  load_key_codes<kFp8>(kt, base, o, half);
+  load_key_scale<kFp8>(kt, base, o);
 }
 
 // B operand of k-step s: dims 64 * half + 8 s .. +8 of the lane's token.
@@ -128,6 +138,13 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
+  // the request's score rows and candidate lists as buffer resources (sizes checked on the
+  // host to stay below 2^31 bytes); kOffEnd lies past both
+  constexpr uint32_t kOffEnd = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      scores + (int64_t)b * S * lmax, (short)0, (int)(S * lmax * 4), kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      cands + (int64_t)b * S * n_seg * kSegCap, (short)0, S * n_seg * kSegCap * 8, kBufferRsrcWord3);
   // candidate list: this wave's segment of each query's list, and the keys from which a token
   // is listed (kGuessOff: none)
   const int seg = item * kSweepWaves + wave;
@@ -208,39 +225,41 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
       const uint32_t bits = __float_as_uint(total) & 0x7fffffffu;
       const int jj = jp + half;
       const bool vis = jj <= jq && (jq > jp || half == 0) && t < L - S + 1 + jj;
-      if (vis) {
-        scores[(int64_t)(b * S + jj) * lmax + t] = __uint_as_float(bits);
-        const uint32_t bin = bits >> kHistShift;
-        atomicAdd(&lhist[jj][bin >> 1], 1u << (16 * (bin & 1)));
-      }
+      // No branch around a memory instruction in the loop: the stores are buffer stores whose
+      // lanes with nothing to store give an offset past the end (dropped by the hardware), so
+      // every iteration issues the same number of vector-memory instructions and the waits for
+      // the key ring count exactly the loads they need.  (Under a branch, the count differs
+      // between iterations and every wait has to drain all loads in flight.)  The histogram
+      // update adds zero for an invisible token.
+      const uint32_t soff = vis ? (uint32_t)(jj * lmax + t) * 4u : kOffEnd;
+      __builtin_amdgcn_raw_buffer_store_b32(bits, srs, soff, 0, 0);
+      const uint32_t bin = bits >> kHistShift;
+      atomicAdd(&lhist[jj][bin >> 1], vis ? 1u << (16 * (bin & 1)) : 0u);
       // list the token for the next select if its key reaches the query's guess: lanes 0-31
       // serve query jp, lanes 32-63 query jq; a lane's place is the number of listed lanes
       // below it in its half
       const bool cand = vis && bits >= (half ? gq[jq] : gq[jp]);
       const uint64_t m = __ballot(cand);
-      if (m) {
-        const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
-        const int pos = (half ? cq[jq] : cq[jp]) +
-                        (int)(half ? __builtin_amdgcn_mbcnt_hi(mhi, 0u) : __builtin_amdgcn_mbcnt_lo(mlo, 0u));
-        if (cand && pos < kSegCap)
-          cands[((int64_t)(b * S + jj) * n_seg + seg) * kSegCap + pos] =
-              ((uint64_t)bits << 32) | (uint32_t)(~(uint32_t)t);
-        cq[jp] += __popc(mlo);
-        if (jq > jp) cq[jq] += __popc(mhi);
-      }
+      const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+      const int pos = (half ? cq[jq] : cq[jp]) +
+                      (int)(half ? __builtin_amdgcn_mbcnt_hi(mhi, 0u) : __builtin_amdgcn_mbcnt_lo(mlo, 0u));
+      const uint32_t coff = cand && pos < kSegCap ? (uint32_t)((jj * n_seg + seg) * kSegCap + pos) * 8u : kOffEnd;
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{~(uint32_t)t, bits}, crs, coff, 0, 0);
+      cq[jp] += __popc(mlo);
+      if (jq > jp) cq[jq] += __popc(mhi);
     }
   };
 
-  // The last query's sum of tile k runs during tile k + 1 (before the first tile it is a
-  // masked no-op on zero accumulators); with one query there is nothing to overlap.
-  int t_prev = INT32_MAX / 2;
-  float sc_prev = 0.0f;
+  // Each query's weighted ReLU sum runs beside the next query's MFMA chain; the last one ends
+  // the tile.  A slot's key codes are refilled right after its conversion, its scale only once
+  // the tile's last sum has used the old one: no value of a slot lives across the refill, so
+  // the loop carries no register copies of loads in flight (a copy would make the loop wait
+  // for the load).
   for (int k0 = 0; k0 < kTilesPerWave; k0 += kRing) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
       const int k = k0 + u;
       const int t = ring_t0[u] + col;
-      const float sc = ring[u].scale;
       asm volatile("" : "+v"(q_off), "+v"(w_off));
       bf16x8 kb[8];
 #pragma unroll
@@ -248,7 +267,9 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
       // refill the slot with tile k + kRing (the last round re-reads the final tile, masked
       // by never being scored)
       const int kn = min(k + kRing, kTilesPerWave - 1);
-      load_key_tile<kFp8>(ring[u], tile_src(kn, ring_t0[u]), (kn & 1) * 32 + col, half);
+      const uint8_t* src = tile_src(kn, ring_t0[u]);
+      const int o_next = (kn & 1) * 32 + col;
+      load_key_codes<kFp8>(ring[u], src, o_next, half);
 #pragma unroll
       for (int j = 0; j < S; ++j) {
         // A operand of k-step s for query j: Q[j][head = col][dims 64*half + 8*s .. +8]
@@ -258,15 +279,12 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
           a = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(lq + q_off + j * kIdxHeads * kQRowBytes + 16 * s)),
                            kb[s], a);
         acc[j] = a;
-        if (S == 1) finish(0, t, sc);
-        else if (j > 0) finish(j - 1, t, sc);
-        else finish(S - 1, t_prev, sc_prev);
+        if (j > 0) finish(j - 1, t, ring[u].scale);
       }
-      t_prev = t;
-      sc_prev = sc;
+      finish(S - 1, t, ring[u].scale);
+      load_key_scale<kFp8>(ring[u], src, o_next);
     }
   }
-  if (S > 1) finish(S - 1, t_prev, sc_prev);
   if (lane == 0) {
 #pragma unroll
     for (int j = 0; j < S; ++j) seg_count[(int64_t)(b * S + j) * n_seg + seg] = (uint32_t)cq[j];
@@ -843,9 +861,11 @@ hipError_t launch_scores(const hs_ctx* ctx, const void* q_idx, const float* w,
 
 using namespace hs;
 
-// Dynamic-LDS limit of the select: the candidates plus, with the LDS bitmap, the bitmap.
-hipError_t hs_select_set_attributes(const hs_config& c) {
-  const int lds = hs_select_cand_cap(c) * (int)sizeof(uint64_t) + kLdsBitmapMaxWords * 4;
+// Dynamic-LDS limit of the select: the largest candidate list plus the largest LDS bitmap.  The
+// attribute is process-wide, so it is always set to this one maximum, whatever the context's
+// own cap: a context created later never lowers it under a live one.
+hipError_t hs_select_set_attributes() {
+  const int lds = kDefaultCandCap * (int)sizeof(uint64_t) + kLdsBitmapMaxWords * 4;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_select_kernel<true>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e == hipSuccess)

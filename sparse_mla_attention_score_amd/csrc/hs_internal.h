@@ -36,6 +36,8 @@ constexpr int kSegCap = 192;
 constexpr int kSweepWaves = 4;
 constexpr uint32_t kGuessOff = 0xFFFFFFFFu;  // no guess: no candidates are written
 
+constexpr int kZeroRowBytes = 1024;  // >= one FP8 row (656 bytes)
+
 // Decode split-K.
 constexpr int kTileRows = 64;
 constexpr int kMaxSplits = 32;
@@ -62,12 +64,14 @@ struct Workspace {
   uint32_t* seg_count;   // [Bmax][Smax][n_seg] candidates each sweep wave found (> kSegCap: overflow)
   uint64_t* cands;       // [Bmax][Smax][n_seg][kSegCap] (key << 32) | ~token
   unsigned long long* path_count;  // [2] selections made from the candidate list / the scores
+  uint8_t* zero_row;     // [kZeroRowBytes]    zeros: what a skipped row of the decode reads
 };
 
 struct Layout {
   size_t off_slot_token, off_slot_stamp, off_lru_order, off_tok2slot, off_req_step, off_req_used,
       off_err, off_scores, off_hist, off_bitmap, off_miss_src, off_miss_dst, off_miss_cnt,
-      off_part_o, off_part_ml, off_guess, off_seg_count, off_cands, off_path_count, total;
+      off_part_o, off_part_ml, off_guess, off_seg_count, off_cands, off_path_count, off_zero_row,
+      total;
   int32_t hot_rows;
   int64_t lmax;       // max_pages_per_req * 64
   int64_t bm_words;   // bitmap words per (request, query): lmax rounded up to 1,024, / 32

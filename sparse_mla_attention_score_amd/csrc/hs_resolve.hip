@@ -499,10 +499,6 @@ static size_t resolve_lds_with_tables(int S, int K, int H, int max_pages) {
   return with <= 160 * 1024 - 2048 ? with : base;
 }
 
-size_t hs_resolve_lds_bytes(int S, int K, int H, int max_pages) {
-  return resolve_lds_with_tables(S, K, H, max_pages);
-}
-
 hipError_t hs_launch_resolve(const hs_ctx* ctx, const int32_t* topk, const int32_t* ctx_lens, int B,
                              int S, int32_t* row_ids, int32_t* stats, hipStream_t stream) {
   const hs_config& c = ctx->cfg;
@@ -553,7 +549,15 @@ hipError_t hs_launch_hot_reset(const hs_ctx* ctx, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t hs_resolve_set_attributes(size_t lds_bytes) {
+// The resolver's dynamic-LDS limit: everything a CU's 160 KiB leaves beside the kernel's static
+// arrays.  The attribute is process-wide (per kernel, not per context), so it is always set to
+// this one maximum: a context created later can never lower it under a live one, and every
+// layout a call picks (at most 160 KiB less 2 KiB) stays within it.
+hipError_t hs_resolve_set_attributes() {
+  hipFuncAttributes fa;
+  hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&resolve_kernel));
+  if (e != hipSuccess) return e;
+  const int lds = 160 * 1024 - (int)fa.sharedSizeBytes;
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&resolve_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
 }
