@@ -29,7 +29,8 @@
  *     context shorter than its query count) set a sticky device error word, read with
  *     hs_read_device_error() outside the hot loop; the offending item is skipped, no access
  *     leaves its buffer, and the other results of that call are unspecified (a skipped key
- *     page leaves its tokens' scores stale, a skipped row reads as zeros).
+ *     page leaves its tokens' scores stale; a skipped row id, or -1 inside a query's range,
+ *     is left out of that query's softmax).
  *   - Device buffers are borrowed: the caller allocates them (e.g. with PyTorch) and keeps
  *     them alive while bound.  The library owns only the context and the pinned host pool.
  *   - The three step calls allocate nothing, never synchronise and take every per-step

@@ -33,14 +33,23 @@ def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
 
 class GpuWorkload:
     def __init__(self, wl: synth.Workload, device: str = "cuda:0", topk_lds_candidates: int = 0,
-                 layout: synth.Layout | None = None, verbose: bool = False):
+                 layout: synth.Layout | None = None, verbose: bool = False,
+                 max_pages: int | None = None, max_queries: int | None = None):
+        """`max_pages` / `max_queries` configure the context wider than the workload needs (the
+        block tables are padded with placeholders)."""
         self.wl = wl
         self.lay = layout or synth.make_layout(wl)
         lay = self.lay
+        if max_pages is not None and max_pages > lay.block_table.shape[1]:
+            pad = ((0, 0), (0, max_pages - lay.block_table.shape[1]))
+            lay.block_table = np.pad(lay.block_table, pad, constant_values=-1)
+            lay.host_block_table = np.pad(lay.host_block_table, pad, constant_values=-1)
+            lay.idx_block_table = np.pad(lay.idx_block_table, pad, constant_values=-1)
         self.dev = torch.device(device)
         cfg = hsb.make_config(topk=wl.topk, kv_dtype=wl.kv_dtype, idx_dtype=wl.idx_dtype,
-                              n_layers=wl.n_layers, max_batch=wl.batch, max_queries=wl.queries,
-                              max_pages_per_req=wl.max_pages, hot_rows_per_req=wl.hot_rows,
+                              n_layers=wl.n_layers, max_batch=wl.batch,
+                              max_queries=max_queries or wl.queries,
+                              max_pages_per_req=lay.block_table.shape[1], hot_rows_per_req=wl.hot_rows,
                               num_gpu_blocks=lay.num_gpu_blocks, num_idx_blocks=lay.num_idx_blocks,
                               num_host_blocks=lay.num_host_blocks,
                               topk_lds_candidates=topk_lds_candidates)
@@ -76,7 +85,8 @@ class GpuWorkload:
         self.w = torch.from_numpy(self.w_np).to(self.dev)
         self.sm_scale = 1.0 / math.sqrt(576.0)
         self._keys = {}
-        self.states = [oracle.HotState.cold(wl.hot_rows, wl.max_pages * 64) for _ in range(wl.batch)]
+        self.states = [oracle.HotState.cold(wl.hot_rows, lay.block_table.shape[1] * 64)
+                       for _ in range(wl.batch)]
 
     # ------------------------------------------------------------ inputs
     def inputs(self, step: int):

@@ -6,8 +6,9 @@ import numpy as np
 import pytest
 import torch
 
+import sparse_mla_attention_score_amd.hisparse as hsb
 import synth
-from hs_harness import GpuWorkload, check_topk
+from hs_harness import GpuWorkload, check_attention, check_topk
 
 pytestmark = pytest.mark.gpu
 
@@ -176,3 +177,96 @@ def test_kernel_timing_counts_each_launch():
     assert t["decode"][1] == 2
     assert all(ms > 0 for ms, n in t.values() if n)
     gw.close()
+
+
+def test_fp8_decode_ignores_nan_bytes_outside_its_rows():
+    # Block 0 of the pool is never used and holds NaN codes (0xFF) and a NaN scale in every
+    # row.  A short context (97 rows: a partial 64-row tile) and row ids replaced by -1 in the
+    # middle of a list must still give the oracle's output over the remaining rows.
+    wl = synth.toy(seed=26, batch=2, queries=1, ctx=(97, 300), topk=128, steps=1,
+                   residency=[(synth.RES_FULL, 1.0)] * 2)
+    lay = synth.make_layout(wl)
+    lay.block_table[lay.block_table >= 0] += 1
+    lay.hot_blocks = lay.hot_blocks + 1
+    lay.num_gpu_blocks += 1
+    print("[nan pool] build", flush=True)
+    gw = GpuWorkload(wl, layout=lay)
+    kv = gw.ctx.kv_pool.view(wl.n_layers, lay.num_gpu_blocks, 64 * wl.row_bytes)
+    kv[:, 0] = 0xFF
+    torch.cuda.synchronize()
+    qidx, q, lens = gw.inputs(0)
+    tk = gw.gpu_topk(qidx, lens)
+    rows, _ = gw.gpu_resolve(tk, lens)
+    rows_np = rows.cpu().numpy()
+    tk_np = tk.cpu().numpy()
+    drop = {1: [5, 17, 100]}  # request 1: three entries skipped
+    for b, idx in drop.items():
+        rows_np[b, 0, idx] = -1
+    rows_cut = torch.from_numpy(rows_np).to(gw.dev)
+    out, lse = gw.gpu_decode(0, q, rows_cut, lens)
+    out = out.float().cpu().numpy().astype(np.float64)
+    lse = lse.cpu().numpy().astype(np.float64)
+    # a -1 inside a query's range is an invalid row id: flagged, and left out of the softmax
+    assert gw.ctx.device_error() == hsb.HS_DEVERR_BAD_ROW
+    for b in range(wl.batch):
+        keep = tk_np[b, 0] >= 0
+        for i in drop.get(b, []):
+            keep[i] = False
+        o_ref, l_ref = gw.oracle_attention(b, 0, 0, tk_np[b, 0][keep], q)
+        assert np.all(np.isfinite(out[b, 0])), f"NaN in request {b}"
+        check_attention(out[b, 0], lse[b, 0], o_ref, l_ref)
+    gw.close()
+
+
+def test_two_live_contexts_of_different_shapes():
+    # Kernel LDS limits are process-wide: a second, smaller context created while a larger
+    # one is alive must not break it.  The wide context also resolves one query at a time
+    # although it is configured for two, on a page table large enough that the one-query
+    # layout keeps the page tables in LDS.
+    from test_gpu_parity import run_isolated
+    big = synth.toy(seed=27, batch=2, queries=4, ctx=(6000, 2600), topk=512, steps=4)
+    print("[two contexts] build", flush=True)
+    a = GpuWorkload(big)
+    small = synth.toy(seed=28, batch=3, queries=1, ctx=(3000, 900, 1400), topk=64, steps=4)
+    b = GpuWorkload(small, topk_lds_candidates=1)
+    wide = synth.toy(seed=29, batch=1, queries=1, ctx=(5000,), topk=2048, hot_rows=4096, steps=2)
+    c = GpuWorkload(wide, max_pages=12000, max_queries=2)
+    for gw in (a, b, c):
+        gw.steps_done = 0
+    for rnd in range(2):
+        for name, gw in (("big", a), ("small", b), ("wide", c)):
+            print(f"[two contexts] round {rnd} {name}", flush=True)
+            run_one_step(gw)
+    for gw in (a, b, c):
+        assert gw.ctx.device_error() == 0
+        gw.close()
+
+
+def run_one_step(gw: GpuWorkload):
+    """Step `gw.steps_done` of a workload in stage-isolated parity with the oracle."""
+    from hs_harness import check_attention as _chk
+    wl = gw.wl
+    step = gw.steps_done
+    qidx, q, lens = gw.inputs(step)
+    tk_gpu = gw.gpu_topk(qidx, lens).cpu().numpy()
+    tk_ref = np.empty_like(tk_gpu)
+    for b in range(wl.batch):
+        ref, sc = gw.oracle_topk(b, qidx, int(lens[b]))
+        tk_ref[b] = ref
+        for j in range(wl.queries):
+            check_topk(tk_gpu[b, j], sc[j], wl.topk)
+    rows_dev, stats_dev = gw.gpu_resolve(torch.from_numpy(tk_ref).to(gw.dev), lens)
+    rows, stats = rows_dev.cpu().numpy(), stats_dev.cpu().numpy()
+    for b in range(wl.batch):
+        rows_ref, _, st_ref = gw.oracle_resolve(b, tk_ref[b])
+        assert np.array_equal(rows[b], rows_ref), f"row ids differ, request {b}"
+        assert tuple(int(x) for x in stats[b]) == st_ref
+    out, lse = gw.gpu_decode(0, q, rows_dev, lens)
+    out = out.float().cpu().numpy().astype(np.float64)
+    lse = lse.cpu().numpy().astype(np.float64)
+    for b in range(wl.batch):
+        for j in range(wl.queries):
+            toks = tk_ref[b, j][tk_ref[b, j] >= 0]
+            o_ref, l_ref = gw.oracle_attention(b, j, 0, toks, q)
+            _chk(out[b, j], lse[b, j], o_ref, l_ref)
+    gw.steps_done = step + 1
