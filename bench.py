@@ -137,10 +137,15 @@ def main() -> int:
         if ev is not None:
             ev[3].record(stream)
 
-    misses_warm = []
+    # warm-up steps, each timed on its own (step 0 starts from a cold hot buffer)
+    misses_warm, warm_ms = [], []
     for step in range(args.warmup):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         run_step(step)
+        e1.record(stream)
         torch.cuda.synchronize()
+        warm_ms.append(e0.elapsed_time(e1))
         misses_warm.append(int(stats[:, 2].sum()))
     err = ctx.device_error()
     if err:
@@ -232,7 +237,11 @@ def main() -> int:
     idx_gbps = idx_b / (t_idx * 1e-3) / 1e9
     gat_gbps = gat_b / (t_dec * 1e-3) / 1e9
     both_gbps = (idx_b + gat_b) / ((t_idx + t_dec) * 1e-3) / 1e9
-    mfma_util = att_f / (t_dec * 1e-3) / (BF16_DENSE_TFLOPS * 1e12)
+    # the decode kernels' own time (plus the split-K merge where it runs), not the stage time
+    # between events, which also holds launch gaps
+    t_dec_kernels_ms = (ktimes["decode"][0] + ktimes["decode_merge"][0]) / args.steps
+    mfma_util = att_f / (t_dec_kernels_ms * 1e-3) / (BF16_DENSE_TFLOPS * 1e12)
+    stream_read = measure_stream_read(torch, dev)
     # host link: the copy kernel's rate over the instrumented steps' misses, and the rate over
     # the whole resolve stage (resolver + copy)
     inst_misses = int(miss_acc.item()) / args.steps
@@ -243,6 +252,8 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, chains, args.cpu_sample_requests)
+    all_ms = sum(warm_ms) + elapsed_ms
+    n_all = args.warmup + args.steps
 
     splits = hsb.hs_decode_splits(ctx.ctx, B, S)
     line = {
@@ -256,8 +267,21 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8+bf16",
+        "dtype_detail": {
+            "indexer": "bf16 MFMA over FP8 E4M3 keys converted to bf16 exactly; fp32 accumulate and weighted ReLU sum",
+            "attention_qk_nope": "FP8 E4M3 MFMA; the bf16 query as two exact E4M3 parts under a per-head power-of-two scale; fp32 accumulate",
+            "attention_qk_rope_and_pv": "bf16 MFMA, fp32 accumulate",
+            "softmax": "fp32", "outputs": "bf16 (lse fp32)"},
         "data": "synthetic (seeded; FP8 E4M3 rows and keys, bf16 queries)",
+        "rates": {"steady_layer_steps_per_s": round(layer_steps_per_s, 3),
+                  "all_steps_layer_steps_per_s": round(n_all * NL / (all_ms / 1e3), 3),
+                  "all_steps_note": f"{args.warmup} warm-up steps (the first from a cold hot buffer) "
+                                    f"and the {args.steps} timed steps",
+                  "cold_step0_ms": round(warm_ms[0], 4) if warm_ms else None,
+                  "warmup_steps_ms": [round(x, 4) for x in warm_ms],
+                  "request_layer_steps_per_s": round(layer_steps_per_s * B, 1),
+                  "query_tokens_per_s": round(layer_steps_per_s / NL * B * S, 1)},
         "config": {"workload": wl.name, "batch": B, "queries_per_request": S,
                    "ctx": int(wl.ctx[0]), "topk": K, "layers": NL, "hot_rows": wl.hot_rows,
                    "resident_fraction": wl.residency[0][1], "scale": args.scale,
@@ -270,8 +294,11 @@ def main() -> int:
                     "selections_from_candidate_list": sel_list, "selections_from_scores": sel_scores},
         "gather": {"algorithmic_bytes": int(gat_b), "gbps": round(gat_gbps, 1),
                    "frac_hbm_peak": round(gat_gbps / HBM_PEAK_GBPS, 4)},
-        "attention": {"algorithmic_flops": int(att_f), "tflops": round(att_f / (t_dec * 1e-3) / 1e12, 2),
-                      "mfma_util_bf16_dense": round(mfma_util, 4)},
+        "attention": {"algorithmic_flops": int(att_f),
+                      "kernel_us_per_step": round(t_dec_kernels_ms * 1e3, 1),
+                      "tflops": round(att_f / (t_dec_kernels_ms * 1e-3) / 1e12, 2),
+                      "mfma_util_bf16_dense": round(mfma_util, 4),
+                      "stage_tflops": round(att_f / (t_dec * 1e-3) / 1e12, 2)},
         "materialize": mat,
         "host_link": {"misses_last_step": last_miss, "misses_last_timed_step": timed_miss,
                       "misses_warmup_steps": misses_warm,
@@ -286,6 +313,8 @@ def main() -> int:
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(sweep_b),
                      "avg_launch_us": round(t_sweep_ms * 1e3, 1),
+                     "measured_stream_read_gbps": round(stream_read, 1),
+                     "frac_of_measured_stream_read": round(sweep_gbps / stream_read, 4),
                      "mfma_frac_bf16_dense": round(sweep_f / (t_sweep_ms * 1e-3) / (BF16_DENSE_TFLOPS * 1e12), 4)},
         "cpu_baseline": cpu,
         "host_wall_s": round(t_host, 4),
@@ -293,6 +322,67 @@ def main() -> int:
     print(json.dumps(line), flush=True)
     ctx.close()
     return 0
+
+
+def measure_stream_read(torch, dev) -> float:
+    """The box's streaming-read rate (GB/s): a reduction over a 4 GiB fp32 buffer, best of 5."""
+    x = torch.ones(1 << 30, dtype=torch.float32, device=dev)
+    best = 0.0
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        x.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del x
+    return best
+
+
+def cpu_info() -> dict:
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "model": model}
+
+
+def oracle_one_thread_8k():
+    """The oracle on the 8K single-request workload (bf16 rows and keys), all stages, with the
+    BLAS pool held to one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import synth
+
+    wl = synth.config(1)
+    chains = [synth.qidx(wl, 0, 1)]
+    w = synth.head_weights(wl)
+    q = synth.mla_q(wl, 0)
+    lay = synth.make_layout(wl)
+    L = int(wl.ctx_at(0)[0])
+    codes, sc = synth.idx_tokens(wl, 0, 0, L)
+    rows_all = synth.latent_tokens(wl, 0, 0, np.arange(L))
+    reps, t = 3, 0.0
+    with threadpool_limits(limits=1):
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            keys = oracle.dequant_idx_keys(codes, sc)
+            scores = oracle.indexer_scores(np.stack(chains[0][:1]), w[0], keys)
+            tk = oracle.topk_select(scores[0], wl.topk)
+            st = oracle.HotState.cold(wl.hot_rows, wl.max_pages * 64)
+            oracle.resolve(tk[None], lay.block_table[0], lay.host_block_table[0], lay.hot_blocks[0], st)
+            toks = tk[tk >= 0]
+            lat = oracle.decode_latent_rows(rows_all[toks], wl.kv_dtype)
+            oracle.attention(q[0, 0], lat, 1.0 / math.sqrt(576.0))
+            t += time.perf_counter() - t0
+    return {"workload": wl.name, "value": round(reps / t, 3), "unit": "layer-steps/s", "threads": 1}
 
 
 def cpu_baseline(wl, chains, n_req: int):
@@ -334,7 +424,7 @@ def cpu_baseline(wl, chains, n_req: int):
     per_step_s = t_total / n_req * wl.batch
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": round(wl.n_layers / per_step_s, 6), "unit": "layer-steps/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "host": cpu_info(), "one_thread_8k": oracle_one_thread_8k(),
             "sample": f"{n_req} of {wl.batch} requests, decode step 0 (cold hot buffer), all stages; "
                       f"{t_total:.1f} s of oracle time scaled by {wl.batch}/{n_req}"}
 

@@ -71,6 +71,9 @@ typedef enum { HS_BF16 = 0, HS_FP8_E4M3 = 1 } hs_dtype;
 #define HS_DEVERR_TOPK_COUNT     0x10 /* internal: selection did not produce min(K, L) tokens */
 #define HS_DEVERR_HOT_FULL       0x20 /* more misses than untouched hot slots */
 #define HS_DEVERR_TAIL_PAGE      0x40 /* release of the tail page or of a page past the context */
+#define HS_DEVERR_POOL_EMPTY     0x80 /* a hot page needed a block and the free-block pool was empty */
+#define HS_DEVERR_POOL_FULL      0x100 /* more free blocks given than the pool holds */
+#define HS_DEVERR_BAD_REQUEST    0x200 /* a request index outside [0, max_batch) */
 
 /*
  * Static configuration.  Fixed kernel shapes must be given as listed; the rest size the
@@ -102,7 +105,14 @@ typedef struct hs_config {
   int32_t topk_lds_candidates; /* 0 => default; otherwise caps the on-chip candidate list of
                                   the top-K select (a smaller cap exercises the multi-pass
                                   path; results are identical) */
-  int32_t reserved;
+  int32_t hot_leasing;       /* 0: every request's hot pages have their blocks in hot_blocks from
+                                the start.  1: hot pages are leased from the context's pool of
+                                free blocks when a request first fills a slot on them and go
+                                back to it when the request is released (part-1 page, "How it
+                                works": hot-buffer pages are ordinary KV blocks leased from the
+                                same pool as resident pages, taken when first needed and
+                                returned when no longer needed; one request's freed blocks
+                                become another's hot capacity).  Needs num_host_blocks > 0. */
   int64_t num_gpu_blocks;    /* blocks of the shared KV pool (resident pages + hot pages) */
   int64_t num_idx_blocks;    /* blocks of the indexer key pool */
   int64_t num_host_blocks;   /* blocks of the pinned host pool */
@@ -117,7 +127,9 @@ typedef struct hs_buffers {
                                       placeholder whose rows live only in host memory
                                       (hisparse_release_pages writes placeholders into it) */
   const int32_t* host_block_table; /* [max_batch][max_pages_per_req] host block or -1 */
-  const int32_t* hot_blocks;       /* [max_batch][hot_rows/64] GPU blocks leased as hot pages */
+  int32_t* hot_blocks;             /* [max_batch][hot_rows/64] GPU block of each hot page.  With
+                                      hot_leasing the library owns its contents: -1 for a page
+                                      without a block, written by the leases and releases */
   void* workspace;                 /* hs_workspace_bytes() bytes, 256-byte aligned */
 } hs_buffers;
 
@@ -148,8 +160,10 @@ hs_status hs_host_pool_alloc(hs_ctx* ctx, void** host_base);
  * Re-binding replaces the previous set (the hot state must then be reset). */
 hs_status hs_bind(hs_ctx* ctx, const hs_buffers* bufs);
 
-/* Reset the hot buffer of every request to cold (all slots empty, LRU clock 0), clear
- * the top-K scratch and the device error word.  Enqueued on `stream`. */
+/* Reset the hot buffer of every request to cold (all slots empty, LRU clock 0, a new plan
+ * window), clear the top-K scratch and the device error word.  With hot_leasing the
+ * free-block pool is emptied and every hot_blocks entry set to -1 (give the pool its blocks
+ * with hs_hot_pool_give afterwards).  Enqueued on `stream`. */
 hs_status hs_hot_reset(hs_ctx* ctx, void* stream);
 
 /*
@@ -166,7 +180,7 @@ hs_status hs_hot_reset(hs_ctx* ctx, void* stream);
  * call's selection threshold lies (from this call's score histogram); the sweep then also
  * lists the tokens scoring above the guess, and the select reads that short list instead of
  * every score whenever the histogram proves it complete.  The result is the same either way;
- * hs_hot_reset clears the guesses.
+ * hs_hot_reset and hs_hot_release clear the guesses.
  */
 hs_status hisparse_index_topk(hs_ctx* ctx, const void* q_idx, const float* w,
                               const int32_t* ctx_lens, int32_t B, int32_t S, int32_t* topk_out,
@@ -192,6 +206,53 @@ hs_status hisparse_index_topk(hs_ctx* ctx, const void* q_idx, const float* w,
  */
 hs_status hisparse_resolve(hs_ctx* ctx, const int32_t* topk, const int32_t* ctx_lens, int32_t B,
                            int32_t S, int32_t* row_ids_out, int32_t* stats_out, void* stream);
+
+/*
+ * hisparse_resolve with plan windows (part-1 page, "Composing with the rest of vLLM":
+ * speculative decoding runs on per-step resolver plans that can be replayed and share the
+ * request's hot state).  A plan is the row_ids one call emits.  Reading taken: consecutive
+ * calls of a request form a window; no slot touched by a call of the current window is given
+ * to a miss, so every plan of the window stays valid (its rows keep their tokens and can be
+ * gathered again, e.g. to replay sparse_mla_decode) until a call begins a new window, for
+ * instance after drafts are rejected.
+ *   begin_window  device [B] int32: nonzero where request b's call begins a new window; NULL
+ *                 means every call begins one (hisparse_resolve)
+ * The union of the selections of one window must fit the hot buffer; otherwise the misses
+ * past the free slots are flagged HS_DEVERR_HOT_FULL and get row -1.
+ */
+hs_status hisparse_resolve_plan(hs_ctx* ctx, const int32_t* topk, const int32_t* ctx_lens,
+                                int32_t B, int32_t S, const int32_t* begin_window,
+                                int32_t* row_ids_out, int32_t* stats_out, void* stream);
+
+/*
+ * Hot-buffer lifetime of single requests (part-1 page, "How it works": hot pages are taken
+ * when a request first needs them and returned when it no longer does).
+ *
+ * hs_hot_release: for each of the n request slots in `reqs` (device [n] int32), in order,
+ *   the request's hot buffer becomes cold, as after hs_hot_reset for that request alone:
+ *   empty slots, LRU clock 0, no token mapped to a slot, a new plan window, no top-K guess.
+ *   With hot_leasing its blocks go back to the end of the free-block pool in page order and
+ *   its hot_blocks entries become -1.  A slot must be released before a new request reuses it;
+ *   otherwise the old request's tokens would be found in its hot buffer.
+ * hs_hot_pool_give: append the n blocks of `blocks` (device [n] int32; entries < 0 are
+ *   skipped) to the end of the free-block pool, e.g. the blocks hisparse_release_pages freed
+ *   or the blocks set aside for hot pages at start-up.  Blocks past the pool's capacity
+ *   (num_gpu_blocks) are dropped with HS_DEVERR_POOL_FULL.
+ * Leases happen inside hisparse_resolve / hisparse_resolve_plan: after the requests of a call
+ * are resolved, the pages that got their first filled slot take blocks from the front of the
+ * pool, request by request and page by page in ascending order.  An empty pool sets
+ * HS_DEVERR_POOL_EMPTY and those rows read -1; the request should then be released.
+ * Both calls allocate nothing and never synchronise; n = 0 is a no-op.  Host errors:
+ * HS_ERR_INVALID_ARG (NULL ctx, n < 0, NULL list with n > 0), HS_ERR_STATE (not bound;
+ * hs_hot_pool_give without hot_leasing).
+ */
+hs_status hs_hot_release(hs_ctx* ctx, const int32_t* reqs, int32_t n, void* stream);
+hs_status hs_hot_pool_give(hs_ctx* ctx, const int32_t* blocks, int32_t n, void* stream);
+
+/* Synchronise the context's device and copy the free-block pool, front first, into `out`
+ * (host, room for `cap` entries); *n gets the number of free blocks (which may exceed cap).
+ * For tests and inspection; never on the hot path.  HS_ERR_STATE without hot_leasing. */
+hs_status hs_hot_pool_read(hs_ctx* ctx, int32_t* out, int32_t cap, int32_t* n);
 
 /*
  * Sparse MLA decode attention of layer `layer` for B x S queries:
@@ -278,7 +339,10 @@ typedef enum {
   HS_KERNEL_HOT_RESET = 6,    /* hot-buffer reset */
   HS_KERNEL_MATERIALIZE = 7,  /* device-to-host copy of completed pages */
   HS_KERNEL_RELEASE = 8,      /* pages giving up their GPU blocks */
-  HS_KERNEL_COUNT = 9
+  HS_KERNEL_LEASE = 9,        /* hot pages taking blocks from the free-block pool */
+  HS_KERNEL_HOT_RELEASE = 10, /* requests' hot buffers made cold, blocks returned */
+  HS_KERNEL_POOL_GIVE = 11,   /* blocks appended to the free-block pool */
+  HS_KERNEL_COUNT = 12
 } hs_kernel_id;
 
 hs_status hs_kernel_timing(hs_ctx* ctx, int32_t enable);

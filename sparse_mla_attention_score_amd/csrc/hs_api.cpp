@@ -134,6 +134,10 @@ hs_status validate(const hs_config* c) {
     return fail(HS_ERR_INVALID_ARG, "num_idx_blocks out of range");
   if (c->num_host_blocks < 0 || c->num_host_blocks * hs::kBlock > INT32_MAX)
     return fail(HS_ERR_INVALID_ARG, "num_host_blocks out of range (host rows are int32)");
+  if (c->hot_leasing != 0 && c->hot_leasing != 1)
+    return fail(HS_ERR_INVALID_ARG, "hot_leasing must be 0 or 1");
+  if (c->hot_leasing && c->num_host_blocks == 0)
+    return fail(HS_ERR_INVALID_ARG, "hot_leasing needs a host pool (num_host_blocks > 0)");
   return HS_OK;
 }
 
@@ -161,6 +165,9 @@ hs_status hs::compute_layout(const hs_config& c, Layout* L) {
   L->off_tok2slot = take(B * L->lmax * 4);
   L->off_req_step = take(B * 4);
   L->off_req_used = take(B * 4);
+  L->off_win_start = take(B * 4);
+  L->off_pool_ring = take((size_t)c.num_gpu_blocks * 4);
+  L->off_pool_ctr = take(2 * 8);
   L->off_err = take(4);
   L->off_scores = take(B * S * L->lmax * 4);
   L->off_hist = take(B * S * kHistBins * 4);
@@ -352,6 +359,9 @@ hs_status hs_bind(hs_ctx* ctx, const hs_buffers* b) {
   ctx->ws.tok2slot = reinterpret_cast<int32_t*>(w + L.off_tok2slot);
   ctx->ws.req_step = reinterpret_cast<int32_t*>(w + L.off_req_step);
   ctx->ws.req_used = reinterpret_cast<int32_t*>(w + L.off_req_used);
+  ctx->ws.win_start = reinterpret_cast<int32_t*>(w + L.off_win_start);
+  ctx->ws.pool_ring = reinterpret_cast<int32_t*>(w + L.off_pool_ring);
+  ctx->ws.pool_ctr = reinterpret_cast<int64_t*>(w + L.off_pool_ctr);
   ctx->ws.err = reinterpret_cast<int32_t*>(w + L.off_err);
   ctx->ws.scores = reinterpret_cast<float*>(w + L.off_scores);
   ctx->ws.hist = reinterpret_cast<uint32_t*>(w + L.off_hist);
@@ -405,8 +415,9 @@ hs_status hisparse_index_topk(hs_ctx* ctx, const void* q_idx, const float* w,
   return e == hipSuccess ? ok() : hip_fail(e, "hisparse_index_topk launch");
 }
 
-hs_status hisparse_resolve(hs_ctx* ctx, const int32_t* topk, const int32_t* ctx_lens, int32_t B,
-                           int32_t S, int32_t* row_ids_out, int32_t* stats_out, void* stream) {
+hs_status hisparse_resolve_plan(hs_ctx* ctx, const int32_t* topk, const int32_t* ctx_lens,
+                                int32_t B, int32_t S, const int32_t* begin_window,
+                                int32_t* row_ids_out, int32_t* stats_out, void* stream) {
   hs_status s = check_step(ctx, B, S, "hisparse_resolve");
   if (s != HS_OK) return s;
   if (B == 0) return ok();
@@ -414,9 +425,58 @@ hs_status hisparse_resolve(hs_ctx* ctx, const int32_t* topk, const int32_t* ctx_
     return fail(HS_ERR_INVALID_ARG, "hisparse_resolve: a pointer argument is NULL");
   if (ctx->cfg.num_host_blocks > 0 && !ctx->host_pool_dev)
     return fail(HS_ERR_STATE, "hisparse_resolve: host pool missing");
-  hipError_t e = hs_launch_resolve(ctx, topk, ctx_lens, B, S, row_ids_out, stats_out,
-                                   static_cast<hipStream_t>(stream));
+  hipError_t e = hs_launch_resolve(ctx, topk, ctx_lens, B, S, begin_window, row_ids_out,
+                                   stats_out, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "hisparse_resolve launch");
+}
+
+hs_status hisparse_resolve(hs_ctx* ctx, const int32_t* topk, const int32_t* ctx_lens, int32_t B,
+                           int32_t S, int32_t* row_ids_out, int32_t* stats_out, void* stream) {
+  return hisparse_resolve_plan(ctx, topk, ctx_lens, B, S, nullptr, row_ids_out, stats_out, stream);
+}
+
+static hs_status check_list(const hs_ctx* ctx, const int32_t* list, int32_t n, const char* what) {
+  if (!ctx) return fail(HS_ERR_INVALID_ARG, "%s: ctx is NULL", what);
+  if (!ctx->bound) return fail(HS_ERR_STATE, "%s: context is not bound", what);
+  if (n < 0) return fail(HS_ERR_INVALID_ARG, "%s: n=%d is negative", what, n);
+  if (n > 0 && !list) return fail(HS_ERR_INVALID_ARG, "%s: list is NULL", what);
+  return HS_OK;
+}
+
+hs_status hs_hot_release(hs_ctx* ctx, const int32_t* reqs, int32_t n, void* stream) {
+  hs_status s = check_list(ctx, reqs, n, "hs_hot_release");
+  if (s != HS_OK || n == 0) return s;
+  hipError_t e = hs_launch_hot_release(ctx, reqs, n, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "hs_hot_release launch");
+}
+
+hs_status hs_hot_pool_give(hs_ctx* ctx, const int32_t* blocks, int32_t n, void* stream) {
+  hs_status s = check_list(ctx, blocks, n, "hs_hot_pool_give");
+  if (s != HS_OK) return s;
+  if (!ctx->cfg.hot_leasing) return fail(HS_ERR_STATE, "hs_hot_pool_give: the context does not lease hot pages");
+  if (n == 0) return ok();
+  hipError_t e = hs_launch_pool_give(ctx, blocks, n, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "hs_hot_pool_give launch");
+}
+
+hs_status hs_hot_pool_read(hs_ctx* ctx, int32_t* out, int32_t cap, int32_t* n) {
+  if (!ctx || !n || cap < 0 || (cap > 0 && !out)) return fail(HS_ERR_INVALID_ARG, "hs_hot_pool_read: bad argument");
+  if (!ctx->bound) return fail(HS_ERR_STATE, "hs_hot_pool_read: context is not bound");
+  if (!ctx->cfg.hot_leasing) return fail(HS_ERR_STATE, "hs_hot_pool_read: the context does not lease hot pages");
+  int64_t ctr[2] = {0, 0};
+  hipError_t e = hipSetDevice(ctx->device);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(ctr, ctx->ws.pool_ctr, sizeof(ctr), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hs_hot_pool_read");
+  const int64_t ring = ctx->cfg.num_gpu_blocks;
+  const int64_t count = ctr[1] - ctr[0];
+  if (count < 0 || count > ring) return fail(HS_ERR_STATE, "hs_hot_pool_read: pool counters corrupt");
+  std::vector<int32_t> all((size_t)ring);
+  e = hipMemcpy(all.data(), ctx->ws.pool_ring, (size_t)ring * 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hs_hot_pool_read");
+  for (int64_t i = 0; i < count && i < cap; ++i) out[i] = all[(size_t)((ctr[0] + i) % ring)];
+  *n = (int32_t)count;
+  return ok();
 }
 
 hs_status sparse_mla_decode(hs_ctx* ctx, int32_t layer, const void* q, const int32_t* row_ids,

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
     const int32_t* __restrict__ ctx_lens, const uint8_t* __restrict__ idx_pool,
     const int32_t* __restrict__ idx_block_table, int max_pages, int64_t num_idx_blocks, int B,
     float* __restrict__ scores, int64_t lmax, uint32_t* __restrict__ hist,
-    const uint32_t* __restrict__ guess, uint32_t* __restrict__ seg_count,
+    const uint32_t* __restrict__ guess, int guess_stride, uint32_t* __restrict__ seg_count,
     uint64_t* __restrict__ cands, int n_seg, int32_t* __restrict__ err) {
   constexpr int kBlkBytes = kFp8 ? kIdxFp8Block : kIdxBf16Block;
   constexpr int kRing = 2;  // tile slots per wave
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
   int cq[S];
 #pragma unroll
   for (int j = 0; j < S; ++j) {
-    gq[j] = guess[b * S + j];
+    gq[j] = guess[b * guess_stride + j];
     cq[j] = 0;
   }
   __syncthreads();
@@ -398,7 +398,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const int32_t* __restrict__ ctx_lens, int B, int S, int K, int max_ctx,
     const float* __restrict__ scores, int64_t lmax, uint32_t* __restrict__ hist,
     uint32_t* __restrict__ bitmap, int64_t bm_words, int32_t* __restrict__ topk_out,
-    int cand_cap, uint32_t* __restrict__ guess, const uint32_t* __restrict__ seg_count,
+    int cand_cap, uint32_t* __restrict__ guess_all, int guess_stride,
+    const uint32_t* __restrict__ seg_count,
     const uint64_t* __restrict__ cands, int n_seg_max, unsigned long long* __restrict__ path_count,
     int32_t* __restrict__ err) {
   extern __shared__ __align__(16) unsigned char dyn[];
@@ -411,18 +412,20 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   const int Lb = ctx_lens[b];
   int32_t* out = topk_out + (int64_t)bj * K;
   uint32_t* gh = hist + (int64_t)bj * kHistBins;
-  const uint32_t g_used = guess[bj];  // the guess the sweep listed candidates from
+  // the request slot's guesses persist across calls, laid out [max_batch][max_queries]
+  uint32_t* guess = guess_all + b * guess_stride + j;
+  const uint32_t g_used = *guess;  // the guess the sweep listed candidates from
   if (Lb < S || Lb > max_ctx) {
     for (int i = tid; i < kHistBins; i += kSelThreads) gh[i] = 0;
     for (int i = tid; i < K; i += kSelThreads) out[i] = -1;
-    if (tid == 0) guess[bj] = kGuessOff;
+    if (tid == 0) *guess = kGuessOff;
     return;
   }
   const int Lj = Lb - S + 1 + j;
   if (Lj <= K) {  // everything is selected; keep the histogram zero for the next call
     for (int i = tid; i < kHistBins; i += kSelThreads) gh[i] = 0;
     for (int i = tid; i < K; i += kSelThreads) out[i] = i < Lj ? i : -1;
-    if (tid == 0) guess[bj] = kGuessOff;
+    if (tid == 0) *guess = kGuessOff;
     return;
   }
 
@@ -456,7 +459,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   const int n2 = min(8 * K, n_slots / 4);
   int above, beta, gbin;
   find_threshold_bins2(sh, kHistBins, K, n2 > K ? n2 : 8 * K, &beta, &above, &gbin);
-  if (tid == 0) guess[bj] = n2 > K && gbin > 0 ? (uint32_t)gbin << kHistShift : kGuessOff;
+  if (tid == 0) *guess = n2 > K && gbin > 0 ? (uint32_t)gbin << kHistShift : kGuessOff;
   const int cnt_beta = beta >= 0 ? (int)sh.hist[beta] : 0;
   const int need = K - above;  // tokens to take from bin beta
   const float* sc = scores + (int64_t)bj * lmax;
@@ -850,7 +853,7 @@ hipError_t launch_scores(const hs_ctx* ctx, const void* q_idx, const float* w,
                      static_cast<const uint16_t*>(q_idx), w, ctx_lens,
                      static_cast<const uint8_t*>(ctx->buf.idx_pool), ctx->buf.idx_block_table,
                      c.max_pages_per_req, (int64_t)c.num_idx_blocks, B, ctx->ws.scores,
-                     ctx->lay.lmax, ctx->ws.hist, ctx->ws.guess, ctx->ws.seg_count, ctx->ws.cands,
+                     ctx->lay.lmax, ctx->ws.hist, ctx->ws.guess, c.max_queries, ctx->ws.seg_count, ctx->ws.cands,
                      ctx->lay.n_seg, ctx->ws.err);
   hs_timer_mark(ctx, HS_KERNEL_INDEX_SCORE, false, stream);
   return hipGetLastError();
@@ -905,13 +908,13 @@ hipError_t hs_launch_index_topk(const hs_ctx* ctx, const void* q_idx, const floa
     hipLaunchKernelGGL(topk_select_kernel<true>, dim3((unsigned)(B * S)), dim3(kSelThreads), dyn, stream,
                        ctx_lens, B, S, ctx->cfg.topk, ctx->cfg.max_pages_per_req * kBlock,
                        ctx->ws.scores, ctx->lay.lmax, ctx->ws.hist, ctx->ws.bitmap,
-                       (int64_t)ctx->lay.bm_words, topk_out, cap, ctx->ws.guess, ctx->ws.seg_count,
+                       (int64_t)ctx->lay.bm_words, topk_out, cap, ctx->ws.guess, ctx->cfg.max_queries, ctx->ws.seg_count,
                        ctx->ws.cands, ctx->lay.n_seg, ctx->ws.path_count, ctx->ws.err);
   else
     hipLaunchKernelGGL(topk_select_kernel<false>, dim3((unsigned)(B * S)), dim3(kSelThreads), dyn, stream,
                        ctx_lens, B, S, ctx->cfg.topk, ctx->cfg.max_pages_per_req * kBlock,
                        ctx->ws.scores, ctx->lay.lmax, ctx->ws.hist, ctx->ws.bitmap,
-                       (int64_t)ctx->lay.bm_words, topk_out, cap, ctx->ws.guess, ctx->ws.seg_count,
+                       (int64_t)ctx->lay.bm_words, topk_out, cap, ctx->ws.guess, ctx->cfg.max_queries, ctx->ws.seg_count,
                        ctx->ws.cands, ctx->lay.n_seg, ctx->ws.path_count, ctx->ws.err);
   hs_timer_mark(ctx, HS_KERNEL_TOPK_SELECT, false, stream);
   return hipGetLastError();

@@ -51,6 +51,9 @@ struct Workspace {
   int32_t* tok2slot;     // [Bmax][Lmax]       hot slot of each token, -1 absent
   int32_t* req_step;     // [Bmax]             resolve calls made per request
   int32_t* req_used;     // [Bmax]             hot slots ever filled per request
+  int32_t* win_start;    // [Bmax]             call counter at which the current plan window began
+  int32_t* pool_ring;    // [num_gpu_blocks]   free-block pool (hot_leasing), a ring
+  int64_t* pool_ctr;     // [2]                pool front and back, monotonic (entry = ring[x % cap])
   int32_t* err;          // [1]                sticky device error word (HS_DEVERR_*)
   float* scores;         // [Bmax][Smax][Lmax] indexer scores of one call
   uint32_t* hist;        // [Bmax][Smax][kHistBins] first-digit histogram (kept zero between calls)
@@ -69,7 +72,7 @@ struct Workspace {
 
 struct Layout {
   size_t off_slot_token, off_slot_stamp, off_lru_order, off_tok2slot, off_req_step, off_req_used,
-      off_err, off_scores, off_hist, off_bitmap, off_miss_src, off_miss_dst, off_miss_cnt,
+      off_win_start, off_pool_ring, off_pool_ctr, off_err, off_scores, off_hist, off_bitmap, off_miss_src, off_miss_dst, off_miss_cnt,
       off_part_o, off_part_ml, off_guess, off_seg_count, off_cands, off_path_count, off_zero_row,
       total;
   int32_t hot_rows;
@@ -112,7 +115,10 @@ hipError_t hs_launch_index_topk(const hs_ctx* ctx, const void* q_idx, const floa
                                 const int32_t* ctx_lens, int B, int S, int32_t* topk_out,
                                 hipStream_t stream);
 hipError_t hs_launch_resolve(const hs_ctx* ctx, const int32_t* topk, const int32_t* ctx_lens, int B,
-                             int S, int32_t* row_ids, int32_t* stats, hipStream_t stream);
+                             int S, const int32_t* begin_window, int32_t* row_ids, int32_t* stats,
+                             hipStream_t stream);
+hipError_t hs_launch_hot_release(const hs_ctx* ctx, const int32_t* reqs, int n, hipStream_t stream);
+hipError_t hs_launch_pool_give(const hs_ctx* ctx, const int32_t* blocks, int n, hipStream_t stream);
 hipError_t hs_launch_decode(const hs_ctx* ctx, int layer, const void* q, const int32_t* row_ids,
                             const int32_t* ctx_lens, int B, int S, float sm_scale, void* out,
                             float* lse, int splits, hipStream_t stream);

@@ -61,7 +61,8 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     int32_t* __restrict__ req_used, int32_t* __restrict__ miss_src, int32_t* __restrict__ miss_dst,
     int32_t* __restrict__ miss_cnt, int union_cap, int32_t* __restrict__ row_ids,
     int32_t* __restrict__ stats, uint32_t* __restrict__ ubits, int64_t ubits_stride,
-    int tables_off, int32_t* __restrict__ err) {
+    int tables_off, const int32_t* __restrict__ begin_window, int32_t* __restrict__ win_start,
+    int leasing, int32_t* __restrict__ err) {
   extern __shared__ __align__(16) unsigned char dyn[];
   // union_cap (a power of two, >= S*K and >= 1024) entries each: sorted union U, per-entry
   // class `cls` (row id, -1, or -2 - miss rank), the token of each miss (then its host row),
@@ -80,6 +81,11 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
   const int tid = threadIdx.x;
   const int Lb = ctx_lens[b];
   const int step = req_step[b];
+  // Plan window: slots touched by a call of the current window (stamp >= protect) are never
+  // given to a miss.  A call that begins a window protects only its own hits.
+  const bool begin = begin_window == nullptr || begin_window[b] != 0;
+  const int protect = begin ? step : min(win_start[b], step);
+  const bool windowed = protect < step;
   const int32_t* tk = topk + (int64_t)b * S * K;
   int32_t* out = row_ids + (int64_t)b * S * K;
   const int32_t* bt = block_table + (int64_t)b * max_pages;
@@ -106,11 +112,14 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
   const int n_in = S * K;
   const int perH = (H + kResThreads - 1) / kResThreads;  // <= kPerH
   const int h0 = tid * perH;
-  int32_t tkv[kPerU], ord[kPerH];
+  int32_t tkv[kPerU], ord[kPerH], ost[kPerH];
 #pragma unroll
   for (int e = 0; e < kPerU; ++e) tkv[e] = tid + e * kResThreads < n_in ? tk[tid + e * kResThreads] : -1;
 #pragma unroll
   for (int e = 0; e < kPerH; ++e) ord[e] = e < perH && h0 + e < H ? order_cur[h0 + e] : -1;
+  // inside a window, the stamps of the listed slots (before this call) decide which are free
+#pragma unroll
+  for (int e = 0; e < kPerH; ++e) ost[e] = windowed && ord[e] >= 0 && ord[e] < H ? st_stamp[ord[e]] : -1;
   for (int i = tid; i < H / kBlock; i += kResThreads) lhot[i] = hot[i];
   // The page tables are read per union entry (up to 8 per thread, at random pages): from LDS
   // when they fit, staged here with coalesced loads.
@@ -270,19 +279,23 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     n_miss = tot;
   }
 
-  // ---- 3. victims: the first n_miss untouched slots of the recency list, then the new list
-  // (untouched slots in old order, then every touched slot in ascending slot order)
+  // ---- 3. victims: the first n_miss slots of the recency list untouched in this call (and,
+  // inside a window, in the window's earlier calls), then the new list (untouched slots in old
+  // order, then every slot touched by this call in ascending slot order)
   int n_assign;
   {
+    auto free_slot = [&](int e) {
+      return ord[e] >= 0 && ord[e] < H && !flag[ord[e]] && (!windowed || ost[e] < protect);
+    };
     int my_cand = 0;
 #pragma unroll
     for (int e = 0; e < kPerH; ++e)
-      if (ord[e] >= 0 && ord[e] < H && !flag[ord[e]]) ++my_cand;
+      if (free_slot(e)) ++my_cand;
     int tot;
     int r = block_exclusive_scan<kResThreads>(my_cand, scan, &tot);
 #pragma unroll
     for (int e = 0; e < kPerH; ++e) {
-      if (ord[e] >= 0 && ord[e] < H && !flag[ord[e]]) {
+      if (free_slot(e)) {
         if (r < n_miss) mdst[r] = ord[e];
         ++r;
       }
@@ -332,6 +345,7 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     const int32_t h = lhot[v >> 6];
     int32_t row = -1;
     if (h >= 0 && h < num_gpu_blocks) row = h * kBlock + (v & 63);
+    else if (leasing && h < 0) row = -2 - v;  // the page leases its block after this kernel
     else raise_error(err, HS_DEVERR_BAD_BLOCK);
     mdst[r] = row;
     miss_src[(int64_t)b * n_in + r] = hbk * kBlock + (u & 63);
@@ -377,6 +391,7 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     const int used = min(H, req_used[b] + cnt[2]);
     req_used[b] = used;
     req_step[b] = step + 1;
+    if (begin) win_start[b] = step;
     if (stats) {
       stats[b * 4 + 0] = cnt[0];
       stats[b * 4 + 1] = cnt[1];
@@ -386,9 +401,50 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
   }
 }
 
+// Leases of one resolve call (hot_leasing): every hot page below a request's filled slots that
+// has no block yet takes the next block of the free-block pool, request by request, page by
+// page (a scan over the flattened (request, page) order keeps that order with any number of
+// threads).  An empty pool leaves the page at -1 and flags the call.
+constexpr int kLeaseThreads = 1024;
+
+__global__ __launch_bounds__(kLeaseThreads) void lease_kernel(
+    int B, int pages_per_req, const int32_t* __restrict__ req_used, int32_t* __restrict__ hot_blocks,
+    const int32_t* __restrict__ ring, int64_t* __restrict__ ctr, int64_t cap, int64_t num_gpu_blocks,
+    int32_t* __restrict__ err) {
+  __shared__ int scan[kLeaseThreads / 64 + 1];
+  const int64_t head = ctr[0], avail = ctr[1] - ctr[0];
+  const int total = B * pages_per_req;
+  int64_t carry = 0;
+  for (int base = 0; base < total; base += kLeaseThreads) {
+    const int f = base + (int)threadIdx.x;
+    int need = 0;
+    if (f < total) {
+      const int b = f / pages_per_req, p = f - b * pages_per_req;
+      const int used = min(max(req_used[b], 0), pages_per_req * kBlock);
+      need = p < (used + kBlock - 1) / kBlock && hot_blocks[f] < 0;
+    }
+    int tot;
+    const int x = block_exclusive_scan<kLeaseThreads>(need, scan, &tot);
+    if (need) {
+      const int64_t pos = carry + x;
+      if (pos < avail) {
+        const int32_t blk = ring[(head + pos) % cap];
+        if (blk >= 0 && blk < num_gpu_blocks) hot_blocks[f] = blk;
+        else raise_error(err, HS_DEVERR_BAD_BLOCK);
+      } else {
+        raise_error(err, HS_DEVERR_POOL_EMPTY);
+      }
+    }
+    carry += tot;
+  }
+  if (threadIdx.x == 0) ctr[0] = head + (carry < avail ? carry : avail);
+}
+
 // Single-row copies of every miss of the batch, spread over the whole grid: host row
 // miss_src -> device row miss_dst, for every layer, 16 bytes per work item, eight loads in
-// flight per thread.  Rows whose destination is invalid (-1) are skipped.
+// flight per thread.  Rows whose destination is invalid (-1) are skipped.  With leasing, a
+// destination on a page leased after the resolver ran is given as -2 - slot and is looked up
+// in the hot-page table here, and the row ids the resolver left in that form are rewritten.
 constexpr int kCopyThreads = 256;
 constexpr int kCopyBlocks = 256;
 
@@ -396,7 +452,8 @@ __global__ __launch_bounds__(kCopyThreads) void miss_copy_kernel(
     const int32_t* __restrict__ miss_src, const int32_t* __restrict__ miss_dst,
     const int32_t* __restrict__ miss_cnt, int B, int per_req, const uint8_t* __restrict__ host_pool,
     uint8_t* __restrict__ kv_pool, int n_layers, int row_bytes, int64_t num_gpu_blocks,
-    int64_t num_host_blocks) {
+    int64_t num_host_blocks, const int32_t* __restrict__ hot_blocks, int pages_per_req,
+    int32_t* __restrict__ row_ids, int64_t n_row_ids, int row_ids_per_req) {
   __shared__ int scan[kCopyThreads / 64 + 1];
   // prefix sums of the per-request miss counts (B may exceed the block: chunks with carry)
   extern __shared__ int req_start[];  // [B + 1]
@@ -437,7 +494,13 @@ __global__ __launch_bounds__(kCopyThreads) void miss_copy_kernel(
           else hi = mid - 1;
         }
         const int64_t k = (int64_t)lo * per_req + (row - req_start[lo]);
-        const int32_t s = miss_src[k], d = miss_dst[k];
+        const int32_t s = miss_src[k];
+        int32_t d = miss_dst[k];
+        if (hot_blocks && d <= -2) {
+          const int v = -2 - d;
+          const int32_t blk = hot_blocks[(int64_t)lo * pages_per_req + (v >> 6)];
+          d = blk >= 0 ? blk * kBlock + (v & 63) : -1;
+        }
         if (d >= 0 && d < num_gpu_blocks * kBlock && s >= 0 && s < num_host_blocks * kBlock) {
           v[e] = __builtin_nontemporal_load(
               reinterpret_cast<const u32x4*>(host_pool + layer * host_layer + (int64_t)s * row_bytes + q * 16));
@@ -449,13 +512,99 @@ __global__ __launch_bounds__(kCopyThreads) void miss_copy_kernel(
     for (int e = 0; e < kBatch; ++e)
       if (dst[e] >= 0) *reinterpret_cast<u32x4*>(kv_pool + dst[e]) = v[e];
   }
+  if (hot_blocks) {
+    for (int64_t i = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x; i < n_row_ids; i += stride) {
+      const int32_t r = row_ids[i];
+      if (r > -2) continue;
+      const int v = -2 - r;
+      const int32_t blk = hot_blocks[(i / row_ids_per_req) * pages_per_req + (v >> 6)];
+      row_ids[i] = blk >= 0 ? blk * kBlock + (v & 63) : -1;
+    }
+  }
+}
+
+// Requests' hot buffers made cold (hs_hot_release): one workgroup per listed request clears its
+// slots, recency lists, token-to-slot entries (through the tokens its slots hold), counters and
+// top-K guesses.  A request listed twice is cleared twice, to the same state.
+__global__ __launch_bounds__(256) void hot_release_kernel(
+    const int32_t* __restrict__ reqs, int max_batch, int H, int max_queries,
+    int32_t* __restrict__ slot_token, int32_t* __restrict__ slot_stamp,
+    int32_t* __restrict__ lru_order, int32_t* __restrict__ tok2slot, int64_t lmax,
+    int32_t* __restrict__ req_step, int32_t* __restrict__ req_used, int32_t* __restrict__ win_start,
+    uint32_t* __restrict__ guess, int32_t* __restrict__ err) {
+  const int b = reqs[blockIdx.x];
+  if (b < 0 || b >= max_batch) {
+    if (threadIdx.x == 0) raise_error(err, HS_DEVERR_BAD_REQUEST);
+    return;
+  }
+  int32_t* st_tok = slot_token + (int64_t)b * H;
+  int32_t* t2s = tok2slot + (int64_t)b * lmax;
+  for (int s = threadIdx.x; s < H; s += blockDim.x) {
+    const int32_t u = st_tok[s];
+    if (u >= 0 && u < lmax) t2s[u] = -1;
+    st_tok[s] = -1;
+    slot_stamp[(int64_t)b * H + s] = -1;
+    lru_order[(int64_t)b * H + s] = s;
+    lru_order[((int64_t)max_batch + b) * H + s] = s;
+  }
+  if (threadIdx.x == 0) {
+    req_step[b] = 0;
+    req_used[b] = 0;
+    win_start[b] = 0;
+  }
+  if (threadIdx.x < max_queries) guess[b * max_queries + threadIdx.x] = kGuessOff;
+}
+
+// The free-block pool's sequential updates, one wave: blocks of released requests (page order,
+// list order) or given blocks appended at the back.  A released request's pages are cleared
+// as they are returned, so a request listed twice returns its blocks once.
+__global__ __launch_bounds__(64) void pool_append_kernel(
+    const int32_t* __restrict__ list, int n, int from_requests, int max_batch, int pages_per_req,
+    int32_t* __restrict__ hot_blocks, int32_t* __restrict__ ring, int64_t* __restrict__ ctr,
+    int64_t cap, int64_t num_gpu_blocks, int32_t* __restrict__ err) {
+  const int lane = threadIdx.x;
+  const int64_t head = ctr[0];
+  int64_t tail = ctr[1];
+  auto push = [&](int32_t blk, bool ok) {
+    const uint64_t m = __ballot(ok);
+    const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    const int64_t room = cap - (tail - head);
+    if (ok) {
+      if (pos < room) ring[(tail + pos) % cap] = blk;
+      else raise_error(err, HS_DEVERR_POOL_FULL);
+    }
+    const int64_t cnt = __popcll(m);
+    tail += cnt < room ? cnt : room;
+  };
+  if (from_requests) {
+    for (int i = 0; i < n; ++i) {
+      const int b = list[i];
+      if (b < 0 || b >= max_batch) continue;  // flagged by hot_release_kernel
+      for (int p0 = 0; p0 < pages_per_req; p0 += 64) {
+        const int p = p0 + lane;
+        int32_t* e = hot_blocks + (int64_t)b * pages_per_req + p;
+        const int32_t blk = p < pages_per_req ? *e : -1;
+        push(blk, blk >= 0);
+        if (blk >= 0) *e = -1;
+      }
+    }
+  } else {
+    for (int i0 = 0; i0 < n; i0 += 64) {
+      const int32_t blk = i0 + lane < n ? list[i0 + lane] : -1;
+      if (blk >= num_gpu_blocks) raise_error(err, HS_DEVERR_BAD_BLOCK);
+      push(blk, blk >= 0 && blk < num_gpu_blocks);
+    }
+  }
+  if (lane == 0) ctr[1] = tail;
 }
 
 __global__ void hot_reset_kernel(int32_t* slot_token, int32_t* slot_stamp, int32_t* lru_order,
                                  int64_t n_slots, int H, int32_t* tok2slot, int64_t n_tok,
-                                 int32_t* req_step, int32_t* req_used, int max_batch,
-                                 uint32_t* hist, int64_t n_hist, uint32_t* guess, int n_guess,
-                                 unsigned long long* path_count, int64_t n_all, int32_t* err) {
+                                 int32_t* req_step, int32_t* req_used, int32_t* win_start,
+                                 int max_batch, uint32_t* hist, int64_t n_hist, uint32_t* guess,
+                                 int n_guess, unsigned long long* path_count, int32_t* hot_blocks,
+                                 int64_t n_hot_blocks, int64_t* pool_ctr, int64_t n_all,
+                                 int32_t* err) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_all; i += stride) {
     if (i < n_tok) tok2slot[i] = -1;
@@ -471,7 +620,10 @@ __global__ void hot_reset_kernel(int32_t* slot_token, int32_t* slot_stamp, int32
     if (i < max_batch) {
       req_step[i] = 0;
       req_used[i] = 0;
+      win_start[i] = 0;
     }
+    if (i < n_hot_blocks) hot_blocks[i] = -1;  // only with leasing (n_hot_blocks = 0 otherwise)
+    if (pool_ctr && i < 2) pool_ctr[i] = 0;
     if (i == 0) *err = 0;
   }
 }
@@ -500,7 +652,8 @@ static size_t resolve_lds_with_tables(int S, int K, int H, int max_pages) {
 }
 
 hipError_t hs_launch_resolve(const hs_ctx* ctx, const int32_t* topk, const int32_t* ctx_lens, int B,
-                             int S, int32_t* row_ids, int32_t* stats, hipStream_t stream) {
+                             int S, const int32_t* begin_window, int32_t* row_ids, int32_t* stats,
+                             hipStream_t stream) {
   const hs_config& c = ctx->cfg;
   const int H = ctx->lay.hot_rows;
   const int cap = union_cap_for(S, c.topk);
@@ -515,17 +668,62 @@ hipError_t hs_launch_resolve(const hs_ctx* ctx, const int32_t* topk, const int32
                      ctx->ws.slot_stamp, ctx->ws.lru_order, ctx->ws.tok2slot, ctx->lay.lmax,
                      ctx->ws.req_step, ctx->ws.req_used, ctx->ws.miss_src, ctx->ws.miss_dst,
                      ctx->ws.miss_cnt, cap, row_ids, stats, ctx->ws.bitmap,
-                     (int64_t)c.max_queries * ctx->lay.bm_words, tables_off, ctx->ws.err);
+                     (int64_t)c.max_queries * ctx->lay.bm_words, tables_off, begin_window,
+                     ctx->ws.win_start, c.hot_leasing, ctx->ws.err);
   hs_timer_mark(ctx, HS_KERNEL_RESOLVE, false, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || c.num_host_blocks == 0) return e;
+  const int pages_per_req = H / kBlock;
+  if (c.hot_leasing) {
+    hs_timer_mark(ctx, HS_KERNEL_LEASE, true, stream);
+    hipLaunchKernelGGL(lease_kernel, dim3(1), dim3(kLeaseThreads), 0, stream, B, pages_per_req,
+                       ctx->ws.req_used, ctx->buf.hot_blocks, ctx->ws.pool_ring, ctx->ws.pool_ctr,
+                       (int64_t)c.num_gpu_blocks, (int64_t)c.num_gpu_blocks, ctx->ws.err);
+    hs_timer_mark(ctx, HS_KERNEL_LEASE, false, stream);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hs_timer_mark(ctx, HS_KERNEL_MISS_COPY, true, stream);
   hipLaunchKernelGGL(miss_copy_kernel, dim3(kCopyBlocks), dim3(kCopyThreads), (size_t)(B + 1) * 4,
                      stream, ctx->ws.miss_src, ctx->ws.miss_dst, ctx->ws.miss_cnt, B, S * c.topk,
                      static_cast<const uint8_t*>(ctx->host_pool_dev),
                      static_cast<uint8_t*>(ctx->buf.kv_pool), c.n_layers, ctx->row_bytes,
-                     (int64_t)c.num_gpu_blocks, (int64_t)c.num_host_blocks);
+                     (int64_t)c.num_gpu_blocks, (int64_t)c.num_host_blocks,
+                     c.hot_leasing ? ctx->buf.hot_blocks : nullptr, pages_per_req, row_ids,
+                     (int64_t)B * S * c.topk, S * c.topk);
   hs_timer_mark(ctx, HS_KERNEL_MISS_COPY, false, stream);
+  return hipGetLastError();
+}
+
+hipError_t hs_launch_hot_release(const hs_ctx* ctx, const int32_t* reqs, int n, hipStream_t stream) {
+  const hs_config& c = ctx->cfg;
+  const int H = ctx->lay.hot_rows;
+  if (c.hot_leasing) {
+    hs_timer_mark(ctx, HS_KERNEL_POOL_GIVE, true, stream);
+    hipLaunchKernelGGL(pool_append_kernel, dim3(1), dim3(64), 0, stream, reqs, n, 1, c.max_batch,
+                       H / kBlock, ctx->buf.hot_blocks, ctx->ws.pool_ring, ctx->ws.pool_ctr,
+                       (int64_t)c.num_gpu_blocks, (int64_t)c.num_gpu_blocks, ctx->ws.err);
+    hs_timer_mark(ctx, HS_KERNEL_POOL_GIVE, false, stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hs_timer_mark(ctx, HS_KERNEL_HOT_RELEASE, true, stream);
+  hipLaunchKernelGGL(hot_release_kernel, dim3((unsigned)n), dim3(256), 0, stream, reqs, c.max_batch,
+                     H, c.max_queries, ctx->ws.slot_token, ctx->ws.slot_stamp, ctx->ws.lru_order,
+                     ctx->ws.tok2slot, ctx->lay.lmax, ctx->ws.req_step, ctx->ws.req_used,
+                     ctx->ws.win_start, ctx->ws.guess, ctx->ws.err);
+  hs_timer_mark(ctx, HS_KERNEL_HOT_RELEASE, false, stream);
+  return hipGetLastError();
+}
+
+hipError_t hs_launch_pool_give(const hs_ctx* ctx, const int32_t* blocks, int n, hipStream_t stream) {
+  const hs_config& c = ctx->cfg;
+  hs_timer_mark(ctx, HS_KERNEL_POOL_GIVE, true, stream);
+  hipLaunchKernelGGL(pool_append_kernel, dim3(1), dim3(64), 0, stream, blocks, n, 0, c.max_batch,
+                     ctx->lay.hot_rows / kBlock, ctx->buf.hot_blocks, ctx->ws.pool_ring,
+                     ctx->ws.pool_ctr, (int64_t)c.num_gpu_blocks, (int64_t)c.num_gpu_blocks,
+                     ctx->ws.err);
+  hs_timer_mark(ctx, HS_KERNEL_POOL_GIVE, false, stream);
   return hipGetLastError();
 }
 
@@ -534,17 +732,20 @@ hipError_t hs_launch_hot_reset(const hs_ctx* ctx, hipStream_t stream) {
   const int64_t n_slots = (int64_t)c.max_batch * ctx->lay.hot_rows;
   const int64_t n_tok = (int64_t)c.max_batch * ctx->lay.lmax;
   const int64_t n_hist = (int64_t)c.max_batch * c.max_queries * kHistBins;
+  const int64_t n_hot_blocks = c.hot_leasing ? (int64_t)c.max_batch * (ctx->lay.hot_rows / kBlock) : 0;
   int64_t n = n_tok;
   if (n_slots > n) n = n_slots;
   if (n_hist > n) n = n_hist;
+  if (n_hot_blocks > n) n = n_hot_blocks;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   hs_timer_mark(ctx, HS_KERNEL_HOT_RESET, true, stream);
   hipLaunchKernelGGL(hot_reset_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      ctx->ws.slot_token, ctx->ws.slot_stamp, ctx->ws.lru_order, n_slots,
                      ctx->lay.hot_rows, ctx->ws.tok2slot, n_tok, ctx->ws.req_step, ctx->ws.req_used,
-                     c.max_batch, ctx->ws.hist, n_hist, ctx->ws.guess, c.max_batch * c.max_queries,
-                     ctx->ws.path_count, n, ctx->ws.err);
+                     ctx->ws.win_start, c.max_batch, ctx->ws.hist, n_hist, ctx->ws.guess,
+                     c.max_batch * c.max_queries, ctx->ws.path_count, ctx->buf.hot_blocks,
+                     n_hot_blocks, c.hot_leasing ? ctx->ws.pool_ctr : nullptr, n, ctx->ws.err);
   hs_timer_mark(ctx, HS_KERNEL_HOT_RESET, false, stream);
   return hipGetLastError();
 }

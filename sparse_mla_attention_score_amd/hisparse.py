@@ -23,17 +23,21 @@ HS_DEVERR_SHORT_CONTEXT = 0x8
 HS_DEVERR_TOPK_COUNT = 0x10
 HS_DEVERR_HOT_FULL = 0x20
 HS_DEVERR_TAIL_PAGE = 0x40
+HS_DEVERR_POOL_EMPTY = 0x80
+HS_DEVERR_POOL_FULL = 0x100
+HS_DEVERR_BAD_REQUEST = 0x200
 
 # hs_kernel_id
 KERNEL_NAMES = ["index_score", "topk_select", "resolve", "miss_copy", "decode", "decode_merge",
-                "hot_reset", "materialize", "release"]
+                "hot_reset", "materialize", "release", "lease", "hot_release", "pool_give"]
 HS_KERNEL_COUNT = len(KERNEL_NAMES)
 
 EXPORTED = ["hs_create", "hs_destroy", "hs_workspace_bytes", "hs_host_pool_bytes",
             "hs_host_pool_alloc", "hs_bind", "hs_hot_reset", "hisparse_index_topk",
             "hisparse_resolve", "sparse_mla_decode", "hs_read_device_error", "hs_decode_splits",
             "hs_hot_state", "hs_kernel_timing", "hs_kernel_times", "hs_select_paths",
-            "hisparse_materialize_pages", "hisparse_release_pages", "hs_status_string",
+            "hisparse_materialize_pages", "hisparse_release_pages", "hisparse_resolve_plan",
+            "hs_hot_release", "hs_hot_pool_give", "hs_hot_pool_read", "hs_status_string",
             "hs_last_error"]
 
 
@@ -45,7 +49,7 @@ class hs_config(ctypes.Structure):
                 ("n_layers", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("max_queries", ctypes.c_int32), ("max_pages_per_req", ctypes.c_int32),
                 ("hot_rows_per_req", ctypes.c_int32), ("topk_lds_candidates", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("num_gpu_blocks", ctypes.c_int64),
+                ("hot_leasing", ctypes.c_int32), ("num_gpu_blocks", ctypes.c_int64),
                 ("num_idx_blocks", ctypes.c_int64), ("num_host_blocks", ctypes.c_int64)]
 
 
@@ -90,6 +94,10 @@ def lib() -> ctypes.CDLL:
             "hs_hot_reset": [P, P],
             "hisparse_index_topk": [P, P, P, P, i32, i32, P, P],
             "hisparse_resolve": [P, P, P, i32, i32, P, P, P],
+            "hisparse_resolve_plan": [P, P, P, i32, i32, P, P, P, P],
+            "hs_hot_release": [P, P, i32, P],
+            "hs_hot_pool_give": [P, P, i32, P],
+            "hs_hot_pool_read": [P, ctypes.POINTER(i32), i32, ctypes.POINTER(i32)],
             "sparse_mla_decode": [P, i32, P, P, P, i32, i32, f32, P, P, P],
             "hs_read_device_error": [P, ctypes.POINTER(i32)],
             "hs_decode_splits": [P, i32, i32, ctypes.POINTER(i32)],
@@ -176,6 +184,28 @@ def hisparse_resolve(ctx: int, topk: int, ctx_lens: int, B: int, S: int, row_ids
            "hisparse_resolve")
 
 
+def hisparse_resolve_plan(ctx: int, topk: int, ctx_lens: int, B: int, S: int, begin_window: int,
+                          row_ids_out: int, stats_out: int, stream: int) -> None:
+    _check(lib().hisparse_resolve_plan(ctx, topk, ctx_lens, B, S, begin_window or None, row_ids_out,
+                                       stats_out or None, stream), "hisparse_resolve_plan")
+
+
+def hs_hot_release(ctx: int, reqs: int, n: int, stream: int) -> None:
+    _check(lib().hs_hot_release(ctx, reqs, n, stream), "hs_hot_release")
+
+
+def hs_hot_pool_give(ctx: int, blocks: int, n: int, stream: int) -> None:
+    _check(lib().hs_hot_pool_give(ctx, blocks, n, stream), "hs_hot_pool_give")
+
+
+def hs_hot_pool_read(ctx: int, cap: int) -> list:
+    """The free-block pool, front first (synchronises)."""
+    buf = (ctypes.c_int32 * max(cap, 1))()
+    n = ctypes.c_int32()
+    _check(lib().hs_hot_pool_read(ctx, buf, cap, ctypes.byref(n)), "hs_hot_pool_read")
+    return [buf[i] for i in range(min(n.value, cap))]
+
+
 def sparse_mla_decode(ctx: int, layer: int, q: int, row_ids: int, ctx_lens: int, B: int, S: int,
                       sm_scale: float, out: int, lse: int, stream: int) -> None:
     _check(lib().sparse_mla_decode(ctx, layer, q, row_ids, ctx_lens, B, S, sm_scale, out,
@@ -230,10 +260,10 @@ def hs_kernel_times(ctx: int) -> dict:
 def make_config(*, topk: int = 2048, kv_dtype: int = HS_FP8_E4M3, idx_dtype: int = HS_FP8_E4M3,
                 n_layers: int = 1, max_batch: int, max_queries: int, max_pages_per_req: int,
                 hot_rows_per_req: int = 0, num_gpu_blocks: int, num_idx_blocks: int,
-                num_host_blocks: int, topk_lds_candidates: int = 0) -> hs_config:
+                num_host_blocks: int, topk_lds_candidates: int = 0, hot_leasing: int = 0) -> hs_config:
     return hs_config(64, topk, 32, 128, 64, 576, 512, kv_dtype, idx_dtype, n_layers, max_batch,
-                     max_queries, max_pages_per_req, hot_rows_per_req, topk_lds_candidates, 0,
-                     num_gpu_blocks, num_idx_blocks, num_host_blocks)
+                     max_queries, max_pages_per_req, hot_rows_per_req, topk_lds_candidates,
+                     hot_leasing, num_gpu_blocks, num_idx_blocks, num_host_blocks)
 
 
 # ---------------------------------------------------------------- torch plumbing
@@ -295,11 +325,27 @@ class Context:
         hisparse_index_topk(self.ctx, q_idx.data_ptr(), w.data_ptr(), ctx_lens.data_ptr(), B, S,
                             topk_out.data_ptr(), self.stream())
 
-    def resolve(self, topk, ctx_lens, row_ids_out, stats_out=None) -> None:
+    def resolve(self, topk, ctx_lens, row_ids_out, stats_out=None, begin_window=None) -> None:
+        """begin_window: None (every call begins a plan window) or a device int32 [B]."""
         B, S = topk.shape[0], topk.shape[1]
-        hisparse_resolve(self.ctx, topk.data_ptr(), ctx_lens.data_ptr(), B, S,
-                         row_ids_out.data_ptr(), stats_out.data_ptr() if stats_out is not None else 0,
-                         self.stream())
+        st = stats_out.data_ptr() if stats_out is not None else 0
+        if begin_window is None:
+            hisparse_resolve(self.ctx, topk.data_ptr(), ctx_lens.data_ptr(), B, S,
+                             row_ids_out.data_ptr(), st, self.stream())
+        else:
+            hisparse_resolve_plan(self.ctx, topk.data_ptr(), ctx_lens.data_ptr(), B, S,
+                                  begin_window.data_ptr(), row_ids_out.data_ptr(), st, self.stream())
+
+    def hot_release(self, reqs) -> None:
+        """reqs: device int32 [n] of request slots whose hot buffers become cold."""
+        hs_hot_release(self.ctx, reqs.data_ptr(), reqs.shape[0], self.stream())
+
+    def pool_give(self, blocks) -> None:
+        """blocks: device int32 [n] appended to the free-block pool (entries < 0 skipped)."""
+        hs_hot_pool_give(self.ctx, blocks.data_ptr(), blocks.shape[0], self.stream())
+
+    def pool_free(self) -> list:
+        return hs_hot_pool_read(self.ctx, int(self.cfg.num_gpu_blocks))
 
     def decode(self, layer, q, row_ids, ctx_lens, sm_scale, out, lse=None) -> None:
         B, S = q.shape[0], q.shape[1]

@@ -34,9 +34,12 @@ def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
 class GpuWorkload:
     def __init__(self, wl: synth.Workload, device: str = "cuda:0", topk_lds_candidates: int = 0,
                  layout: synth.Layout | None = None, verbose: bool = False,
-                 max_pages: int | None = None, max_queries: int | None = None):
+                 max_pages: int | None = None, max_queries: int | None = None,
+                 lease_pool: list | None = None):
         """`max_pages` / `max_queries` configure the context wider than the workload needs (the
-        block tables are padded with placeholders)."""
+        block tables are padded with placeholders).  With `lease_pool` (a list of GPU blocks, in
+        pool order) hot pages are leased from that free-block pool on first need, on the GPU and
+        in the oracle alike, instead of taking the layout's hot blocks."""
         self.wl = wl
         self.lay = layout or synth.make_layout(wl)
         lay = self.lay
@@ -52,7 +55,8 @@ class GpuWorkload:
                               max_pages_per_req=lay.block_table.shape[1], hot_rows_per_req=wl.hot_rows,
                               num_gpu_blocks=lay.num_gpu_blocks, num_idx_blocks=lay.num_idx_blocks,
                               num_host_blocks=lay.num_host_blocks,
-                              topk_lds_candidates=topk_lds_candidates)
+                              topk_lds_candidates=topk_lds_candidates,
+                              hot_leasing=1 if lease_pool is not None else 0)
         self.ctx = hsb.Context(cfg, device)
         t0 = time.time()
         idx_stage = np.zeros(lay.num_idx_blocks * wl.idx_block_bytes, np.uint8)
@@ -77,7 +81,14 @@ class GpuWorkload:
         self.ctx.idx_block_table.copy_(torch.from_numpy(lay.idx_block_table))
         self.ctx.block_table.copy_(torch.from_numpy(lay.block_table))
         self.ctx.host_block_table.copy_(torch.from_numpy(lay.host_block_table))
-        if lay.hot_blocks.size:
+        self.leasing = lease_pool is not None
+        self.pool = None
+        self.hot = lay.hot_blocks                       # the oracle's hot-page tables
+        if self.leasing:
+            self.hot = np.full_like(lay.hot_blocks, -1)
+            self.pool = oracle.HotPool(lease_pool)
+            self.ctx.pool_give(torch.tensor(list(lease_pool), dtype=torch.int32, device=self.dev))
+        elif lay.hot_blocks.size:
             self.ctx.hot_blocks.copy_(torch.from_numpy(lay.hot_blocks))
         torch.cuda.synchronize()
         self.chains = [synth.qidx(wl, b, (wl.steps + 1) * wl.queries) for b in range(wl.batch)]
@@ -137,10 +148,13 @@ class GpuWorkload:
         sc = self.oracle_scores(b, qidx, ctx_len)
         return np.stack([oracle.topk_select(s, self.wl.topk) for s in sc]), sc
 
-    def oracle_resolve(self, b: int, topk_b: np.ndarray):
+    def oracle_resolve(self, b: int, topk_b: np.ndarray, window_start: int | None = None):
         lay = self.lay
-        return oracle.resolve(topk_b, lay.block_table[b], lay.host_block_table[b], lay.hot_blocks[b],
-                              self.states[b])
+        return oracle.resolve(topk_b, lay.block_table[b], lay.host_block_table[b], self.hot[b],
+                              self.states[b], self.pool, window_start)
+
+    def oracle_release(self, b: int) -> list:
+        return oracle.release_hot(self.states[b], self.hot[b], self.pool)
 
     def oracle_attention(self, b: int, j: int, layer: int, tokens: np.ndarray, q) -> tuple:
         rows = synth.latent_tokens(self.wl, b, layer, tokens)

@@ -58,6 +58,7 @@ def test_workspace_and_pool_sizes():
     ("kv_dtype", 7, hsb.HS_ERR_UNSUPPORTED),
     ("num_gpu_blocks", 0, hsb.HS_ERR_INVALID_ARG),
     ("num_gpu_blocks", 1 << 26, hsb.HS_ERR_INVALID_ARG),     # row ids would overflow int32
+    ("hot_leasing", 2, hsb.HS_ERR_INVALID_ARG),
 ])
 def test_config_validation(field, value, status):
     cfg = _cfg()
@@ -110,3 +111,19 @@ def test_write_side_argument_checks():
     assert "ctx is NULL" in hsb.hs_last_error()
     a, b = ctypes.c_int64(), ctypes.c_int64()
     assert lib.hs_select_paths(None, ctypes.byref(a), ctypes.byref(b)) == hsb.HS_ERR_INVALID_ARG
+
+
+def test_leasing_argument_checks():
+    # NULL contexts and lists are refused on the host; leasing needs a host pool
+    lib = hsb.lib()
+    lst = (ctypes.c_int32 * 2)(0, 1)
+    assert lib.hs_hot_release(None, lst, 2, None) == hsb.HS_ERR_INVALID_ARG
+    assert lib.hs_hot_pool_give(None, lst, 2, None) == hsb.HS_ERR_INVALID_ARG
+    n = ctypes.c_int32()
+    assert lib.hs_hot_pool_read(None, lst, 2, ctypes.byref(n)) == hsb.HS_ERR_INVALID_ARG
+    assert lib.hisparse_resolve_plan(None, None, None, 1, 1, None, None, None, None) == hsb.HS_ERR_INVALID_ARG
+    with pytest.raises(hsb.HiSparseError) as e:
+        hsb.hs_workspace_bytes(_cfg(hot_leasing=1, num_host_blocks=0))
+    assert e.value.status == hsb.HS_ERR_INVALID_ARG and "host pool" in hsb.hs_last_error()
+    # the pool's ring takes one int32 per GPU block
+    assert hsb.hs_workspace_bytes(_cfg(num_gpu_blocks=4096)) >= hsb.hs_workspace_bytes(_cfg(num_gpu_blocks=2048)) + 8192 - 256
