@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--scale", type=int, default=1, help="divide context lengths (development only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-requests", type=int, default=64)
+    ap.add_argument("--prefill-tokens", type=int, default=32768,
+                    help="prompt length of the prefill measurement (0: skip it)")
     return ap.parse_args()
 
 
@@ -249,6 +251,8 @@ def main() -> int:
     copy_gbps = copy_bytes / (ktimes["miss_copy"][0] / ktimes["miss_copy"][1] * 1e-3) / 1e9 if ktimes["miss_copy"][1] else 0.0
     host_gbps = copy_bytes / (t_res * 1e-3) / 1e9
 
+    pre = bench_prefill(torch, dev, args.prefill_tokens) if args.prefill_tokens > 0 else None
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, chains, args.cpu_sample_requests)
@@ -316,6 +320,7 @@ def main() -> int:
                      "measured_stream_read_gbps": round(stream_read, 1),
                      "frac_of_measured_stream_read": round(sweep_gbps / stream_read, 4),
                      "mfma_frac_bf16_dense": round(sweep_f / (t_sweep_ms * 1e-3) / (BF16_DENSE_TFLOPS * 1e12), 4)},
+        "prefill": pre,
         "cpu_baseline": cpu,
         "host_wall_s": round(t_host, 4),
     }
@@ -324,19 +329,89 @@ def main() -> int:
     return 0
 
 
-def measure_stream_read(torch, dev) -> float:
-    """The box's streaming-read rate (GB/s): a reduction over a 4 GiB fp32 buffer, best of 5."""
-    x = torch.ones(1 << 30, dtype=torch.float32, device=dev)
-    best = 0.0
-    for _ in range(6):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        x.sum()
-        e1.record()
+def bench_prefill(torch, dev, P: int) -> dict:
+    """One request's prompt of P tokens (all pages resident, FP8 rows and keys, K = 2,048): the
+    prefill indexer (every new token scores every earlier token, then its top-K) and sparse MLA
+    attention of one layer on the decode kernel over those selections.  Compute-bound: the
+    roofline is bf16 dense MFMA.  Queries are seeded N(0,1) drawn on the device (timing only;
+    the prefill parity tests use the host generator)."""
+    import numpy as np
+
+    import synth
+    from sparse_mla_attention_score_amd import accounting as acc
+    from sparse_mla_attention_score_amd import hisparse as hsb
+
+    K = 2048
+    wl = synth.toy(seed=synth.SEED_BASE + 6, batch=1, queries=4, ctx=(P,), topk=K, steps=1,
+                   residency=[(synth.RES_FULL, 1.0)])
+    lay = synth.make_layout(wl)
+    max_batch = 64                               # chunks of 64 x 4 prompt tokens
+    pad = ((0, max_batch - 1), (0, 0))
+    cfg = hsb.make_config(topk=K, n_layers=1, max_batch=max_batch, max_queries=4,
+                          max_pages_per_req=wl.max_pages, num_gpu_blocks=lay.num_gpu_blocks,
+                          num_idx_blocks=lay.num_idx_blocks, num_host_blocks=0)
+    ctx = hsb.Context(cfg, dev)
+    stage = np.zeros(lay.num_idx_blocks * wl.idx_block_bytes, np.uint8)
+    synth.fill_idx_pool(wl, lay, stage)
+    ctx.idx_pool.copy_(torch.from_numpy(stage))
+    stage = np.zeros(lay.num_gpu_blocks * 64 * wl.row_bytes, np.uint8)
+    synth.fill_kv(wl, lay, stage, None)
+    ctx.kv_pool.copy_(torch.from_numpy(stage))
+    del stage
+    ctx.idx_block_table.copy_(torch.from_numpy(np.pad(lay.idx_block_table, pad, constant_values=-1)))
+    ctx.block_table.copy_(torch.from_numpy(np.pad(lay.block_table, pad, constant_values=-1)))
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed)
+    qidx = torch.randn((P, 32, 128), generator=g, device=dev).to(torch.bfloat16)
+    w = torch.rand((P, 32), generator=g, device=dev)
+    q = torch.randn((P, 64, 576), generator=g, device=dev).to(torch.bfloat16)
+    topk = torch.empty((P, K), dtype=torch.int32, device=dev)
+    out = torch.empty((P, 64, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((P, 64), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(576.0)
+    t_idx, t_att = [], []
+    for rep in range(4):                         # the first pass warms up
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        ctx.prefill_index_topk(0, qidx, w, P, topk)
+        e[1].record()
+        ctx.prefill(0, 0, q, topk, P, scale, out, lse)
+        e[2].record()
         torch.cuda.synchronize()
-        best = max(best, x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        if rep:
+            t_idx.append(e[0].elapsed_time(e[1]))
+            t_att.append(e[1].elapsed_time(e[2]))
+    err = ctx.device_error()
+    ctx.close()
+    if err:
+        log(f"device error word after the prefill: {err:#x}")
+        return {"error": err}
+    ms_idx, ms_att = min(t_idx), min(t_att)
+    visible = np.arange(1, P + 1, dtype=np.int64)
+    idx_flops = float(acc.IDX_FLOPS_PER_KEY) * float(visible.sum())
+    att_flops = float(np.minimum(visible, K).sum()) * 64 * acc.FLOPS_PER_HEAD_ROW
+    return {"workload": f"prefill_{P}_fp8", "tokens": P, "topk": K, "layers": 1,
+            "indexer_ms": round(ms_idx, 3), "attention_ms": round(ms_att, 3),
+            "tokens_per_s": round(P / ((ms_idx + ms_att) * 1e-3), 1),
+            "indexer": {"algorithmic_flops": idx_flops, "tflops": round(idx_flops / (ms_idx * 1e-3) / 1e12, 2),
+                        "bound": "mfma", "peak_tflops": BF16_DENSE_TFLOPS,
+                        "frac": round(idx_flops / (ms_idx * 1e-3) / (BF16_DENSE_TFLOPS * 1e12), 4)},
+            "attention": {"algorithmic_flops": att_flops, "tflops": round(att_flops / (ms_att * 1e-3) / 1e12, 2),
+                          "bound": "mfma", "peak_tflops": BF16_DENSE_TFLOPS,
+                          "frac": round(att_flops / (ms_att * 1e-3) / (BF16_DENSE_TFLOPS * 1e12), 4)},
+            "note": "indexer + top-K of every prompt token, then one layer of sparse MLA on the "
+                    "decode kernel; run as groups of 4 tokens, 256 tokens per chunk"}
+
+
+def measure_stream_read(torch, dev) -> float:
+    """The box's streaming-read rate (GB/s): a plain read of a 4 GiB buffer by the library's
+    measurement kernel, best of 5."""
+    from sparse_mla_attention_score_amd import hisparse as hsb
+    x = torch.ones(1 << 30, dtype=torch.float32, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    g = hsb.hs_measure_read_gbps(x.data_ptr(), x.numel() * 4, sink.data_ptr(), 5)
     del x
-    return best
+    return g
 
 
 def cpu_info() -> dict:

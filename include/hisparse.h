@@ -21,6 +21,12 @@
  *                        dims as value.  Part-2 page, "Try it" (the sparse-MLA MQA kernel)
  *                        and footnote 1 (656-byte FP8 rows, QK over 576 dims, PV over 512).
  *
+ * Around the step: the write side of the host pool (hisparse_materialize_pages,
+ * hisparse_release_pages), hot pages leased from a free-block pool and released per request
+ * (hs_config.hot_leasing, hs_hot_pool_give, hs_hot_release), plan windows for speculative
+ * decoding (hisparse_resolve_plan), and the prefill of a prompt on the same kernels
+ * (hisparse_prefill_index_topk, sparse_mla_prefill).
+ *
  * Conventions shared by every call:
  *   - Status codes are returned; nothing throws across the ABI.  hs_last_error() gives a
  *     human-readable reason for the last failing call on the calling thread.
@@ -268,6 +274,38 @@ hs_status sparse_mla_decode(hs_ctx* ctx, int32_t layer, const void* q, const int
                             const int32_t* ctx_lens, int32_t B, int32_t S, float sm_scale,
                             void* out, float* lse, void* stream);
 
+/*
+ * Prefill of request slot b: the P new tokens that end its L-token context (rows and indexer
+ * keys of all L tokens already written; every page resident).  Token i of the P (0-based) is
+ * query i; it sees the rows t < L - P + 1 + i, causally, as a decode query sees its context.
+ *
+ * hisparse_prefill_index_topk: the indexer of every new token over every earlier token, the
+ *   cost that grows with the square of the prompt (GLM-5.3 part-2 page, "PCP: split tokens,
+ *   not heads", the paragraph on the indexer's cost), and the top-K of each, as
+ *   hisparse_index_topk computes them for a decode query.
+ *     q_idx     device [P][32][128] bf16;  w  device [P][32] fp32
+ *     topk_out  device [P][topk] int32, ascending tokens, -1 padded
+ * sparse_mla_prefill: sparse MLA attention of layer `layer` for the P tokens on the decode's
+ *   MQA kernel: every row read serves all 64 heads (part-2 page, "Try it": with
+ *   sparse_mla_force_mqa, prompts within the top-K stay on the sparse-MLA MQA kernel instead
+ *   of dense MHA).
+ *     q         device [P][64][576] bf16
+ *     topk      device [P][topk] int32 (from hisparse_prefill_index_topk), or NULL for every
+ *               row each token sees, which needs L <= topk (the prompt lies within top-K)
+ *     out, lse  device [P][64][512] bf16 and [P][64] fp32 (lse may be NULL)
+ * Both run the prompt in chunks of max_batch x max_queries tokens as decode-shaped groups of
+ * max_queries tokens and use the context's top-K and decode scratch: do not overlap them with
+ * step calls of the same context on other streams.  The request's hot state and top-K guesses
+ * are untouched.  A placeholder page flags HS_DEVERR_BAD_BLOCK, a token a query cannot see
+ * HS_DEVERR_BAD_ROW.  Host errors: HS_ERR_INVALID_ARG (b outside [0, max_batch), P < 1,
+ * L < P, L past the block table, a NULL pointer, NULL topk with L > topk).
+ */
+hs_status hisparse_prefill_index_topk(hs_ctx* ctx, int32_t b, const void* q_idx, const float* w,
+                                      int32_t L, int32_t P, int32_t* topk_out, void* stream);
+hs_status sparse_mla_prefill(hs_ctx* ctx, int32_t layer, int32_t b, const void* q,
+                             const int32_t* topk, int32_t L, int32_t P, float sm_scale, void* out,
+                             float* lse, void* stream);
+
 /* Synchronise the context's device and read (then clear) the device error word. */
 hs_status hs_read_device_error(hs_ctx* ctx, int32_t* code);
 
@@ -347,6 +385,12 @@ typedef enum {
 
 hs_status hs_kernel_timing(hs_ctx* ctx, int32_t enable);
 hs_status hs_kernel_times(hs_ctx* ctx, double* ms, int64_t* launches, int32_t n);
+
+/* Measurement helper, not part of the decode step: the best of `reps` streaming reads of the
+ * device buffer `buf` (`bytes`, 16-byte aligned; each 16-byte piece read once per pass) on the
+ * current device's null stream, in GB/s.  `sink` is a device word the reads are folded into
+ * (written only in the unlikely case the fold meets a fixed constant).  Synchronises. */
+hs_status hs_measure_read_gbps(const void* buf, size_t bytes, void* sink, int32_t reps, double* gbps);
 
 const char* hs_status_string(hs_status status);
 const char* hs_last_error(void);

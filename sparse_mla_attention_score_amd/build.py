@@ -12,7 +12,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhisparse.so")
-SOURCES = ["hs_api.cpp", "hs_index_topk.hip", "hs_resolve.hip", "hs_decode.hip", "hs_offload.hip"]
+SOURCES = ["hs_api.cpp", "hs_index_topk.hip", "hs_resolve.hip", "hs_decode.hip", "hs_offload.hip",
+           "hs_measure.hip"]
 ARCH = os.environ.get("HS_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

@@ -183,6 +183,10 @@ hs_status hs::compute_layout(const hs_config& c, Layout* L) {
   L->off_cands = take(B * S * L->n_seg * kSegCap * 8);
   L->off_path_count = take(2 * 8);
   L->off_zero_row = take(kZeroRowBytes);
+  L->off_pf_lens = take(B * 4);
+  L->off_pf_guess = take(B * S * 4);
+  L->off_pf_paths = take(2 * 8);
+  L->off_pf_rows = take(B * S * c.topk * 4);
   L->total = off;
   return HS_OK;
 }
@@ -376,6 +380,10 @@ hs_status hs_bind(hs_ctx* ctx, const hs_buffers* b) {
   ctx->ws.cands = reinterpret_cast<uint64_t*>(w + L.off_cands);
   ctx->ws.path_count = reinterpret_cast<unsigned long long*>(w + L.off_path_count);
   ctx->ws.zero_row = w + L.off_zero_row;
+  ctx->ws.pf_lens = reinterpret_cast<int32_t*>(w + L.off_pf_lens);
+  ctx->ws.pf_guess = reinterpret_cast<uint32_t*>(w + L.off_pf_guess);
+  ctx->ws.pf_paths = reinterpret_cast<unsigned long long*>(w + L.off_pf_paths);
+  ctx->ws.pf_rows = reinterpret_cast<int32_t*>(w + L.off_pf_rows);
   // the row of zeros the decode reads for skipped rows: written once here, read-only for
   // every kernel
   hipError_t e = hipSetDevice(ctx->device);
@@ -494,6 +502,45 @@ hs_status sparse_mla_decode(hs_ctx* ctx, int32_t layer, const void* q, const int
   hipError_t e = hs_launch_decode(ctx, layer, q, row_ids, ctx_lens, B, S, sm_scale, out, lse,
                                   splits, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "sparse_mla_decode launch");
+}
+
+static hs_status check_prefill(const hs_ctx* ctx, int32_t b, int32_t L, int32_t P, const char* what) {
+  if (!ctx) return fail(HS_ERR_INVALID_ARG, "%s: ctx is NULL", what);
+  if (!ctx->bound) return fail(HS_ERR_STATE, "%s: context is not bound", what);
+  if (b < 0 || b >= ctx->cfg.max_batch)
+    return fail(HS_ERR_INVALID_ARG, "%s: request %d outside [0, %d)", what, b, ctx->cfg.max_batch);
+  if (P < 1 || L < P || (int64_t)L > (int64_t)ctx->cfg.max_pages_per_req * hs::kBlock)
+    return fail(HS_ERR_INVALID_ARG, "%s: need 1 <= P <= L <= %lld (P=%d, L=%d)", what,
+                (long long)ctx->cfg.max_pages_per_req * hs::kBlock, P, L);
+  return HS_OK;
+}
+
+hs_status hisparse_prefill_index_topk(hs_ctx* ctx, int32_t b, const void* q_idx, const float* w,
+                                      int32_t L, int32_t P, int32_t* topk_out, void* stream) {
+  hs_status s = check_prefill(ctx, b, L, P, "hisparse_prefill_index_topk");
+  if (s != HS_OK) return s;
+  if (!q_idx || !w || !topk_out)
+    return fail(HS_ERR_INVALID_ARG, "hisparse_prefill_index_topk: a pointer argument is NULL");
+  hipError_t e = hs_launch_prefill_index_topk(ctx, b, q_idx, w, L, P, topk_out,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "hisparse_prefill_index_topk launch");
+}
+
+hs_status sparse_mla_prefill(hs_ctx* ctx, int32_t layer, int32_t b, const void* q,
+                             const int32_t* topk, int32_t L, int32_t P, float sm_scale, void* out,
+                             float* lse, void* stream) {
+  hs_status s = check_prefill(ctx, b, L, P, "sparse_mla_prefill");
+  if (s != HS_OK) return s;
+  if (layer < 0 || layer >= ctx->cfg.n_layers)
+    return fail(HS_ERR_INVALID_ARG, "sparse_mla_prefill: layer %d outside [0, %d)", layer, ctx->cfg.n_layers);
+  if (!std::isfinite(sm_scale)) return fail(HS_ERR_INVALID_ARG, "sparse_mla_prefill: sm_scale not finite");
+  if (!q || !out) return fail(HS_ERR_INVALID_ARG, "sparse_mla_prefill: a pointer argument is NULL");
+  if (!topk && L > ctx->cfg.topk)
+    return fail(HS_ERR_INVALID_ARG, "sparse_mla_prefill: without a top-K the context (%d) must fit top-K (%d)",
+                L, ctx->cfg.topk);
+  hipError_t e = hs_launch_prefill_decode(ctx, layer, b, q, topk, L, P, sm_scale, out, lse,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "sparse_mla_prefill launch");
 }
 
 hs_status hs_decode_splits(const hs_ctx* ctx, int32_t B, int32_t S, int32_t* splits) {

@@ -872,6 +872,32 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
   *reinterpret_cast<u32x2*>(out + ((int64_t)bj * kHeads + h0 + hl) * kDv + 4 * piece) = u32x2{w0, w1};
 }
 
+// Row ids of a prefill chunk's selections: queries [0, n) of the chunk, query i seeing
+// `visible0 + i` rows; token t of the request reads row block_table[t / 64] * 64 + t % 64 (a
+// prefill reads resident pages: a placeholder page flags HS_DEVERR_BAD_BLOCK).  Without a
+// top-K (topk == nullptr) query i takes every row it sees, as a prompt within top-K does.
+__global__ void prefill_rows_kernel(const int32_t* __restrict__ topk, int K, int n, int visible0,
+                                    const int32_t* __restrict__ bt, int n_pages,
+                                    int64_t num_gpu_blocks, int32_t* __restrict__ rows,
+                                    int32_t* __restrict__ err) {
+  const int64_t total = (int64_t)n * K;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int i = (int)(idx / K), k = (int)(idx - (int64_t)i * K);
+    const int visible = visible0 + i;
+    const int32_t t = topk ? topk[idx] : (k < visible ? k : -1);
+    int32_t r = -1;
+    if (t >= visible || (t >= 0 && (t >> 6) >= n_pages)) {
+      raise_error(err, HS_DEVERR_BAD_ROW);
+    } else if (t >= 0) {
+      const int32_t blk = bt[t >> 6];
+      if (blk >= 0 && blk < num_gpu_blocks) r = blk * kBlock + (t & 63);
+      else raise_error(err, HS_DEVERR_BAD_BLOCK);
+    }
+    rows[idx] = r;
+  }
+}
+
 }  // namespace
 }  // namespace hs
 
@@ -935,4 +961,46 @@ hipError_t hs_launch_decode(const hs_ctx* ctx, int layer, const void* q, const i
 hipError_t hs_set_kernel_attributes() {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&sparse_mla_decode_kernel<false>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, DecLds::kTotal);
+}
+
+// Prefill attention on the sparse-MLA decode kernel: the P new tokens of request b, in chunks of
+// max_batch x max_queries queries run as decode-shaped groups (see hs_launch_prefill_lens).
+hipError_t hs_launch_prefill_decode(const hs_ctx* ctx, int layer, int b, const void* q,
+                                    const int32_t* topk, int L, int P, float sm_scale, void* out,
+                                    float* lse, hipStream_t stream) {
+  const hs_config& c = ctx->cfg;
+  const int S = c.max_queries, chunk = c.max_batch * c.max_queries, K = c.topk;
+  const int32_t* bt = ctx->buf.block_table + (int64_t)b * c.max_pages_per_req;
+  const size_t q_bytes = (size_t)kHeads * kDqk * 2, o_bytes = (size_t)kHeads * kDv * 2;
+  for (int c0 = 0; c0 < P; c0 += chunk) {
+    const int n = P - c0 < chunk ? P - c0 : chunk;
+    const int full = n / S, rem = n - full * S;
+    hipError_t e = hs_launch_prefill_lens(ctx, L, P, c0, n, stream);
+    if (e != hipSuccess) return e;
+    const int64_t cells = (int64_t)n * K;
+    int blocks = (int)((cells + 255) / 256);
+    if (blocks > 2048) blocks = 2048;
+    hipLaunchKernelGGL(prefill_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       topk ? topk + (int64_t)c0 * K : nullptr, K, n, L - P + 1 + c0, bt,
+                       c.max_pages_per_req, (int64_t)c.num_gpu_blocks, ctx->ws.pf_rows, ctx->ws.err);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned char* qb = static_cast<const unsigned char*>(q) + (size_t)c0 * q_bytes;
+    unsigned char* ob = static_cast<unsigned char*>(out) + (size_t)c0 * o_bytes;
+    float* lb = lse ? lse + (int64_t)c0 * kHeads : nullptr;
+    if (full) {
+      e = hs_launch_decode(ctx, layer, qb, ctx->ws.pf_rows, ctx->ws.pf_lens, full, S, sm_scale, ob,
+                           lb, hs_choose_splits(ctx, full, S), stream);
+      if (e != hipSuccess) return e;
+    }
+    if (rem) {
+      const int i0 = full * S;
+      e = hs_launch_decode(ctx, layer, qb + (size_t)i0 * q_bytes, ctx->ws.pf_rows + (int64_t)i0 * K,
+                           ctx->ws.pf_lens + full, 1, rem, sm_scale, ob + (size_t)i0 * o_bytes,
+                           lb ? lb + (int64_t)i0 * kHeads : nullptr, hs_choose_splits(ctx, 1, rem),
+                           stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }

@@ -87,7 +87,8 @@ template <int S, bool kFp8>
 __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const int32_t* __restrict__ ctx_lens, const uint8_t* __restrict__ idx_pool,
-    const int32_t* __restrict__ idx_block_table, int max_pages, int64_t num_idx_blocks, int B,
+    const int32_t* __restrict__ idx_block_table, int64_t table_stride, int max_pages,
+    int64_t num_idx_blocks, int B,
     float* __restrict__ scores, int64_t lmax, uint32_t* __restrict__ hist,
     const uint32_t* __restrict__ guess, int guess_stride, uint32_t* __restrict__ seg_count,
     uint64_t* __restrict__ cands, int n_seg, int32_t* __restrict__ err) {
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
     const int p = p_begin + threadIdx.x;
     int32_t blk = -1;
     if (p < p_end) {
-      blk = idx_block_table[(int64_t)b * max_pages + p];
+      blk = idx_block_table[(int64_t)b * table_stride + p];
       if (blk < 0 || blk >= num_idx_blocks) {
         raise_error(err, HS_DEVERR_BAD_BLOCK);
         blk = -1;
@@ -842,21 +843,85 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   if (tid == 0 && total != K) raise_error(err, HS_DEVERR_TOPK_COUNT);
 }
 
+// One sweep + select over B requests of S queries.  `idx_table` rows are `table_stride` apart
+// (0: every request reads the same row, as the groups of one prefill do); the select keeps its
+// guesses in `guess` ([B][guess_stride]) and counts its paths in `paths`.
+struct IndexCall {
+  const void* q_idx;
+  const float* w;
+  const int32_t* ctx_lens;
+  int B, S;
+  const int32_t* idx_table;
+  int64_t table_stride;
+  uint32_t* guess;
+  int guess_stride;
+  unsigned long long* paths;
+  int32_t* topk_out;
+};
+
 template <int S, bool kFp8>
-hipError_t launch_scores(const hs_ctx* ctx, const void* q_idx, const float* w,
-                         const int32_t* ctx_lens, int B, hipStream_t stream) {
+hipError_t launch_scores(const hs_ctx* ctx, const IndexCall& a, hipStream_t stream) {
   const hs_config& c = ctx->cfg;
   const int items = (c.max_pages_per_req + kPagesPerItem - 1) / kPagesPerItem;
-  dim3 grid((unsigned)(B * items)), block(kSweepThreads);
+  dim3 grid((unsigned)(a.B * items)), block(kSweepThreads);
   hs_timer_mark(ctx, HS_KERNEL_INDEX_SCORE, true, stream);
   hipLaunchKernelGGL((index_score_kernel<S, kFp8>), grid, block, 0, stream,
-                     static_cast<const uint16_t*>(q_idx), w, ctx_lens,
-                     static_cast<const uint8_t*>(ctx->buf.idx_pool), ctx->buf.idx_block_table,
-                     c.max_pages_per_req, (int64_t)c.num_idx_blocks, B, ctx->ws.scores,
-                     ctx->lay.lmax, ctx->ws.hist, ctx->ws.guess, c.max_queries, ctx->ws.seg_count, ctx->ws.cands,
-                     ctx->lay.n_seg, ctx->ws.err);
+                     static_cast<const uint16_t*>(a.q_idx), a.w, a.ctx_lens,
+                     static_cast<const uint8_t*>(ctx->buf.idx_pool), a.idx_table, a.table_stride,
+                     c.max_pages_per_req, (int64_t)c.num_idx_blocks, a.B, ctx->ws.scores,
+                     ctx->lay.lmax, ctx->ws.hist, a.guess, a.guess_stride, ctx->ws.seg_count,
+                     ctx->ws.cands, ctx->lay.n_seg, ctx->ws.err);
   hs_timer_mark(ctx, HS_KERNEL_INDEX_SCORE, false, stream);
   return hipGetLastError();
+}
+
+hipError_t launch_index_call(const hs_ctx* ctx, const IndexCall& a, hipStream_t stream) {
+  const bool fp8 = ctx->cfg.idx_dtype == HS_FP8_E4M3;
+  hipError_t e;
+  switch (a.S * 2 + (fp8 ? 1 : 0)) {
+    case 2: e = launch_scores<1, false>(ctx, a, stream); break;
+    case 3: e = launch_scores<1, true>(ctx, a, stream); break;
+    case 4: e = launch_scores<2, false>(ctx, a, stream); break;
+    case 5: e = launch_scores<2, true>(ctx, a, stream); break;
+    case 6: e = launch_scores<3, false>(ctx, a, stream); break;
+    case 7: e = launch_scores<3, true>(ctx, a, stream); break;
+    case 8: e = launch_scores<4, false>(ctx, a, stream); break;
+    case 9: e = launch_scores<4, true>(ctx, a, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  const int cap = hs_select_cand_cap(ctx->cfg);
+  const bool lds_bitmap = ctx->lay.bm_words <= kLdsBitmapMaxWords;
+  const size_t dyn = (size_t)cap * sizeof(uint64_t) + (lds_bitmap ? (size_t)ctx->lay.bm_words * 4 : 0);
+  const dim3 grid((unsigned)(a.B * a.S));
+  hs_timer_mark(ctx, HS_KERNEL_TOPK_SELECT, true, stream);
+  if (lds_bitmap)
+    hipLaunchKernelGGL(topk_select_kernel<true>, grid, dim3(kSelThreads), dyn, stream, a.ctx_lens,
+                       a.B, a.S, ctx->cfg.topk, ctx->cfg.max_pages_per_req * kBlock,
+                       ctx->ws.scores, ctx->lay.lmax, ctx->ws.hist, ctx->ws.bitmap,
+                       (int64_t)ctx->lay.bm_words, a.topk_out, cap, a.guess, a.guess_stride,
+                       ctx->ws.seg_count, ctx->ws.cands, ctx->lay.n_seg, a.paths, ctx->ws.err);
+  else
+    hipLaunchKernelGGL(topk_select_kernel<false>, grid, dim3(kSelThreads), dyn, stream, a.ctx_lens,
+                       a.B, a.S, ctx->cfg.topk, ctx->cfg.max_pages_per_req * kBlock,
+                       ctx->ws.scores, ctx->lay.lmax, ctx->ws.hist, ctx->ws.bitmap,
+                       (int64_t)ctx->lay.bm_words, a.topk_out, cap, a.guess, a.guess_stride,
+                       ctx->ws.seg_count, ctx->ws.cands, ctx->lay.n_seg, a.paths, ctx->ws.err);
+  hs_timer_mark(ctx, HS_KERNEL_TOPK_SELECT, false, stream);
+  return hipGetLastError();
+}
+
+// A prefill chunk as decode-shaped groups: queries [c0, c0 + n) of the P new tokens that end an
+// L-token context, S at a time (the last group may be smaller).  Group v's context length is
+// base + end_v with base = L - P + c0 and end_v its last query + 1, so query j of the group sees
+// L - P + 1 + (c0 + S v + j) rows, as the prefill's causal rule asks.  The groups' top-K guesses
+// start off (a prefill has no previous call to guess from).
+__global__ void prefill_setup_kernel(int32_t* __restrict__ lens, uint32_t* __restrict__ guess,
+                                     int groups, int S, int n, int base, int n_guess) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_guess; i += gridDim.x * blockDim.x) {
+    if (i < groups) lens[i] = base + min(n, S * (i + 1));
+    guess[i] = kGuessOff;
+  }
 }
 
 }  // namespace
@@ -886,36 +951,46 @@ int hs_select_cand_cap(const hs_config& c) {
 hipError_t hs_launch_index_topk(const hs_ctx* ctx, const void* q_idx, const float* w,
                                 const int32_t* ctx_lens, int B, int S, int32_t* topk_out,
                                 hipStream_t stream) {
-  const bool fp8 = ctx->cfg.idx_dtype == HS_FP8_E4M3;
-  hipError_t e;
-  switch (S * 2 + (fp8 ? 1 : 0)) {
-    case 2: e = launch_scores<1, false>(ctx, q_idx, w, ctx_lens, B, stream); break;
-    case 3: e = launch_scores<1, true>(ctx, q_idx, w, ctx_lens, B, stream); break;
-    case 4: e = launch_scores<2, false>(ctx, q_idx, w, ctx_lens, B, stream); break;
-    case 5: e = launch_scores<2, true>(ctx, q_idx, w, ctx_lens, B, stream); break;
-    case 6: e = launch_scores<3, false>(ctx, q_idx, w, ctx_lens, B, stream); break;
-    case 7: e = launch_scores<3, true>(ctx, q_idx, w, ctx_lens, B, stream); break;
-    case 8: e = launch_scores<4, false>(ctx, q_idx, w, ctx_lens, B, stream); break;
-    case 9: e = launch_scores<4, true>(ctx, q_idx, w, ctx_lens, B, stream); break;
-    default: return hipErrorInvalidValue;
-  }
-  if (e != hipSuccess) return e;
-  const int cap = hs_select_cand_cap(ctx->cfg);
-  const bool lds_bitmap = ctx->lay.bm_words <= kLdsBitmapMaxWords;
-  const size_t dyn = (size_t)cap * sizeof(uint64_t) + (lds_bitmap ? (size_t)ctx->lay.bm_words * 4 : 0);
-  hs_timer_mark(ctx, HS_KERNEL_TOPK_SELECT, true, stream);
-  if (lds_bitmap)
-    hipLaunchKernelGGL(topk_select_kernel<true>, dim3((unsigned)(B * S)), dim3(kSelThreads), dyn, stream,
-                       ctx_lens, B, S, ctx->cfg.topk, ctx->cfg.max_pages_per_req * kBlock,
-                       ctx->ws.scores, ctx->lay.lmax, ctx->ws.hist, ctx->ws.bitmap,
-                       (int64_t)ctx->lay.bm_words, topk_out, cap, ctx->ws.guess, ctx->cfg.max_queries, ctx->ws.seg_count,
-                       ctx->ws.cands, ctx->lay.n_seg, ctx->ws.path_count, ctx->ws.err);
-  else
-    hipLaunchKernelGGL(topk_select_kernel<false>, dim3((unsigned)(B * S)), dim3(kSelThreads), dyn, stream,
-                       ctx_lens, B, S, ctx->cfg.topk, ctx->cfg.max_pages_per_req * kBlock,
-                       ctx->ws.scores, ctx->lay.lmax, ctx->ws.hist, ctx->ws.bitmap,
-                       (int64_t)ctx->lay.bm_words, topk_out, cap, ctx->ws.guess, ctx->cfg.max_queries, ctx->ws.seg_count,
-                       ctx->ws.cands, ctx->lay.n_seg, ctx->ws.path_count, ctx->ws.err);
-  hs_timer_mark(ctx, HS_KERNEL_TOPK_SELECT, false, stream);
+  const IndexCall a{q_idx, w, ctx_lens, B, S, ctx->buf.idx_block_table, ctx->cfg.max_pages_per_req,
+                    ctx->ws.guess, ctx->cfg.max_queries, ctx->ws.path_count, topk_out};
+  return launch_index_call(ctx, a, stream);
+}
+
+hipError_t hs_launch_prefill_lens(const hs_ctx* ctx, int L, int P, int c0, int n, hipStream_t stream) {
+  const int S = ctx->cfg.max_queries;
+  const int groups = (n + S - 1) / S;
+  const int n_guess = ctx->cfg.max_batch * S;
+  hipLaunchKernelGGL(prefill_setup_kernel, dim3((unsigned)((n_guess + 255) / 256)), dim3(256), 0,
+                     stream, ctx->ws.pf_lens, ctx->ws.pf_guess, groups, S, n, L - P + c0, n_guess);
   return hipGetLastError();
+}
+
+hipError_t hs_launch_prefill_index_topk(const hs_ctx* ctx, int b, const void* q_idx, const float* w,
+                                        int L, int P, int32_t* topk_out, hipStream_t stream) {
+  const hs_config& c = ctx->cfg;
+  const int S = c.max_queries, chunk = c.max_batch * c.max_queries;
+  const int32_t* table = ctx->buf.idx_block_table + (int64_t)b * c.max_pages_per_req;
+  const size_t q_bytes = (size_t)kIdxHeads * kIdxDim * 2;
+  for (int c0 = 0; c0 < P; c0 += chunk) {
+    const int n = P - c0 < chunk ? P - c0 : chunk;
+    const int full = n / S, rem = n - full * S;
+    hipError_t e = hs_launch_prefill_lens(ctx, L, P, c0, n, stream);
+    if (e != hipSuccess) return e;
+    const unsigned char* qb = static_cast<const unsigned char*>(q_idx) + (size_t)c0 * q_bytes;
+    if (full) {
+      const IndexCall a{qb, w + (int64_t)c0 * kIdxHeads, ctx->ws.pf_lens, full, S, table, 0,
+                        ctx->ws.pf_guess, S, ctx->ws.pf_paths, topk_out + (int64_t)c0 * c.topk};
+      e = launch_index_call(ctx, a, stream);
+      if (e != hipSuccess) return e;
+    }
+    if (rem) {
+      const int i0 = c0 + full * S;
+      const IndexCall a{qb + (size_t)full * S * q_bytes, w + (int64_t)i0 * kIdxHeads,
+                        ctx->ws.pf_lens + full, 1, rem, table, 0, ctx->ws.pf_guess + full * S, S,
+                        ctx->ws.pf_paths, topk_out + (int64_t)i0 * c.topk};
+      e = launch_index_call(ctx, a, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }

@@ -68,13 +68,18 @@ struct Workspace {
   uint64_t* cands;       // [Bmax][Smax][n_seg][kSegCap] (key << 32) | ~token
   unsigned long long* path_count;  // [2] selections made from the candidate list / the scores
   uint8_t* zero_row;     // [kZeroRowBytes]    zeros: what a skipped row of the decode reads
+  // prefill, run as decode-shaped groups of max_queries queries
+  int32_t* pf_lens;      // [Bmax]             context length of each group
+  uint32_t* pf_guess;    // [Bmax][Smax]       the groups' top-K guesses (off)
+  unsigned long long* pf_paths;  // [2]        selection paths of prefill calls
+  int32_t* pf_rows;      // [Bmax][Smax][K]    row ids of a prefill chunk's selections
 };
 
 struct Layout {
   size_t off_slot_token, off_slot_stamp, off_lru_order, off_tok2slot, off_req_step, off_req_used,
       off_win_start, off_pool_ring, off_pool_ctr, off_err, off_scores, off_hist, off_bitmap, off_miss_src, off_miss_dst, off_miss_cnt,
       off_part_o, off_part_ml, off_guess, off_seg_count, off_cands, off_path_count, off_zero_row,
-      total;
+      off_pf_lens, off_pf_guess, off_pf_paths, off_pf_rows, total;
   int32_t hot_rows;
   int64_t lmax;       // max_pages_per_req * 64
   int64_t bm_words;   // bitmap words per (request, query): lmax rounded up to 1,024, / 32
@@ -127,3 +132,9 @@ hipError_t hs_launch_materialize(const hs_ctx* ctx, const int32_t* pages, int n,
 hipError_t hs_launch_release(const hs_ctx* ctx, const int32_t* pages, int n, const int32_t* ctx_lens,
                              int32_t* freed, hipStream_t stream);
 int hs_select_cand_cap(const hs_config& c);
+hipError_t hs_launch_prefill_lens(const hs_ctx* ctx, int L, int P, int c0, int n, hipStream_t stream);
+hipError_t hs_launch_prefill_index_topk(const hs_ctx* ctx, int b, const void* q_idx, const float* w,
+                                        int L, int P, int32_t* topk_out, hipStream_t stream);
+hipError_t hs_launch_prefill_decode(const hs_ctx* ctx, int layer, int b, const void* q,
+                                    const int32_t* topk, int L, int P, float sm_scale, void* out,
+                                    float* lse, hipStream_t stream);

@@ -37,8 +37,9 @@ EXPORTED = ["hs_create", "hs_destroy", "hs_workspace_bytes", "hs_host_pool_bytes
             "hisparse_resolve", "sparse_mla_decode", "hs_read_device_error", "hs_decode_splits",
             "hs_hot_state", "hs_kernel_timing", "hs_kernel_times", "hs_select_paths",
             "hisparse_materialize_pages", "hisparse_release_pages", "hisparse_resolve_plan",
-            "hs_hot_release", "hs_hot_pool_give", "hs_hot_pool_read", "hs_status_string",
-            "hs_last_error"]
+            "hs_hot_release", "hs_hot_pool_give", "hs_hot_pool_read",
+            "hisparse_prefill_index_topk", "sparse_mla_prefill", "hs_measure_read_gbps",
+            "hs_status_string", "hs_last_error"]
 
 
 class hs_config(ctypes.Structure):
@@ -98,6 +99,9 @@ def lib() -> ctypes.CDLL:
             "hs_hot_release": [P, P, i32, P],
             "hs_hot_pool_give": [P, P, i32, P],
             "hs_hot_pool_read": [P, ctypes.POINTER(i32), i32, ctypes.POINTER(i32)],
+            "hisparse_prefill_index_topk": [P, i32, P, P, i32, i32, P, P],
+            "sparse_mla_prefill": [P, i32, i32, P, P, i32, i32, f32, P, P, P],
+            "hs_measure_read_gbps": [P, ctypes.c_size_t, P, i32, ctypes.POINTER(ctypes.c_double)],
             "sparse_mla_decode": [P, i32, P, P, P, i32, i32, f32, P, P, P],
             "hs_read_device_error": [P, ctypes.POINTER(i32)],
             "hs_decode_splits": [P, i32, i32, ctypes.POINTER(i32)],
@@ -204,6 +208,24 @@ def hs_hot_pool_read(ctx: int, cap: int) -> list:
     n = ctypes.c_int32()
     _check(lib().hs_hot_pool_read(ctx, buf, cap, ctypes.byref(n)), "hs_hot_pool_read")
     return [buf[i] for i in range(min(n.value, cap))]
+
+
+def hisparse_prefill_index_topk(ctx: int, b: int, q_idx: int, w: int, L: int, P: int, topk_out: int,
+                                stream: int) -> None:
+    _check(lib().hisparse_prefill_index_topk(ctx, b, q_idx, w, L, P, topk_out, stream),
+           "hisparse_prefill_index_topk")
+
+
+def sparse_mla_prefill(ctx: int, layer: int, b: int, q: int, topk: int, L: int, P: int,
+                       sm_scale: float, out: int, lse: int, stream: int) -> None:
+    _check(lib().sparse_mla_prefill(ctx, layer, b, q, topk or None, L, P, sm_scale, out, lse or None,
+                                    stream), "sparse_mla_prefill")
+
+
+def hs_measure_read_gbps(buf: int, nbytes: int, sink: int, reps: int = 5) -> float:
+    g = ctypes.c_double()
+    _check(lib().hs_measure_read_gbps(buf, nbytes, sink, reps, ctypes.byref(g)), "hs_measure_read_gbps")
+    return g.value
 
 
 def sparse_mla_decode(ctx: int, layer: int, q: int, row_ids: int, ctx_lens: int, B: int, S: int,
@@ -352,6 +374,17 @@ class Context:
         sparse_mla_decode(self.ctx, layer, q.data_ptr(), row_ids.data_ptr(), ctx_lens.data_ptr(),
                           B, S, sm_scale, out.data_ptr(), lse.data_ptr() if lse is not None else 0,
                           self.stream())
+
+    def prefill_index_topk(self, b, q_idx, w, L, topk_out) -> None:
+        """q_idx [P][32][128] bf16, w [P][32] fp32, topk_out [P][K] int32 (device)."""
+        hisparse_prefill_index_topk(self.ctx, b, q_idx.data_ptr(), w.data_ptr(), L, q_idx.shape[0],
+                                    topk_out.data_ptr(), self.stream())
+
+    def prefill(self, layer, b, q, topk, L, sm_scale, out, lse=None) -> None:
+        """q [P][64][576] bf16; topk [P][K] int32 or None (every visible row, L <= K)."""
+        sparse_mla_prefill(self.ctx, layer, b, q.data_ptr(), topk.data_ptr() if topk is not None else 0,
+                           L, q.shape[0], sm_scale, out.data_ptr(),
+                           lse.data_ptr() if lse is not None else 0, self.stream())
 
     def device_error(self) -> int:
         return hs_read_device_error(self.ctx)

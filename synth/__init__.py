@@ -368,6 +368,37 @@ def mla_q(wl: Workload, step: int, batches=None) -> np.ndarray:
     return out
 
 
+# Prefill inputs of request b: its P new tokens are query tokens numbered from PREFILL_QUERY0 on,
+# a range no decode step reaches, so they never repeat a decode step's draws.
+PREFILL_QUERY0 = 1 << 24
+
+
+def prefill_qidx(wl: Workload, b: int, P: int) -> np.ndarray:
+    """[P][32][128] bf16 codes: indexer queries of the P new tokens (the request's drifting
+    chain: neighbouring prompt tokens are correlated)."""
+    return qidx(wl, b, P)
+
+
+def prefill_head_weights(wl: Workload, b: int, P: int) -> np.ndarray:
+    """[P][32] float32 head weights ~ U(0,1), one set per new token."""
+    w = np.empty((P, 32), np.float32)
+    for i in range(P):
+        w[i] = uniforms(wl.seed, KIND_W, b, i, 1, 32).astype(np.float32)
+    return w
+
+
+def prefill_mla_q(wl: Workload, b: int, P: int) -> np.ndarray:
+    """[P][64][576] bf16 codes: MLA queries of the P new tokens (fresh N(0,1))."""
+    return prefill_mla_q_range(wl, b, 0, P)
+
+
+def prefill_mla_q_range(wl: Workload, b: int, i0: int, n: int) -> np.ndarray:
+    """MLA queries of new tokens i0 .. i0 + n of a prefill (token i's draw does not depend on P)."""
+    out = np.empty((n, 64, 576), np.uint16)
+    lib().synth_mla_q(wl.seed, b, PREFILL_QUERY0 + i0, n, _p(out))
+    return out
+
+
 def salient_mask(wl: Workload, b: int, t0: int, n: int) -> np.ndarray:
     out = np.empty(n, np.uint8)
     lib().synth_salient_mask(wl.seed, b, t0, n, wl.salient_frac, _p(out))

@@ -35,9 +35,9 @@ class GpuWorkload:
     def __init__(self, wl: synth.Workload, device: str = "cuda:0", topk_lds_candidates: int = 0,
                  layout: synth.Layout | None = None, verbose: bool = False,
                  max_pages: int | None = None, max_queries: int | None = None,
-                 lease_pool: list | None = None):
-        """`max_pages` / `max_queries` configure the context wider than the workload needs (the
-        block tables are padded with placeholders).  With `lease_pool` (a list of GPU blocks, in
+                 lease_pool: list | None = None, max_batch: int | None = None):
+        """`max_pages` / `max_queries` / `max_batch` configure the context wider than the workload
+        needs (the block tables are padded with placeholders).  With `lease_pool` (a list of GPU blocks, in
         pool order) hot pages are leased from that free-block pool on first need, on the GPU and
         in the oracle alike, instead of taking the layout's hot blocks."""
         self.wl = wl
@@ -48,9 +48,15 @@ class GpuWorkload:
             lay.block_table = np.pad(lay.block_table, pad, constant_values=-1)
             lay.host_block_table = np.pad(lay.host_block_table, pad, constant_values=-1)
             lay.idx_block_table = np.pad(lay.idx_block_table, pad, constant_values=-1)
+        if max_batch is not None and max_batch > lay.block_table.shape[0]:
+            pad = ((0, max_batch - lay.block_table.shape[0]), (0, 0))
+            lay.block_table = np.pad(lay.block_table, pad, constant_values=-1)
+            lay.host_block_table = np.pad(lay.host_block_table, pad, constant_values=-1)
+            lay.idx_block_table = np.pad(lay.idx_block_table, pad, constant_values=-1)
+            lay.hot_blocks = np.pad(lay.hot_blocks, pad, constant_values=0)
         self.dev = torch.device(device)
         cfg = hsb.make_config(topk=wl.topk, kv_dtype=wl.kv_dtype, idx_dtype=wl.idx_dtype,
-                              n_layers=wl.n_layers, max_batch=wl.batch,
+                              n_layers=wl.n_layers, max_batch=lay.block_table.shape[0],
                               max_queries=max_queries or wl.queries,
                               max_pages_per_req=lay.block_table.shape[1], hot_rows_per_req=wl.hot_rows,
                               num_gpu_blocks=lay.num_gpu_blocks, num_idx_blocks=lay.num_idx_blocks,
