@@ -306,6 +306,22 @@ hs_status sparse_mla_prefill(hs_ctx* ctx, int32_t layer, int32_t b, const void* 
                              const int32_t* topk, int32_t L, int32_t P, float sm_scale, void* out,
                              float* lse, void* stream);
 
+/*
+ * sparse_mla_decode for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  Same arguments, kernels
+ * and results as sparse_mla_decode (bit for bit); its split-K partials live in a fixed scratch
+ * array compiled into the library, 512 (query, split) partials (about 64 MiB) per device, held
+ * by every device the library runs on until the process ends, instead of the bound workspace.
+ * The split rule never needs more than the array holds (fewer than 256 queries use at most
+ * 255 + queries partials; 256 queries or more use none); a call that would is refused with
+ * HS_ERR_INVALID_ARG.  Every call on one device shares that device's array: calls that overlap
+ * on one device (e.g. on two streams) race and must be ordered by the caller.  Allocates
+ * nothing, never synchronises; the array's address is taken once per device at hs_create.
+ */
+hs_status sparse_mla_decode_noalloc(hs_ctx* ctx, int32_t layer, const void* q,
+                                    const int32_t* row_ids, const int32_t* ctx_lens, int32_t B,
+                                    int32_t S, float sm_scale, void* out, float* lse, void* stream);
+
 /* Synchronise the context's device and read (then clear) the device error word. */
 hs_status hs_read_device_error(hs_ctx* ctx, int32_t* code);
 

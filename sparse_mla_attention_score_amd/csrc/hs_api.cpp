@@ -301,6 +301,7 @@ hs_status hs_create(const hs_config* cfg, hs_ctx** out) {
   if (e == hipSuccess) e = hs_set_kernel_attributes();
   if (e == hipSuccess) e = hs_resolve_set_attributes();
   if (e == hipSuccess) e = hs_select_set_attributes();
+  if (e == hipSuccess) e = hs_fixed_scratch_init(ctx->device);
   if (e != hipSuccess) {
     delete ctx;
     return hip_fail(e, "hs_create");
@@ -541,6 +542,33 @@ hs_status sparse_mla_prefill(hs_ctx* ctx, int32_t layer, int32_t b, const void* 
   hipError_t e = hs_launch_prefill_decode(ctx, layer, b, q, topk, L, P, sm_scale, out, lse,
                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "sparse_mla_prefill launch");
+}
+
+hs_status sparse_mla_decode_noalloc(hs_ctx* ctx, int32_t layer, const void* q,
+                                    const int32_t* row_ids, const int32_t* ctx_lens, int32_t B,
+                                    int32_t S, float sm_scale, void* out, float* lse, void* stream) {
+  hs_status s = check_step(ctx, B, S, "sparse_mla_decode_noalloc");
+  if (s != HS_OK) return s;
+  if (layer < 0 || layer >= ctx->cfg.n_layers)
+    return fail(HS_ERR_INVALID_ARG, "sparse_mla_decode_noalloc: layer %d outside [0, %d)", layer,
+                ctx->cfg.n_layers);
+  if (!std::isfinite(sm_scale)) return fail(HS_ERR_INVALID_ARG, "sparse_mla_decode_noalloc: sm_scale not finite");
+  if (B == 0) return ok();
+  if (!q || !row_ids || !ctx_lens || !out)
+    return fail(HS_ERR_INVALID_ARG, "sparse_mla_decode_noalloc: a pointer argument is NULL");
+  const int splits = hs_choose_splits(ctx, B, S);
+  const int64_t partials = splits > 1 ? (int64_t)B * S * splits : 0;
+  if (partials > hs::kFixedPartials)
+    return fail(HS_ERR_INVALID_ARG,
+                "sparse_mla_decode_noalloc: %d queries x %d splits need %lld split partials; the "
+                "fixed scratch holds %d", B * S, splits, (long long)partials, hs::kFixedPartials);
+  unsigned char* p = static_cast<unsigned char*>(hs_fixed_scratch(ctx->device));
+  if (!p) return fail(HS_ERR_STATE, "sparse_mla_decode_noalloc: no fixed scratch on device %d", ctx->device);
+  float* part_o = reinterpret_cast<float*>(p);
+  float* part_ml = reinterpret_cast<float*>(p + (size_t)hs::kFixedPartials * hs::kHeads * hs::kDv * 4);
+  hipError_t e = hs_launch_decode(ctx, layer, q, row_ids, ctx_lens, B, S, sm_scale, out, lse,
+                                  splits, static_cast<hipStream_t>(stream), part_o, part_ml);
+  return e == hipSuccess ? ok() : hip_fail(e, "sparse_mla_decode_noalloc launch");
 }
 
 hs_status hs_decode_splits(const hs_ctx* ctx, int32_t B, int32_t S, int32_t* splits) {

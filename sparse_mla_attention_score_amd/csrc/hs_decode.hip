@@ -27,6 +27,8 @@
 // Each wave computes S^T for its 32 heads on half the tile's rows and O^T for its 32 heads on
 // half the value dims over all the rows, on 32x32x16 bf16 MFMAs; the two waves of a head group
 // swap their row maxima and probabilities through LDS.
+#include <mutex>
+
 #include "hs_device.h"
 #include "hs_internal.h"
 
@@ -899,9 +901,38 @@ __global__ void prefill_rows_kernel(const int32_t* __restrict__ topk, int K, int
 }
 
 }  // namespace
+
+// Fixed scratch of sparse_mla_decode_noalloc, for callers that cannot allocate: the split-K
+// partials of up to kFixedPartials (query, split) pairs, the outputs [kFixedPartials][64][512]
+// fp32 first, then the (max, sum) pairs [kFixedPartials][64][2].  Host code never passes the
+// array's name to a kernel: it takes the device address from hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[(size_t)kFixedPartials * kHeads * (kDv + 2) * 4];
+
 }  // namespace hs
 
 using namespace hs;
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[hs::kMaxDevices] = {};
+}  // namespace
+
+hipError_t hs_fixed_scratch_init(int device) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device]) return hipSuccess;
+  void* p = nullptr;
+  hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(hs::scratch));
+  if (e != hipSuccess) return e;
+  g_scratch_ptr[device] = p;
+  return hipSuccess;
+}
+
+void* hs_fixed_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[device];
+}
 
 size_t hs_decode_lds_bytes(int) { return DecLds::kTotal; }
 
@@ -918,7 +949,10 @@ int hs_choose_splits(const hs_ctx* ctx, int B, int S) {
 
 hipError_t hs_launch_decode(const hs_ctx* ctx, int layer, const void* q, const int32_t* row_ids,
                             const int32_t* ctx_lens, int B, int S, float sm_scale, void* out,
-                            float* lse, int splits, hipStream_t stream) {
+                            float* lse, int splits, hipStream_t stream, float* part_o,
+                            float* part_ml) {
+  if (!part_o) part_o = ctx->ws.part_o;
+  if (!part_ml) part_ml = ctx->ws.part_ml;
   const hs_config& c = ctx->cfg;
   const int64_t n_rows_pool = c.num_gpu_blocks * kBlock;
   const uint8_t* kv = static_cast<const uint8_t*>(ctx->buf.kv_pool) +
@@ -931,13 +965,13 @@ hipError_t hs_launch_decode(const hs_ctx* ctx, int layer, const void* q, const i
     hipLaunchKernelGGL(sparse_mla_decode_fp8_kernel, grid, dim3(kF8Threads), 0, stream,
                        static_cast<const uint16_t*>(q), row_ids, ctx_lens, B, S, c.topk,
                        c.max_pages_per_req * kBlock, kv, n_rows_pool, qk_scale_log2, splits,
-                       xcd_map, static_cast<uint16_t*>(out), lse, ctx->ws.part_o, ctx->ws.part_ml,
+                       xcd_map, static_cast<uint16_t*>(out), lse, part_o, part_ml,
                        ctx->ws.zero_row, ctx->ws.err);
   else
     hipLaunchKernelGGL(sparse_mla_decode_kernel<false>, grid, dim3(kDecThreads), DecLds::kTotal, stream,
                        static_cast<const uint16_t*>(q), row_ids, ctx_lens, B, S, c.topk,
                        c.max_pages_per_req * kBlock, kv, n_rows_pool, qk_scale_log2, splits,
-                       xcd_map, static_cast<uint16_t*>(out), lse, ctx->ws.part_o, ctx->ws.part_ml,
+                       xcd_map, static_cast<uint16_t*>(out), lse, part_o, part_ml,
                        ctx->ws.err);
   hs_timer_mark(ctx, HS_KERNEL_DECODE, false, stream);
   hipError_t e = hipGetLastError();
@@ -946,13 +980,13 @@ hipError_t hs_launch_decode(const hs_ctx* ctx, int layer, const void* q, const i
   static_assert(kMaxSplits == 32, "merge shapes below cover up to 32 splits");
   if (splits > 8)
     hipLaunchKernelGGL((decode_merge_kernel<1, 4, 8>), dim3((unsigned)(B * S * kHeads)), dim3(kMergeThreads), 0,
-                       stream, ctx->ws.part_o, ctx->ws.part_ml, splits, static_cast<uint16_t*>(out), lse);
+                       stream, part_o, part_ml, splits, static_cast<uint16_t*>(out), lse);
   else if (splits > 2)
     hipLaunchKernelGGL((decode_merge_kernel<4, 1, 8>), dim3((unsigned)(B * S * kHeads / 4)), dim3(kMergeThreads), 0,
-                       stream, ctx->ws.part_o, ctx->ws.part_ml, splits, static_cast<uint16_t*>(out), lse);
+                       stream, part_o, part_ml, splits, static_cast<uint16_t*>(out), lse);
   else
     hipLaunchKernelGGL((decode_merge_kernel<4, 1, 2>), dim3((unsigned)(B * S * kHeads / 4)), dim3(kMergeThreads), 0,
-                       stream, ctx->ws.part_o, ctx->ws.part_ml, splits, static_cast<uint16_t*>(out), lse);
+                       stream, part_o, part_ml, splits, static_cast<uint16_t*>(out), lse);
   hs_timer_mark(ctx, HS_KERNEL_DECODE_MERGE, false, stream);
   return hipGetLastError();
 }

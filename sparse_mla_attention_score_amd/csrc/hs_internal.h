@@ -41,6 +41,11 @@ constexpr int kZeroRowBytes = 1024;  // >= one FP8 row (656 bytes)
 // Decode split-K.
 constexpr int kTileRows = 64;
 constexpr int kMaxSplits = 32;
+// sparse_mla_decode_noalloc: (query, split) partials the fixed scratch holds.  The split rule
+// (hs_choose_splits) keeps queries x splits below 256 + queries for fewer than 256 queries and
+// uses no partials from 256 queries on, so every call fits.
+constexpr int kFixedPartials = 512;
+constexpr int kMaxDevices = 64;
 
 // Pointers into the borrowed device workspace.
 struct Workspace {
@@ -126,7 +131,12 @@ hipError_t hs_launch_hot_release(const hs_ctx* ctx, const int32_t* reqs, int n, 
 hipError_t hs_launch_pool_give(const hs_ctx* ctx, const int32_t* blocks, int n, hipStream_t stream);
 hipError_t hs_launch_decode(const hs_ctx* ctx, int layer, const void* q, const int32_t* row_ids,
                             const int32_t* ctx_lens, int B, int S, float sm_scale, void* out,
-                            float* lse, int splits, hipStream_t stream);
+                            float* lse, int splits, hipStream_t stream, float* part_o = nullptr,
+                            float* part_ml = nullptr);
+// The fixed scratch of sparse_mla_decode_noalloc: its device address on `device`, taken once
+// with that device current (hs_create does it); nullptr before that.
+hipError_t hs_fixed_scratch_init(int device);
+void* hs_fixed_scratch(int device);
 int hs_choose_splits(const hs_ctx* ctx, int B, int S);
 hipError_t hs_launch_materialize(const hs_ctx* ctx, const int32_t* pages, int n, hipStream_t stream);
 hipError_t hs_launch_release(const hs_ctx* ctx, const int32_t* pages, int n, const int32_t* ctx_lens,

@@ -39,6 +39,7 @@ EXPORTED = ["hs_create", "hs_destroy", "hs_workspace_bytes", "hs_host_pool_bytes
             "hisparse_materialize_pages", "hisparse_release_pages", "hisparse_resolve_plan",
             "hs_hot_release", "hs_hot_pool_give", "hs_hot_pool_read",
             "hisparse_prefill_index_topk", "sparse_mla_prefill", "hs_measure_read_gbps",
+            "sparse_mla_decode_noalloc",
             "hs_status_string", "hs_last_error"]
 
 
@@ -103,6 +104,7 @@ def lib() -> ctypes.CDLL:
             "sparse_mla_prefill": [P, i32, i32, P, P, i32, i32, f32, P, P, P],
             "hs_measure_read_gbps": [P, ctypes.c_size_t, P, i32, ctypes.POINTER(ctypes.c_double)],
             "sparse_mla_decode": [P, i32, P, P, P, i32, i32, f32, P, P, P],
+            "sparse_mla_decode_noalloc": [P, i32, P, P, P, i32, i32, f32, P, P, P],
             "hs_read_device_error": [P, ctypes.POINTER(i32)],
             "hs_decode_splits": [P, i32, i32, ctypes.POINTER(i32)],
             "hs_select_paths": [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)],
@@ -232,6 +234,12 @@ def sparse_mla_decode(ctx: int, layer: int, q: int, row_ids: int, ctx_lens: int,
                       sm_scale: float, out: int, lse: int, stream: int) -> None:
     _check(lib().sparse_mla_decode(ctx, layer, q, row_ids, ctx_lens, B, S, sm_scale, out,
                                    lse or None, stream), "sparse_mla_decode")
+
+
+def sparse_mla_decode_noalloc(ctx: int, layer: int, q: int, row_ids: int, ctx_lens: int, B: int,
+                              S: int, sm_scale: float, out: int, lse: int, stream: int) -> None:
+    _check(lib().sparse_mla_decode_noalloc(ctx, layer, q, row_ids, ctx_lens, B, S, sm_scale, out,
+                                           lse or None, stream), "sparse_mla_decode_noalloc")
 
 
 def hs_read_device_error(ctx: int) -> int:
@@ -385,6 +393,12 @@ class Context:
         sparse_mla_prefill(self.ctx, layer, b, q.data_ptr(), topk.data_ptr() if topk is not None else 0,
                            L, q.shape[0], sm_scale, out.data_ptr(),
                            lse.data_ptr() if lse is not None else 0, self.stream())
+
+    def decode_noalloc(self, layer, q, row_ids, ctx_lens, sm_scale, out, lse=None) -> None:
+        B, S = q.shape[0], q.shape[1]
+        sparse_mla_decode_noalloc(self.ctx, layer, q.data_ptr(), row_ids.data_ptr(), ctx_lens.data_ptr(),
+                                  B, S, sm_scale, out.data_ptr(), lse.data_ptr() if lse is not None else 0,
+                                  self.stream())
 
     def device_error(self) -> int:
         return hs_read_device_error(self.ctx)
