@@ -381,6 +381,14 @@ def bench_prefill(torch, dev, P: int) -> dict:
         if rep:
             t_idx.append(e[0].elapsed_time(e[1]))
             t_att.append(e[1].elapsed_time(e[2]))
+    # one more pass with the library's per-kernel timing: where the prefill's time goes
+    ctx.kernel_timing(True)
+    torch.cuda.synchronize()
+    ctx.prefill_index_topk(0, qidx, w, P, topk)
+    ctx.prefill(0, 0, q, topk, P, scale, out, lse)
+    torch.cuda.synchronize()
+    kt = {k: (round(ms * 1e3, 1), n) for k, (ms, n) in ctx.kernel_times().items() if n}
+    ctx.kernel_timing(False)
     err = ctx.device_error()
     ctx.close()
     if err:
@@ -399,6 +407,7 @@ def bench_prefill(torch, dev, P: int) -> dict:
             "attention": {"algorithmic_flops": att_flops, "tflops": round(att_flops / (ms_att * 1e-3) / 1e12, 2),
                           "bound": "mfma", "peak_tflops": BF16_DENSE_TFLOPS,
                           "frac": round(att_flops / (ms_att * 1e-3) / (BF16_DENSE_TFLOPS * 1e12), 4)},
+            "kernels_us_total_launches": kt,
             "note": "indexer + top-K of every prompt token, then one layer of sparse MLA on the "
                     "decode kernel; run as groups of 4 tokens, 256 tokens per chunk"}
 
