@@ -18,8 +18,9 @@
 // with log-sum-exp, the same algebra as merging per-shard partial attention (part-2 page, "DCP"
 // section).
 //
-// FP8 rows (sparse_mla_decode_fp8_kernel, below): 8 waves = 4 groups of 16 heads x 2 halves of
-// the dims; tiles stay FP8 in LDS, double-buffered and filled by direct loads one tile ahead.
+// FP8 rows (sparse_mla_decode_fp8_kernel, below): 8 waves, 4 that score (QK and the softmax, 16
+// heads each) and 4 that accumulate (PV, 128 value dims each), working on consecutive tiles;
+// tiles stay FP8 in LDS, in a ring of three filled by direct loads one tile ahead.
 //
 // bf16 rows (sparse_mla_decode_kernel): 4 waves = 2 head groups (32 heads each) x 2 halves.  A
 // tile is gathered from HBM once (8-byte pieces of 8 rows per thread, coalesced along the row)
@@ -364,28 +365,29 @@ __global__ __launch_bounds__(kDecThreads) void sparse_mla_decode_kernel(
 // FP8 rows: tiles stay FP8 in LDS.
 //
 // A tile is fetched by direct global->LDS loads (16 bytes per lane; rows keep their stored
-// 656-byte pitch) one tile ahead of the tile being computed, so the gather's latency hides
-// behind the MFMAs and no registers hold rows in flight.  QK over the 512 nope dims runs on the
-// FP8 codes as stored (16x16x128 FP8 MFMAs, 32 bytes of a row per lane), the bf16 query carried
-// by two E4M3 parts with per-head power-of-two scales that together keep its 8 significant bits
-// (set up once per workgroup); the 64 rope dims stay bf16.  V^T is read with the transposing
-// 8-byte read (ds_read_b64_tr_b8: in each group of 16 lanes, lanes 2k and 2k+1 address the two
-// halves of a 16-byte segment of "row" k and lane r receives byte r of all eight segments), which
-// hands a lane the 8 rows of one value dim that its MFMA k-slots take, and converted to bf16
-// exactly for the PV product (the probabilities stay bf16: their FP8 parts would need scales per
-// 32 rows, which the output layout of QK does not group).  The rows behind the k-slots are
-// addressed in the order the probabilities come out of the QK result, so nothing is permuted in
-// memory.  The barrier that opens a tile waits for that tile's loads; the next tile's loads are
-// issued right after it, so no barrier waits for them.
+// 656-byte pitch) one tile ahead of the tile being computed, so no registers hold rows in
+// flight.  QK over the 512 nope dims runs on the FP8 codes as stored (16x16x128 FP8 MFMAs, 32
+// bytes of a row per lane), the bf16 query carried by two E4M3 parts with per-head power-of-two
+// scales that together keep its 8 significant bits (set up once per workgroup); the 64 rope dims
+// stay bf16.  V^T is read with the transposing 8-byte read (ds_read_b64_tr_b8: in each group of
+// 16 lanes, lanes 2k and 2k+1 address the two halves of a 16-byte segment of "row" k and lane r
+// receives byte r of all eight segments), which hands a lane the 8 rows of one value dim that its
+// MFMA k-slots take, and converted to bf16 exactly for the PV product (the probabilities stay
+// bf16: their FP8 parts would need scales per 32 rows, which the output layout of QK does not
+// group).  The rows behind the k-slots are addressed in the order the probabilities come out of
+// the QK result, so nothing is permuted in memory.
 //
-// Work split: for QK, wave (hb, rh) holds Q for heads 16 hb .. +15 over all 576 dims and scores
-// rows 32 rh .. +31 of the tile, so no partial scores cross waves; the two row halves of a head
-// group agree on the head's running maximum through LDS.  For PV, wave w accumulates O^T for
-// value dims 64 w .. +63 of all 64 heads, so each FP8 value of the tile is converted once; the
-// probabilities reach it through LDS, already in its B-operand layout (the QK result of lane
-// (head, g) is exactly the P fragment of that lane for that head block and row half).  Three
-// barriers per tile: tile landed (and the previous tile finished), maxima written,
-// probabilities written.  A wave stays under 256 registers, so two waves share each SIMD.
+// Work split (the waves specialise): score wave hb (0..3) holds Q for heads 16 hb .. +15 over
+// all 576 dims and scores all 64 rows of a tile, so it alone decides its heads' running maxima
+// (no exchange between waves) and writes the probabilities to LDS, already in the PV B-operand
+// layout (the QK result of lane (head, g) is exactly the P fragment of that lane for that head
+// block and 32-row k-step), with the factor by which the tile rescales O.  Value wave pw (0..3)
+// accumulates O^T for value dims 128 pw .. +127 of all 64 heads, so each FP8 value of a tile is
+// converted once.  The two kinds work on consecutive tiles through a ring of three tile buffers
+// (being loaded, being scored, being accumulated), so each SIMD holds one wave of each and their
+// MFMA and VALU work overlaps; one barrier per tile.  The score waves issue the tile loads (the
+// value waves hold the larger register state: O is 128 registers).  Each role runs a loop of its
+// own, so a wave keeps only its own role's registers, under 256, and two waves share each SIMD.
 constexpr int kF8RowChunks = kFp8Row / 16;                   // 41 pieces of 16 bytes per row
 constexpr int kF8TileBytes = kTileRows * kFp8Row;            // 41,984
 constexpr int kF8TileLoads = kTileRows * kF8RowChunks / 64;  // 41 wave-wide loads per tile
@@ -465,8 +467,8 @@ __device__ __forceinline__ f32x4 mfma_f8_16x16x128(const i32x8& a, const i32x8& 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, scale_b);
 }
 
-constexpr int kF8Threads = 512;  // 8 waves: QK 4 head groups x 2 row halves; PV 8 x 64 value dims
-constexpr int kF8Waves = kF8Threads / 64;
+constexpr int kF8Threads = 512;  // 8 waves: 4 score waves (QK + softmax), 4 value waves (PV)
+constexpr int kF8Bufs = 3;       // tile ring: scored, accumulated, loading
 constexpr float kNoMax = -1.0e30f;  // running maximum before any row (finite: exp2 of it is 0)
 
 __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
@@ -475,16 +477,16 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
     const uint8_t* __restrict__ kv, int64_t n_rows_pool, float qk_scale_log2, int splits,
     int xcd_map, uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml, const uint8_t* __restrict__ zero_row, int32_t* __restrict__ err) {
-  // two tiles of raw rows (distinct objects, one filled while the other is read)
-  __shared__ __align__(16) unsigned char tile_a[kF8TileBytes];
-  __shared__ __align__(16) unsigned char tile_b[kF8TileBytes];
-  __shared__ __align__(16) int32_t rids[kMaxTopk];  // this workgroup's row ids (-1: skipped)
-  __shared__ __align__(16) bf16x8 pls[2][4][64];    // P fragments: [row half][head group][lane]
-  __shared__ float smax[2][kHeads];                 // tile maximum per row half and head
-  __shared__ float lsum[2][kHeads];                 // row sums per row half and head
+  // the tile ring (distinct objects: one being loaded, one scored, one accumulated)
+  __shared__ __align__(16) unsigned char tiles[kF8Bufs][kF8TileBytes];
+  __shared__ __align__(16) int32_t rids[kMaxTopk];        // this workgroup's row ids (-1: skipped)
+  __shared__ __align__(16) float bias[kMaxTopk];          // 0 for a row in the softmax, -inf otherwise
+  __shared__ __align__(16) bf16x8 pls[2][2][4][64];       // P fragments: [tile parity][k-step][head block][lane]
+  __shared__ float alph[2][kHeads];                       // rescale of O before the tile, per head
+  __shared__ float lsum[kHeads];                          // final row sum per head
   // The tiles are written only by the asm loads: hand their addresses to asm so that the
   // compiler does not take them for never-written memory.
-  asm volatile("" : : "v"(tile_a), "v"(tile_b) : "memory");
+  asm volatile("" : : "v"(tiles) : "memory");
 
   const int per_req = S * splits;
   int b, r;
@@ -500,10 +502,11 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
   const int bj = b * S + j;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // QK: heads 16 hb .. +15, tile rows 32 rh .. +31.  PV: value dims 64 wave .. +63.  In the
-  // 16x16 MFMA layouts lane l works on head (16 x block) + l%16 and on rows / dims in groups of
-  // 4 selected by l/16.
-  const int hb = wave & 3, rh = wave >> 2;
+  // Score wave hb (0..3): heads 16 hb .. +15 over all 64 rows of a tile.  Value wave pw (0..3):
+  // value dims 128 pw .. +127 of all 64 heads.  In the 16x16 MFMA layouts lane l works on head
+  // (16 x block) + l%16 and on rows / dims in groups of 4 selected by l/16.
+  const bool scorer = wave < 4;
+  const int hb = wave & 3, pw = wave & 3;
   const int c16 = lane & 15, g = lane >> 4;
   const int head = 16 * hb + c16;
 
@@ -514,10 +517,10 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
   const int per = ((n + splits - 1) / splits + kTileRows - 1) / kTileRows * kTileRows;
   const int r0 = min(n, sp * per), r1 = min(n, r0 + per);
   const int nrows = r1 - r0;
+  const int ntiles = (nrows + kTileRows - 1) / kTileRows;
 
   // staged up to a whole tile (-1 past the range), so tile loads read them without bounds
-  const int nrows_pad = (nrows + kTileRows - 1) / kTileRows * kTileRows;
-  for (int i = tid; i < nrows_pad; i += kF8Threads) {
+  for (int i = tid; i < ntiles * kTileRows; i += kF8Threads) {
     int32_t v = -1;
     if (i < nrows) {
       v = row_ids[(int64_t)bj * K + r0 + i];
@@ -527,9 +530,10 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
       }
     }
     rids[i] = v;
+    bias[i] = v >= 0 ? 0.0f : -INFINITY;
   }
-  // Q^T for the nope dims, as the B operand of four FP8 k-steps of 128 dims (128 ks ..): lane
-  // group g holds dims 32 g .. +31 of the step for head `head`.  Each bf16 value q is carried by
+  // Score waves: Q^T for the nope dims as the B operand of four FP8 k-steps of 128 dims (lane
+  // group g holds dims 32 g .. +31 of the step for head `head`).  Each bf16 value q is carried by
   // two E4M3 parts: q 2^E = hi + lo / 16, with one power of two E per head and k-step that puts
   // the largest |q| in [128, 256).  hi keeps 4 significant bits, lo the next 4 of the remainder
   // (|remainder| <= half a step of hi), so hi + lo / 16 carries bf16's 8; the MFMA's per-column
@@ -538,7 +542,7 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
   i32x8 qh[4], ql[4];
   int q_sh[4];
   bf16x8 q_rope[2];
-  {
+  if (scorer) {
     const uint16_t* qp = q + ((int64_t)bj * kHeads + head) * kDqk;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -578,193 +582,235 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
     for (int kr = 0; kr < 2; ++kr)
       q_rope[kr] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 512 + 32 * kr + 8 * g));
   }
-  f32x4 o[4][4];  // O^T[value dim 64 wave + 16 db + 4 g + i][head 16 hg + c16] in o[db][hg][i]
+  // Value waves: O^T[value dim 128 pw + 16 db + 4 g + i][head 16 hg + c16] in o[db][hg][i]
+  f32x4 o[8][4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 8; ++db)
 #pragma unroll
     for (int hg = 0; hg < 4; ++hg) o[db][hg] = f32x4{};
-  float m_pv[4];  // running maximum of head 16 hg + c16 (log2 units), as every wave keeps it
-#pragma unroll
-  for (int hg = 0; hg < 4; ++hg) m_pv[hg] = kNoMax;
-  float m_qk = kNoMax, l_part = 0.0f;  // the same for `head`, and its partial row sum
+  float m_qk = kNoMax, l_part = 0.0f;  // score waves: running maximum of `head`, partial row sum
   // Q and the row ids are in before any tile load is issued, and the compiler knows it: its
   // waits for them would otherwise sit inside the tile loop and also drain the prefetch.  (The
   // empty asm takes the fragments, so their loads cannot sink below this point.)
+  if (scorer) {
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(qh[ks]), "+v"(ql[ks]));
-  asm volatile("" : "+v"(q_rope[0]), "+v"(q_rope[1]));
+    for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(qh[ks]), "+v"(ql[ks]));
+    asm volatile("" : "+v"(q_rope[0]), "+v"(q_rope[1]));
+  }
   wait_vmcnt<0>();
   asm volatile("" ::: "memory");
   __syncthreads();  // row ids staged
 
   // Loads of tile rows [t0, t0 + 64) of the range into LDS address `buf`: wave-wide load ins
   // covers the 64 consecutive 16-byte pieces ins*64 .. ins*64+63 of the tile; wave w issues
-  // w, w+8, ...
-  auto issue = [&](uint32_t buf, int t0) {
+  // w, w+8, ...  The row ids are read together before the first load is issued.
+  // The score waves issue the tile loads (the value waves hold the larger register state).
+  // Lane work of those loads, the same for every tile: wave-wide load i of score wave hb covers
+  // the 64 consecutive 16-byte pieces (4 i + hb) * 64 .. +63 of the tile (rows of 41 pieces);
+  // lane l takes the piece at position c = (4 i + hb) * 64 + l: row c / 41, stored at its
+  // swizzled place in the row.
+  constexpr int kLoaders = 4;
+  constexpr int kPer = (kF8TileLoads + kLoaders - 1) / kLoaders;
+  int row_l[kPer], off_l[kPer];
 #pragma unroll
-    for (int i = 0; i < (kF8TileLoads + kF8Waves - 1) / kF8Waves; ++i) {
-      const int ins = kF8Waves * i + wave;
+  for (int i = 0; i < kPer; ++i) {
+    const int c = min(kLoaders * i + hb, kF8TileLoads - 1) * 64 + lane;
+    row_l[i] = (c * 1599) >> 16;  // c / 41 for c < 2,688
+    off_l[i] = 16 * nope_swizzle(c - row_l[i] * kF8RowChunks, row_l[i]);
+  }
+  // Loads of tile rows [t0, t0 + 64) of the range into LDS address `buf`; the row ids are read
+  // together before the first load is issued.  A skipped row (id -1: past the range, or
+  // flagged) reads a row of zeros, so whatever the pool holds elsewhere cannot reach the
+  // products; its logit is masked as well.
+  auto issue = [&](uint32_t buf, int t0) {
+    int32_t rid_l[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) rid_l[i] = rids[t0 + row_l[i]];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int ins = kLoaders * i + hb;
       if (ins < kF8TileLoads) {
-        int c = ins * 64 + lane;
-        // recomputed per tile: hoisting the lane addresses out of the tile loop costs registers
-        asm volatile("" : "+v"(c));
-        const int row = (c * 1599) >> 16;  // c / 41 for c < 2,688
-        const int piece = c - row * kF8RowChunks;
-        // a skipped row (id -1: past the range, or flagged) reads a row of zeros, so whatever
-        // the pool holds elsewhere cannot reach the products; its logit is masked as well
-        const int32_t rid = rids[t0 + row];
-        const uint8_t* src = rid >= 0 ? kv + (int64_t)rid * kFp8Row + 16 * nope_swizzle(piece, row)
-                                      : zero_row + 16 * piece;
-        lds_load16(src, buf + ins * 1024);
+        const uint8_t* row = rid_l[i] >= 0 ? kv + (int64_t)rid_l[i] * kFp8Row : zero_row;
+        lds_load16(row + off_l[i], buf + ins * 1024);
       }
     }
   };
 
-  // Transposed V reads: lane group g takes the k-slots 8g .. 8g+7 of a 32-row k-step, which
-  // hold the rows the P fragments put there (rows 4g .. 4g+3 and 16+4g .. 16+4g+3 of the step).
-  // Rows 16+ of a step (kk8 >= 4) have their pieces swizzled: the wave's value dims 64 wave +
-  // 16 db .. +15 are piece 4 wave + db, found at piece (4 wave + db) ^ 8, i.e. 128 bytes later
-  // when bit 3 of the piece is clear (wave & 2 == 0) and 128 bytes earlier when it is set.
-  const int kk8 = (lane & 15) >> 1;
-  const int v_lane_off = (kk8 < 4 ? 4 * g + kk8 : 16 + 4 * g + (kk8 - 4)) * kFp8Row + 64 * wave + 8 * (lane & 1);
-  const int v_sw = kk8 >= 4 ? ((wave & 2) ? -128 : 128) : 0;
-
-  auto compute = [&](const unsigned char* buf, int t0) {
-    // ---- S^T = K Q^T for rows 32 rh + 16 mb + 4 g + i, head `head`: the nope part on the FP8
-    // codes as stored, times the row's scale, plus the rope part
-    f32x4 c[2], rsc[2];
-    bool ok[2][4];
+  // ---- score wave: S^T = K Q^T for rows 16 mb + 4 g + i of the tile, head `head` (the nope
+  // part on the FP8 codes as stored, times the row's scale, plus the rope part); the tile's
+  // maximum per head, the lazy rescale, P (times the row scale) as the B operands of the two PV
+  // k-steps, and the rescale factor the value waves apply before accumulating this tile
+  auto score = [&](const unsigned char* buf, int t0, int par) {
+    f32x4 c[4], rsc[4];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const unsigned char* kp = buf + (32 * rh + 16 * mb + c16) * kFp8Row + 32 * g;
-      c[mb] = f32x4{};
+    for (int mb = 0; mb < 4; ++mb) c[mb] = f32x4{};
+    // k-step by k-step over the four row blocks, so that consecutive MFMAs are independent
+    // and each k-step's key fragments are read while the previous k-step runs
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 4; ++ks) {
+      i32x8 k8[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
         // rows of odd blocks have bit 4 set: their pieces 8 ks + 2 g (+1) sit 8 pieces away
         const int kss = (mb & 1) ? (ks ^ 1) : ks;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(kp + 128 * kss);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(kp + 128 * kss + 16);
-        const i32x8 k8 = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        c[mb] = mfma_f8_16x16x128(k8, qh[ks], q_sh[ks], c[mb]);
-        c[mb] = mfma_f8_16x16x128(k8, ql[ks], q_sh[ks] - 4, c[mb]);
+        const unsigned char* kp = buf + (16 * mb + c16) * kFp8Row + 32 * g + 128 * kss;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(kp);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(kp + 16);
+        k8[mb] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
-      const int row0 = 32 * rh + 16 * mb + 4 * g;
-      const int4 rid4 = *reinterpret_cast<const int4*>(&rids[t0 + row0]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        rsc[mb][i] = *reinterpret_cast<const float*>(buf + (row0 + i) * kFp8Row + 640);
-        ok[mb][i] = row0 + i < nrows - t0 && (i == 0 ? rid4.x : i == 1 ? rid4.y : i == 2 ? rid4.z : rid4.w) >= 0;
-      }
+      for (int mb = 0; mb < 4; ++mb) c[mb] = mfma_f8_16x16x128(k8[mb], qh[ks], q_sh[ks], c[mb]);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) c[mb] = mfma_f8_16x16x128(k8[mb], ql[ks], q_sh[ks] - 4, c[mb]);
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int row0 = 16 * mb + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rsc[mb][i] = *reinterpret_cast<const float*>(buf + (row0 + i) * kFp8Row + 640);
       c[mb] *= rsc[mb];
+    }
 #pragma unroll
-      for (int kr = 0; kr < 2; ++kr) {
-        const unsigned char* rp = buf + (32 * rh + 16 * mb + c16) * kFp8Row + 512 + 64 * kr + 16 * g;
+    for (int kr = 0; kr < 2; ++kr)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const unsigned char* rp = buf + (16 * mb + c16) * kFp8Row + 512 + 64 * kr + 16 * g;
         c[mb] = mfma16x16x32(as_bf16x8(*reinterpret_cast<const u32x4*>(rp)), q_rope[kr], c[mb]);
       }
-    }
-    // ---- logits (log2 units; skipped rows -inf) and this row half's maximum of the head
+    // logits in log2 units; rows outside the softmax get -inf from their bias, so their
+    // probabilities below are exactly 0
     float tmax = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 4; ++mb) {
+      const f32x4 bs = *reinterpret_cast<const f32x4*>(&bias[t0 + 16 * mb + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        c[mb][i] = ok[mb][i] ? c[mb][i] * qk_scale_log2 : -INFINITY;
+        c[mb][i] = __builtin_fmaf(c[mb][i], qk_scale_log2, bs[i]);
         tmax = fmaxf(tmax, c[mb][i]);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    {
-      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+    }
+    {  // the head's maximum over the four lane groups
+      auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
       tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    if (g == 0) smax[rh][head] = tmax;
-    lds_barrier();
-    // ---- the running maximum only moves when it grows by more than 2^kLazyRescale; every wave
-    // applies the same rule to the same values, so all agree on each head's maximum
-    // (v_exp_f32: results below 2^-126 flush to 0, far below what a sum of probabilities
-    // <= 2^kLazyRescale can notice)
-#pragma unroll
-    for (int hg = 0; hg < 4; ++hg) {
-      const float t = fmaxf(smax[0][16 * hg + c16], smax[1][16 * hg + c16]);
-      if (t > m_pv[hg] + kLazyRescale) {
-        const float alpha = __builtin_amdgcn_exp2f(m_pv[hg] - t);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[db][hg] *= alpha;
-        m_pv[hg] = t;
-      }
+    // the running maximum only moves when it grows by more than 2^kLazyRescale (v_exp_f32:
+    // results below 2^-126 flush to 0, far below what a sum of probabilities <= 2^kLazyRescale
+    // can notice)
+    float alpha = 1.0f;
+    if (tmax > m_qk + kLazyRescale) {
+      alpha = __builtin_amdgcn_exp2f(m_qk - tmax);
+      l_part *= alpha;
+      m_qk = tmax;
     }
-    {
-      const float t = fmaxf(smax[0][head], smax[1][head]);
-      if (t > m_qk + kLazyRescale) {
-        l_part *= __builtin_amdgcn_exp2f(m_qk - t);
-        m_qk = t;
-      }
-    }
-    // ---- P (times the row scale) as the B operand of PV k-step rh, head group hb: k-slot 8g + e
-    // holds row 4g + e (e < 4) or 16 + 4g + e - 4 of the step, which is what this lane has
-    bf16x8 pb;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = ok[mb][i] ? __builtin_amdgcn_exp2f(c[mb][i] - m_qk) : 0.0f;
-        l_part += p;
-        pb[4 * mb + i] = (__bf16)(ok[mb][i] ? p * rsc[mb][i] : 0.0f);
-      }
-    pls[rh][hb][lane] = pb;
-    lds_barrier();
-    // ---- O^T += V^T P^T: 4 blocks of 16 value dims x 4 head groups x 2 k-steps of 32 rows
+    if (g == 0) alph[par][head] = alpha;
+    // k-step kk of the PV product: k-slot 8g + e holds row 32 kk + 4g + e (e < 4) or
+    // 32 kk + 16 + 4g + e - 4, i.e. blocks 2 kk and 2 kk + 1 of this lane
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const unsigned char* vp = buf + 32 * kk * kFp8Row + v_lane_off + v_sw;
+      bf16x8 pb;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int mb = 2 * kk + h;
+          const float p = __builtin_amdgcn_exp2f(c[mb][i] - m_qk);
+          l_part += p;
+          pb[4 * h + i] = (__bf16)(p * rsc[mb][i]);
+        }
+      pls[par][kk][hb][lane] = pb;
+    }
+  };
+
+  // Transposed V reads of a value wave: lane group g takes the k-slots 8g .. 8g+7 of a 32-row
+  // k-step, which hold the rows the P fragments put there (rows 4g .. 4g+3 and 16+4g .. 16+4g+3
+  // of the step).  The wave's value dims 128 pw + 16 db .. +15 are piece 8 pw + db; rows 16+ of
+  // a step (kk8 >= 4) have it at piece (8 pw + db) ^ 8, i.e. 128 bytes later when pw is even
+  // and 128 bytes earlier when it is odd.
+  const int kk8 = (lane & 15) >> 1;
+  const int v_lane_off = (kk8 < 4 ? 4 * g + kk8 : 16 + 4 * g + (kk8 - 4)) * kFp8Row + 128 * pw + 8 * (lane & 1) +
+                         (kk8 >= 4 ? ((pw & 1) ? -128 : 128) : 0);
+
+  // ---- value wave: O^T = alpha O^T + V^T P^T over the tile's two k-steps of 32 rows
+  auto accumulate = [&](const unsigned char* buf, int par) {
+    float a[4];
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) a[hg] = alph[par][16 * hg + c16];
+    if (__builtin_amdgcn_ballot_w64(a[0] != 1.0f || a[1] != 1.0f || a[2] != 1.0f || a[3] != 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int hg = 0; hg < 4; ++hg)
+          o[db][hg] *= a[hg];
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const unsigned char* vp = buf + 32 * kk * kFp8Row + v_lane_off;
       bf16x8 pv[4];
 #pragma unroll
-      for (int hg = 0; hg < 4; ++hg) pv[hg] = pls[kk][hg][lane];
+      for (int hg = 0; hg < 4; ++hg) pv[hg] = pls[par][kk][hg][lane];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < 8; ++db) {
         const u32x2 raw = lds_read_tr8(vp + 16 * db);
         const bf16x8 va = e4m3x8_to_bf16(raw[0], raw[1]);
 #pragma unroll
-        for (int hg = 0; hg < 4; ++hg) o[db][hg] = mfma16x16x32(va, pv[hg], o[db][hg]);
+        for (int hg = 0; hg < 4; ++hg)
+          o[db][hg] = mfma16x16x32(va, pv[hg], o[db][hg]);
       }
     }
   };
 
-  // Tile i of the range lives in tile_a (even i) or tile_b (odd i).  Once every wave has seen
-  // tile i land (and so has finished tile i - 1), tile i + 1 is loaded into the buffer tile
-  // i - 1 used, while tile i is computed.  (A third buffer, keeping two tiles in flight, was
-  // measured slower.)
-  auto step = [&](const unsigned char* cur, const unsigned char* nxt, int t0) {
-    wait_vmcnt<0>();  // this wave's loads of `cur` have landed
-    lds_barrier();    // ... and every other wave's; `nxt`, P and the maxima are free again
-    if (t0 + kTileRows < nrows) issue(lds_address(nxt), t0 + kTileRows);
-    compute(cur, t0);
-  };
-  if (nrows > 0) issue(lds_address(tile_a), 0);
-  for (int t0 = 0; t0 < nrows; t0 += 2 * kTileRows) {
-    step(tile_a, tile_b, t0);
-    if (t0 + kTileRows >= nrows) break;
-    step(tile_b, tile_a, t0 + kTileRows);
+  // Tile i lives in ring buffer i % 3.  Round k: after every wave has seen tile k land (and so
+  // has finished round k - 1), tile k + 1 is loaded into the buffer tile k - 2 used, the score
+  // waves score tile k while the value waves accumulate tile k - 1 (scored in round k - 1), so
+  // the two kinds of work share each SIMD.  One barrier per round; the two roles run loops of
+  // their own (the same number of rounds and barriers), so each keeps only its own registers.
+  auto ring = [&](int i) -> unsigned char* { return tiles[i]; };
+  if (scorer) {
+    if (ntiles > 0) issue(lds_address(tiles[0]), 0);
+    for (int k = 0; k <= ntiles; ++k) {
+      wait_vmcnt<0>();  // this wave's loads of tile k have landed
+      lds_barrier();    // ... and every other wave's; round k - 1 is done everywhere
+      if (k + 1 < ntiles) issue(lds_address(ring((k + 1) % kF8Bufs)), (k + 1) * kTileRows);
+      if (k < ntiles) score(ring(k % kF8Bufs), k * kTileRows, k & 1);
+    }
+  } else {
+    for (int k = 0; k <= ntiles; ++k) {
+      lds_barrier();
+      if (k >= 1) accumulate(ring((k - 1) % kF8Bufs), (k - 1) & 1);
+    }
   }
 
-  // ---- finish: the head's row sum over the 4 lane groups and the 2 row halves
-  float l_half = l_part + __shfl_xor(l_part, 16);
-  {
-    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_half), __float_as_uint(l_half), false, false);
-    l_half = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  // ---- finish: the score waves hold each head's running maximum and row sum (over the four
+  // lane groups); the value waves normalise
+  if (scorer) {
+    float l = l_part;
+    auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+    l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+    l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (g == 0) {
+      lsum[head] = l;
+      if (splits == 1) {
+        if (lse) lse[(int64_t)bj * kHeads + head] = (m_qk + log2f(l)) * 0.69314718055994531f;
+      } else {
+        const int64_t part = (int64_t)bj * splits + sp;
+        part_ml[(part * kHeads + head) * 2 + 0] = m_qk;
+        part_ml[(part * kHeads + head) * 2 + 1] = l;
+      }
+    }
   }
-  if (g == 0) lsum[rh][head] = l_half;
   __syncthreads();
-  float l_tot[4];
-#pragma unroll
-  for (int hg = 0; hg < 4; ++hg) l_tot[hg] = lsum[0][16 * hg + c16] + lsum[1][16 * hg + c16];
+  if (scorer) return;
   if (splits == 1) {
 #pragma unroll
     for (int hg = 0; hg < 4; ++hg) {
-      const float inv = l_tot[hg] > 0.0f ? 1.0f / l_tot[hg] : 0.0f;
-      uint16_t* op = out + ((int64_t)bj * kHeads + 16 * hg + c16) * kDv + 64 * wave + 4 * g;
+      const float l_tot = lsum[16 * hg + c16];
+      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+      uint16_t* op = out + ((int64_t)bj * kHeads + 16 * hg + c16) * kDv + 128 * pw + 4 * g;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < 8; ++db) {
         const __bf16 v0 = (__bf16)(o[db][hg][0] * inv), v1 = (__bf16)(o[db][hg][1] * inv);
         const __bf16 v2 = (__bf16)(o[db][hg][2] * inv), v3 = (__bf16)(o[db][hg][3] * inv);
         const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
@@ -773,23 +819,14 @@ __global__ __launch_bounds__(kF8Threads) void sparse_mla_decode_fp8_kernel(
                             ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
         *reinterpret_cast<u32x2*>(op + 16 * db) = u32x2{w0, w1};
       }
-      if (lse && g == 0 && wave == 0)
-        lse[(int64_t)bj * kHeads + 16 * hg + c16] = (m_pv[hg] + log2f(l_tot[hg])) * 0.69314718055994531f;
     }
-  } else {
+  } else if (nrows > 0) {
     const int64_t part = (int64_t)bj * splits + sp;
 #pragma unroll
     for (int hg = 0; hg < 4; ++hg) {
-      const int h = 16 * hg + c16;
-      if (g == 0 && wave == 0) {
-        part_ml[(part * kHeads + h) * 2 + 0] = m_pv[hg];
-        part_ml[(part * kHeads + h) * 2 + 1] = l_tot[hg];
-      }
-      if (nrows > 0) {
-        float* pp = part_o + (part * kHeads + h) * kDv + 64 * wave + 4 * g;
+      float* pp = part_o + (part * kHeads + 16 * hg + c16) * kDv + 128 * pw + 4 * g;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) *reinterpret_cast<f32x4*>(pp + 16 * db) = o[db][hg];
-      }
+      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(pp + 16 * db) = o[db][hg];
     }
   }
 }
