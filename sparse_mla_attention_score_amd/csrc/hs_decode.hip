@@ -403,34 +403,6 @@ __device__ __forceinline__ int nope_swizzle(int piece, int row) {
   return piece < 32 ? piece ^ (8 * ((row >> 4) & 1)) : piece;
 }
 
-// s_waitcnt vmcnt(N) (expcnt, lgkmcnt unconstrained), gfx9 encoding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier that waits for this wave's LDS traffic only (not for loads in flight).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15 | (3 << 14));  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// One wave-wide direct load: lane l's 16 bytes at `src` land at LDS byte address lds + 16 l.
-// Issued from asm on purpose: the compiler does not see these loads, so it adds no waits for
-// them in front of LDS reads it cannot prove disjoint (e.g. the transposing reads); the
-// kernel waits for them itself (wait_vmcnt, which only ever waits for more than the
-// compiler's own bookkeeping would, as vector-memory operations complete in order).  No other
-// instruction of the kernel uses m0.
-__device__ __forceinline__ void lds_load16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)p;
-}
-
 typedef int lds_i32x2 __attribute__((vector_size(8)));
 
 __device__ __forceinline__ u32x2 lds_read_tr8(const unsigned char* p) {

@@ -8,14 +8,18 @@
 // and the selection is the min(K, L_j) tokens ranked by (score desc, token asc), emitted in
 // ascending token order.
 //
-// Sweep: one workgroup scores 64 pages (4,096 tokens) of one request for all S queries; each
-// of its four waves streams 16 of the pages, so each page comes from HBM once.  The contraction
-// [S*32 heads x 128] x [128 x tokens] runs on bf16 MFMA (32x32x16): FP8 keys are converted to
-// bf16 exactly, the per-token fp32 scale is applied after the ReLU (positive scales commute
-// with it).  Lane l reads 64 contiguous key bytes of token l%32 (dims 64*(l/32) .. +64); the
-// 128 dims are assigned to MFMA k-slots in that order, and the query fragments read from LDS
-// use the same assignment.  Scores go to a per-(request, query) scratch row; their first radix
-// digit (bits [30:19]) is counted in LDS and added to a global histogram.
+// Sweep: a work item is 64 pages (4,096 tokens) of one request, scored for all S queries by one
+// workgroup, whose four waves stream 16 of the pages each, so each page comes from HBM once;
+// the workgroups stride over the batch's items, numbered densely from the context lengths.
+// The contraction [S*32 heads x 128] x [128 x tokens] runs on bf16 MFMA (32x32x16): FP8 keys
+// are converted to bf16 exactly, the per-token fp32 scale is applied after the ReLU (positive
+// scales commute with it).  Lane l holds 64 contiguous key bytes of token l%32 (dims
+// 64*(l/32) .. +64); the 128 dims are assigned to MFMA k-slots in that order, and the query
+// fragments read from LDS use the same assignment.  With three or four queries the lanes load
+// their key bytes straight into registers; with one or two the sweep is bound by the key
+// stream, and the key tiles come into LDS first, by direct loads of whole cache lines.  Scores
+// go to a per-(request, query) scratch row; their first radix digit (bits [30:19]) is counted
+// in LDS and added to a global histogram.
 //
 // Select: one workgroup per (request, query).  The histogram gives the threshold bin; one
 // pass over the scores (two rounds of loads in flight) marks the tokens above it in a bitmap
@@ -82,6 +86,8 @@ __device__ __forceinline__ bf16x8 key_operand(const KeyTile<kFp8>& kt, int s) {
 // as large and read the weights from LDS instead.  All of it fits two waves per SIMD.
 constexpr int kSweepThreads = 256;
 constexpr int kQRowBytes = kIdxDim * 2 + 16;
+constexpr int kSweepPrefix = 1024;   // batches up to this size number their items densely
+constexpr int kSweepGridCap = 512;   // workgroups of a dense sweep: two per CU, all resident
 
 template <int S, bool kFp8>
 __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
@@ -97,207 +103,332 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
   constexpr int kTilesPerWave = 2 * kPagesPerItem / 4;
   static_assert(kTilesPerWave % kRing == 0, "whole ring rounds");
   constexpr bool kWeightsInRegs = kFp8;
+  // With one or two queries (FP8 keys) the sweep is bound by the key stream, and key tiles go
+  // through LDS instead of registers (see the loop below); kLRing tiles per wave.
+  constexpr bool kLdsKeys = kFp8 && S <= 2;
+  constexpr int kLRing = S == 1 ? 3 : 2;
+  constexpr int kSlot = 32 * kIdxDim + 32 * 4;  // 32 tokens' codes, then their 32 scales
   // 16-bit LDS counters, two bins per word: one workgroup sees at most 4,096 tokens.
   __shared__ uint32_t lhist[S][kHistBins / 2];
   __shared__ __align__(16) float lw[S][kIdxHeads];  // half the head weights (see finish)
   __shared__ int32_t lblk[kPagesPerItem];
   __shared__ __align__(16) unsigned char lq[S * kIdxHeads * kQRowBytes];
+  __shared__ __align__(16) unsigned char lkeys[kLdsKeys ? kSweepWaves * kLRing * kSlot : 16];
+  __shared__ int32_t litem[kSweepPrefix];              // first item of each request
+  __shared__ int32_t llen[kSweepPrefix];               // context length of each request
+  __shared__ int lscan[kSweepThreads / 64 + 1];
 
-  const int b = blockIdx.x % B;
-  const int item = blockIdx.x / B;
-  const int L = ctx_lens[b];
-  if (L < S || L > max_pages * kBlock) {
-    if (item == 0 && threadIdx.x == 0) raise_error(err, HS_DEVERR_SHORT_CONTEXT);
-    return;
+  // Work items: item i of request b is its pages 64 i .. 64 i + 63.  With up to kSweepPrefix
+  // requests the items of the batch are numbered densely (every workgroup computes the prefix
+  // sum of the requests' item counts from the context lengths, which it keeps) and the grid,
+  // at most as many workgroups as stay resident, strides over them, so a batch of short and
+  // long contexts launches no workgroup without work; beyond that, item w is (request w % B,
+  // item w / B) and workgroups past a request's end exit at once.
+  const bool packed = B <= kSweepPrefix;
+  int total;
+  if (packed) {
+    int carry = 0;
+    for (int b0 = 0; b0 < B; b0 += kSweepThreads) {
+      const int bb = b0 + threadIdx.x;
+      int n = 0;
+      if (bb < B) {
+        const int Lb = ctx_lens[bb];
+        llen[bb] = Lb;
+        // a request whose length is out of range keeps one item, which flags it
+        n = (Lb < S || Lb > max_pages * kBlock) ? 1
+                                                : ((Lb + kBlock - 1) / kBlock + kPagesPerItem - 1) / kPagesPerItem;
+      }
+      int chunk;
+      const int ex = block_exclusive_scan<kSweepThreads>(n, lscan, &chunk);
+      if (bb < B) litem[bb] = carry + ex;
+      carry += chunk;
+    }
+    __syncthreads();
+    total = carry;
+  } else {
+    total = B * ((max_pages + kPagesPerItem - 1) / kPagesPerItem);
   }
-  const int n_pages = (L + kBlock - 1) / kBlock;
-  const int p_begin = item * kPagesPerItem;
-  if (p_begin >= n_pages) return;
-  const int p_end = min(n_pages, p_begin + kPagesPerItem);
+  for (int wi = blockIdx.x; wi < total; wi += gridDim.x) {
+    int b, item;
+    if (packed) {  // the last request whose first item is at or below wi
+      int lo = 0, hi = B - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (litem[mid] <= wi) lo = mid;
+        else hi = mid - 1;
+      }
+      b = lo;
+      item = wi - litem[lo];
+    } else {
+      b = wi % B;
+      item = wi / B;
+    }
+    const int L = packed ? llen[b] : ctx_lens[b];
+    if (L < S || L > max_pages * kBlock) {
+      if (item == 0 && threadIdx.x == 0) raise_error(err, HS_DEVERR_SHORT_CONTEXT);
+      continue;
+    }
+    const int n_pages = (L + kBlock - 1) / kBlock;
+    const int p_begin = item * kPagesPerItem;
+    if (p_begin >= n_pages) continue;
+    const int p_end = min(n_pages, p_begin + kPagesPerItem);
 
-  for (int i = threadIdx.x; i < S * kHistBins / 2; i += kSweepThreads) (&lhist[0][0])[i] = 0;
-  if (threadIdx.x < S * kIdxHeads)
-    (&lw[0][0])[threadIdx.x] = 0.5f * w[b * S * kIdxHeads + threadIdx.x];
-  if (threadIdx.x < kPagesPerItem) {
-    const int p = p_begin + threadIdx.x;
-    int32_t blk = -1;
-    if (p < p_end) {
-      blk = idx_block_table[(int64_t)b * table_stride + p];
-      if (blk < 0 || blk >= num_idx_blocks) {
-        raise_error(err, HS_DEVERR_BAD_BLOCK);
-        blk = -1;
+    for (int i = threadIdx.x; i < S * kHistBins / 2; i += kSweepThreads) (&lhist[0][0])[i] = 0;
+    if (threadIdx.x < S * kIdxHeads)
+      (&lw[0][0])[threadIdx.x] = 0.5f * w[b * S * kIdxHeads + threadIdx.x];
+    if (threadIdx.x < kPagesPerItem) {
+      const int p = p_begin + threadIdx.x;
+      int32_t blk = -1;
+      if (p < p_end) {
+        blk = idx_block_table[(int64_t)b * table_stride + p];
+        if (blk < 0 || blk >= num_idx_blocks) {
+          raise_error(err, HS_DEVERR_BAD_BLOCK);
+          blk = -1;
+        }
+      }
+      lblk[threadIdx.x] = blk;
+    }
+    // Q rows (query j, head h) of 128 bf16, 16-byte pieces
+    for (int i = threadIdx.x; i < S * kIdxHeads * 16; i += kSweepThreads) {
+      const int row = i >> 4, pc = i & 15;
+      *reinterpret_cast<u32x4*>(lq + row * kQRowBytes + 16 * pc) =
+          *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)b * S * kIdxHeads + row) * kIdxDim + 8 * pc);
+    }
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int half = lane >> 5, col = lane & 31;
+    // the request's score rows and candidate lists as buffer resources (sizes checked on the
+    // host to stay below 2^31 bytes); kOffEnd lies past both
+    constexpr uint32_t kOffEnd = 0x80000000u;
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        scores + (int64_t)b * S * lmax, (short)0, (int)(S * lmax * 4), kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        cands + (int64_t)b * S * n_seg * kSegCap, (short)0, S * n_seg * kSegCap * 8, kBufferRsrcWord3);
+    // candidate list: this wave's segment of each query's list, and the keys from which a token
+    // is listed (kGuessOff: none)
+    const int seg = item * kSweepWaves + wave;
+    uint32_t gq[S];
+    int cq[S];
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      gq[j] = guess[b * guess_stride + j];
+      cq[j] = 0;
+    }
+    __syncthreads();
+
+    // Tile k of this wave is half (k & 1) of page p_begin + wave + 4 * (k >> 1).  Tiles past the
+    // workgroup's pages (or on a bad block) read block 0 and are masked, so there are no branches
+    // around the loads and the prefetch ring stays in flight.
+    auto tile_src = [&](int k, int& t0) -> const uint8_t* {
+      const int rel = wave + 4 * (k >> 1);
+      const int32_t blk = lblk[rel];
+      t0 = blk >= 0 ? (p_begin + rel) * kBlock + (k & 1) * 32 : INT32_MAX / 2;
+      return idx_pool + (int64_t)(blk >= 0 ? blk : 0) * kBlkBytes;
+    };
+
+    // Weights lane (col, half) applies to query j: heads 8 g4 + 4 half .. +4, g4 = 0..3.
+    f32x4 wreg[kWeightsInRegs ? S : 1][4];
+    if constexpr (kWeightsInRegs) {
+#pragma unroll
+      for (int j = 0; j < S; ++j)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) wreg[j][g4] = *reinterpret_cast<const f32x4*>(&lw[j][8 * g4 + 4 * half]);
+    }
+    // LDS offsets of this lane's Q (and weight) reads.  They are made opaque again every tile:
+    // otherwise the loop-invariant reads are hoisted out of the loop, and all of Q does not fit
+    // the registers.
+    int q_off = col * kQRowBytes + 128 * half, w_off = half;
+
+    f32x16 acc[S];
+    float part[S];
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      acc[j] = f32x16{};
+      part[j] = 0.0f;
+    }
+    // Weighted ReLU sum of query j over the lane's 16 heads, then (after the second query of a
+    // pair, or a lone last query) the store and histogram update of token t.
+    // w * max(c, 0) == (w / 2) * (c + |c|): both factors are exact power-of-two rescalings, so
+    // the products round identically; c + |c| needs no NaN canonicalising.
+    auto finish = [&](int j, int t, float sc) {
+      float p = 0.0f;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 wv;
+        if constexpr (kWeightsInRegs) wv = wreg[j][g4];
+        else wv = reinterpret_cast<const f32x4*>(&lw[j][8 * g4])[w_off];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float c = acc[j][4 * g4 + i];
+          p = __builtin_fmaf(wv[i], c + __builtin_fabsf(c), p);
+        }
+      }
+      part[j] = p;
+      if ((j & 1) || j == S - 1) {
+        // Add the other half's 16 heads of the same token (lane l ^ 32).  The swap leaves the
+        // first query's total in lanes 0-31 and the second's in lanes 32-63, so one store and
+        // one histogram update serve both.
+        const int jp = j & ~1, jq = j;
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[jp]), __float_as_uint(part[jq]),
+                                                   false, false);
+        const float total = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * sc;
+        // scores are >= 0: clearing the sign bit maps -0 to +0
+        const uint32_t bits = __float_as_uint(total) & 0x7fffffffu;
+        const int jj = jp + half;
+        const bool vis = jj <= jq && (jq > jp || half == 0) && t < L - S + 1 + jj;
+        // No branch around a memory instruction in the loop: the stores are buffer stores whose
+        // lanes with nothing to store give an offset past the end (dropped by the hardware), so
+        // every iteration issues the same number of vector-memory instructions and the waits for
+        // the key ring count exactly the loads they need.  (Under a branch, the count differs
+        // between iterations and every wait has to drain all loads in flight.)  The histogram
+        // update adds zero for an invisible token.
+        const uint32_t soff = vis ? (uint32_t)(jj * lmax + t) * 4u : kOffEnd;
+        __builtin_amdgcn_raw_buffer_store_b32(bits, srs, soff, 0, 0);
+        const uint32_t bin = bits >> kHistShift;
+        atomicAdd(&lhist[jj][bin >> 1], vis ? 1u << (16 * (bin & 1)) : 0u);
+        // list the token for the next select if its key reaches the query's guess: lanes 0-31
+        // serve query jp, lanes 32-63 query jq; a lane's place is the number of listed lanes
+        // below it in its half
+        const bool cand = vis && bits >= (half ? gq[jq] : gq[jp]);
+        const uint64_t m = __ballot(cand);
+        const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+        const int pos = (half ? cq[jq] : cq[jp]) +
+                        (int)(half ? __builtin_amdgcn_mbcnt_hi(mhi, 0u) : __builtin_amdgcn_mbcnt_lo(mlo, 0u));
+        const uint32_t coff = cand && pos < kSegCap ? (uint32_t)((jj * n_seg + seg) * kSegCap + pos) * 8u : kOffEnd;
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{~(uint32_t)t, bits}, crs, coff, 0, 0);
+        cq[jp] += __popc(mlo);
+        if (jq > jp) cq[jq] += __popc(mhi);
+      }
+    };
+
+    if constexpr (kLdsKeys) {
+      // Key tiles through LDS: a tile comes in by direct loads of four contiguous 1 KB pieces of
+      // its 32 token rows (lane l of piece i fetches 16 bytes of token 8 i + l / 8) and its 32
+      // scales, so every load instruction covers whole cache lines.  A token's eight 16-byte
+      // chunks are stored XOR-swizzled by the token's low three bits, so that the reads below,
+      // one token per lane, fall on distinct banks.  The wave keeps kLRing tiles in flight in a
+      // ring of its own and waits for a tile by counting the vector-memory operations issued
+      // after its loads (every iteration issues the same ones: five loads, then the two stores of
+      // the scores and the candidate list).
+      asm volatile("" : : "v"(lkeys) : "memory");
+      unsigned char* myring = lkeys + wave * kLRing * kSlot;
+      auto issue_tile = [&](int k, unsigned char* slot) {
+        int t0u;
+        const uint8_t* blk = tile_src(k, t0u);
+        const uint8_t* codes = blk + (k & 1) * (32 * kIdxDim);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_address(slot));  // wave-uniform (m0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tk = 8 * i + (lane >> 3);
+          lds_load16(codes + tk * kIdxDim + 16 * ((lane & 7) ^ (tk & 7)), dst + 1024 * i);
+        }
+        if (lane < 32) lds_load4(blk + 64 * kIdxDim + (k & 1) * 128 + 4 * lane, dst + 32 * kIdxDim);
+      };
+      constexpr int kPerTile = 5, kStores = 2;
+      static_assert(S <= 2, "two stores per tile");
+      auto wait_tile = [&](int k) {
+        // operations issued after tile k's loads: in the steady state the stores of the iteration
+        // that issued them and kLRing - 1 whole iterations; at the start the later tiles of the
+        // prologue and the iterations so far
+        if (k >= kLRing) wait_vmcnt<kStores + (kLRing - 1) * (kPerTile + kStores)>();
+        else if (k == 0) wait_vmcnt<(kLRing - 1) * kPerTile>();
+        else if (k == 1) wait_vmcnt<(kLRing - 2) * kPerTile + (kPerTile + kStores)>();
+        else wait_vmcnt<(kLRing - 3 > 0 ? kLRing - 3 : 0) * kPerTile + 2 * (kPerTile + kStores)>();
+      };
+      static_assert(kLRing <= 3, "wait_tile covers rings of up to three tiles");
+#pragma unroll
+      for (int u = 0; u < kLRing; ++u) issue_tile(u, myring + u * kSlot);
+      for (int k = 0; k < kTilesPerWave; ++k) {
+        unsigned char* slot = myring + (k % kLRing) * kSlot;
+        wait_tile(k);
+        asm volatile("" : "+v"(q_off), "+v"(w_off));
+        u32x4 raw[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          raw[v] = *reinterpret_cast<const u32x4*>(slot + col * kIdxDim + 16 * ((4 * half + v) ^ (col & 7)));
+        const float scale = *reinterpret_cast<const float*>(slot + 32 * kIdxDim + 4 * col);
+        int t0k;
+        tile_src(k, t0k);
+        const int t = t0k + col;
+        bf16x8 kb[8];
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) kb[s8] = e4m3x8_to_bf16(raw[s8 / 2][(s8 % 2) * 2], raw[s8 / 2][(s8 % 2) * 2 + 1]);
+        // the slot's reads have returned before it is refilled with tile k + kLRing (the last
+        // iterations re-read the final tile, never scored)
+        wait_lgkmcnt0();
+        issue_tile(min(k + kLRing, kTilesPerWave - 1), slot);
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+          f32x16 a = {};
+#pragma unroll
+          for (int s8 = 0; s8 < 8; ++s8)
+            a = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(lq + q_off + j * kIdxHeads * kQRowBytes + 16 * s8)),
+                             kb[s8], a);
+          acc[j] = a;
+          if (j > 0) finish(j - 1, t, scale);
+        }
+        finish(S - 1, t, scale);
+      }
+      wait_vmcnt<0>();  // no load into LDS outlives the loop
+    } else {
+      // Slot u % kRing holds tile u from its load (issued once tile u - kRing is converted) until
+      // its own conversion.
+      KeyTile<kFp8> ring[kRing];
+      int ring_t0[kRing];
+#pragma unroll
+      for (int u = 0; u < kRing; ++u)
+        load_key_tile<kFp8>(ring[u], tile_src(u, ring_t0[u]), (u & 1) * 32 + col, half);
+
+      // Each query's weighted ReLU sum runs beside the next query's MFMA chain; the last one ends
+      // the tile.  A slot's key codes are refilled right after its conversion, its scale only once
+      // the tile's last sum has used the old one: no value of a slot lives across the refill, so
+      // the loop carries no register copies of loads in flight (a copy would make the loop wait
+      // for the load).
+      for (int k0 = 0; k0 < kTilesPerWave; k0 += kRing) {
+#pragma unroll
+        for (int u = 0; u < kRing; ++u) {
+          const int k = k0 + u;
+          const int t = ring_t0[u] + col;
+          asm volatile("" : "+v"(q_off), "+v"(w_off));
+          bf16x8 kb[8];
+#pragma unroll
+          for (int s = 0; s < 8; ++s) kb[s] = key_operand<kFp8>(ring[u], s);
+          // refill the slot with tile k + kRing (the last round re-reads the final tile, masked
+          // by never being scored)
+          const int kn = min(k + kRing, kTilesPerWave - 1);
+          const uint8_t* src = tile_src(kn, ring_t0[u]);
+          const int o_next = (kn & 1) * 32 + col;
+          load_key_codes<kFp8>(ring[u], src, o_next, half);
+#pragma unroll
+          for (int j = 0; j < S; ++j) {
+            // A operand of k-step s for query j: Q[j][head = col][dims 64*half + 8*s .. +8]
+            f32x16 a = {};
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+              a = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(lq + q_off + j * kIdxHeads * kQRowBytes + 16 * s)),
+                               kb[s], a);
+            acc[j] = a;
+            if (j > 0) finish(j - 1, t, ring[u].scale);
+          }
+          finish(S - 1, t, ring[u].scale);
+          load_key_scale<kFp8>(ring[u], src, o_next);
+        }
       }
     }
-    lblk[threadIdx.x] = blk;
-  }
-  // Q rows (query j, head h) of 128 bf16, 16-byte pieces
-  for (int i = threadIdx.x; i < S * kIdxHeads * 16; i += kSweepThreads) {
-    const int row = i >> 4, pc = i & 15;
-    *reinterpret_cast<u32x4*>(lq + row * kQRowBytes + 16 * pc) =
-        *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)b * S * kIdxHeads + row) * kIdxDim + 8 * pc);
-  }
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int half = lane >> 5, col = lane & 31;
-  // the request's score rows and candidate lists as buffer resources (sizes checked on the
-  // host to stay below 2^31 bytes); kOffEnd lies past both
-  constexpr uint32_t kOffEnd = 0x80000000u;
-  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      scores + (int64_t)b * S * lmax, (short)0, (int)(S * lmax * 4), kBufferRsrcWord3);
-  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
-      cands + (int64_t)b * S * n_seg * kSegCap, (short)0, S * n_seg * kSegCap * 8, kBufferRsrcWord3);
-  // candidate list: this wave's segment of each query's list, and the keys from which a token
-  // is listed (kGuessOff: none)
-  const int seg = item * kSweepWaves + wave;
-  uint32_t gq[S];
-  int cq[S];
+    if (lane == 0) {
 #pragma unroll
-  for (int j = 0; j < S; ++j) {
-    gq[j] = guess[b * guess_stride + j];
-    cq[j] = 0;
-  }
-  __syncthreads();
-
-  // Tile k of this wave is half (k & 1) of page p_begin + wave + 4 * (k >> 1).  Tiles past the
-  // workgroup's pages (or on a bad block) read block 0 and are masked, so there are no branches
-  // around the loads and the prefetch ring stays in flight.
-  auto tile_src = [&](int k, int& t0) -> const uint8_t* {
-    const int rel = wave + 4 * (k >> 1);
-    const int32_t blk = lblk[rel];
-    t0 = blk >= 0 ? (p_begin + rel) * kBlock + (k & 1) * 32 : INT32_MAX / 2;
-    return idx_pool + (int64_t)(blk >= 0 ? blk : 0) * kBlkBytes;
-  };
-
-  // Weights lane (col, half) applies to query j: heads 8 g4 + 4 half .. +4, g4 = 0..3.
-  f32x4 wreg[kWeightsInRegs ? S : 1][4];
-  if constexpr (kWeightsInRegs) {
-#pragma unroll
-    for (int j = 0; j < S; ++j)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) wreg[j][g4] = *reinterpret_cast<const f32x4*>(&lw[j][8 * g4 + 4 * half]);
-  }
-  // LDS offsets of this lane's Q (and weight) reads.  They are made opaque again every tile:
-  // otherwise the loop-invariant reads are hoisted out of the loop, and all of Q does not fit
-  // the registers.
-  int q_off = col * kQRowBytes + 128 * half, w_off = half;
-
-  // Slot u % kRing holds tile u from its load (issued once tile u - kRing is converted) until
-  // its own conversion.
-  KeyTile<kFp8> ring[kRing];
-  int ring_t0[kRing];
-#pragma unroll
-  for (int u = 0; u < kRing; ++u)
-    load_key_tile<kFp8>(ring[u], tile_src(u, ring_t0[u]), (u & 1) * 32 + col, half);
-
-  f32x16 acc[S];
-  float part[S];
-#pragma unroll
-  for (int j = 0; j < S; ++j) {
-    acc[j] = f32x16{};
-    part[j] = 0.0f;
-  }
-  // Weighted ReLU sum of query j over the lane's 16 heads, then (after the second query of a
-  // pair, or a lone last query) the store and histogram update of token t.
-  // w * max(c, 0) == (w / 2) * (c + |c|): both factors are exact power-of-two rescalings, so
-  // the products round identically; c + |c| needs no NaN canonicalising.
-  auto finish = [&](int j, int t, float sc) {
-    float p = 0.0f;
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      f32x4 wv;
-      if constexpr (kWeightsInRegs) wv = wreg[j][g4];
-      else wv = reinterpret_cast<const f32x4*>(&lw[j][8 * g4])[w_off];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float c = acc[j][4 * g4 + i];
-        p = __builtin_fmaf(wv[i], c + __builtin_fabsf(c), p);
-      }
+      for (int j = 0; j < S; ++j) seg_count[(int64_t)(b * S + j) * n_seg + seg] = (uint32_t)cq[j];
     }
-    part[j] = p;
-    if ((j & 1) || j == S - 1) {
-      // Add the other half's 16 heads of the same token (lane l ^ 32).  The swap leaves the
-      // first query's total in lanes 0-31 and the second's in lanes 32-63, so one store and
-      // one histogram update serve both.
-      const int jp = j & ~1, jq = j;
-      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[jp]), __float_as_uint(part[jq]),
-                                                 false, false);
-      const float total = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * sc;
-      // scores are >= 0: clearing the sign bit maps -0 to +0
-      const uint32_t bits = __float_as_uint(total) & 0x7fffffffu;
-      const int jj = jp + half;
-      const bool vis = jj <= jq && (jq > jp || half == 0) && t < L - S + 1 + jj;
-      // No branch around a memory instruction in the loop: the stores are buffer stores whose
-      // lanes with nothing to store give an offset past the end (dropped by the hardware), so
-      // every iteration issues the same number of vector-memory instructions and the waits for
-      // the key ring count exactly the loads they need.  (Under a branch, the count differs
-      // between iterations and every wait has to drain all loads in flight.)  The histogram
-      // update adds zero for an invisible token.
-      const uint32_t soff = vis ? (uint32_t)(jj * lmax + t) * 4u : kOffEnd;
-      __builtin_amdgcn_raw_buffer_store_b32(bits, srs, soff, 0, 0);
-      const uint32_t bin = bits >> kHistShift;
-      atomicAdd(&lhist[jj][bin >> 1], vis ? 1u << (16 * (bin & 1)) : 0u);
-      // list the token for the next select if its key reaches the query's guess: lanes 0-31
-      // serve query jp, lanes 32-63 query jq; a lane's place is the number of listed lanes
-      // below it in its half
-      const bool cand = vis && bits >= (half ? gq[jq] : gq[jp]);
-      const uint64_t m = __ballot(cand);
-      const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
-      const int pos = (half ? cq[jq] : cq[jp]) +
-                      (int)(half ? __builtin_amdgcn_mbcnt_hi(mhi, 0u) : __builtin_amdgcn_mbcnt_lo(mlo, 0u));
-      const uint32_t coff = cand && pos < kSegCap ? (uint32_t)((jj * n_seg + seg) * kSegCap + pos) * 8u : kOffEnd;
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2{~(uint32_t)t, bits}, crs, coff, 0, 0);
-      cq[jp] += __popc(mlo);
-      if (jq > jp) cq[jq] += __popc(mhi);
+    __syncthreads();
+    for (int i = threadIdx.x; i < S * kHistBins / 2; i += kSweepThreads) {
+      const uint32_t v = (&lhist[0][0])[i];
+      if (v == 0) continue;
+      const int j = i / (kHistBins / 2), pair = i % (kHistBins / 2);
+      uint32_t* g = hist + (int64_t)(b * S + j) * kHistBins + 2 * pair;
+      if (v & 0xffffu) atomicAdd(g, v & 0xffffu);
+      if (v >> 16) atomicAdd(g + 1, v >> 16);
     }
-  };
-
-  // Each query's weighted ReLU sum runs beside the next query's MFMA chain; the last one ends
-  // the tile.  A slot's key codes are refilled right after its conversion, its scale only once
-  // the tile's last sum has used the old one: no value of a slot lives across the refill, so
-  // the loop carries no register copies of loads in flight (a copy would make the loop wait
-  // for the load).
-  for (int k0 = 0; k0 < kTilesPerWave; k0 += kRing) {
-#pragma unroll
-    for (int u = 0; u < kRing; ++u) {
-      const int k = k0 + u;
-      const int t = ring_t0[u] + col;
-      asm volatile("" : "+v"(q_off), "+v"(w_off));
-      bf16x8 kb[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) kb[s] = key_operand<kFp8>(ring[u], s);
-      // refill the slot with tile k + kRing (the last round re-reads the final tile, masked
-      // by never being scored)
-      const int kn = min(k + kRing, kTilesPerWave - 1);
-      const uint8_t* src = tile_src(kn, ring_t0[u]);
-      const int o_next = (kn & 1) * 32 + col;
-      load_key_codes<kFp8>(ring[u], src, o_next, half);
-#pragma unroll
-      for (int j = 0; j < S; ++j) {
-        // A operand of k-step s for query j: Q[j][head = col][dims 64*half + 8*s .. +8]
-        f32x16 a = {};
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-          a = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(lq + q_off + j * kIdxHeads * kQRowBytes + 16 * s)),
-                           kb[s], a);
-        acc[j] = a;
-        if (j > 0) finish(j - 1, t, ring[u].scale);
-      }
-      finish(S - 1, t, ring[u].scale);
-      load_key_scale<kFp8>(ring[u], src, o_next);
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int j = 0; j < S; ++j) seg_count[(int64_t)(b * S + j) * n_seg + seg] = (uint32_t)cq[j];
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < S * kHistBins / 2; i += kSweepThreads) {
-    const uint32_t v = (&lhist[0][0])[i];
-    if (v == 0) continue;
-    const int j = i / (kHistBins / 2), pair = i % (kHistBins / 2);
-    uint32_t* g = hist + (int64_t)(b * S + j) * kHistBins + 2 * pair;
-    if (v & 0xffffu) atomicAdd(g, v & 0xffffu);
-    if (v >> 16) atomicAdd(g + 1, v >> 16);
+    __syncthreads();  // the item's shared state is free for the next one
   }
 }
 
@@ -863,7 +994,9 @@ template <int S, bool kFp8>
 hipError_t launch_scores(const hs_ctx* ctx, const IndexCall& a, hipStream_t stream) {
   const hs_config& c = ctx->cfg;
   const int items = (c.max_pages_per_req + kPagesPerItem - 1) / kPagesPerItem;
-  dim3 grid((unsigned)(a.B * items)), block(kSweepThreads);
+  int64_t n_wg = (int64_t)a.B * items;
+  if (a.B <= kSweepPrefix && n_wg > kSweepGridCap) n_wg = kSweepGridCap;
+  dim3 grid((unsigned)n_wg), block(kSweepThreads);
   hs_timer_mark(ctx, HS_KERNEL_INDEX_SCORE, true, stream);
   hipLaunchKernelGGL((index_score_kernel<S, kFp8>), grid, block, 0, stream,
                      static_cast<const uint16_t*>(a.q_idx), a.w, a.ctx_lens,
