@@ -273,7 +273,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "fp8+bf16",
         "dtype_detail": {
-            "indexer": "FP8 E4M3 MFMA over the keys as stored; the bf16 query as two exact E4M3 parts under a per-head power-of-two scale; fp32 accumulate and weighted ReLU sum",
+            "indexer": "bf16 MFMA over FP8 E4M3 keys converted to bf16 exactly; fp32 accumulate and weighted ReLU sum",
             "attention_qk_nope": "FP8 E4M3 MFMA; the bf16 query as two exact E4M3 parts under a per-head power-of-two scale; fp32 accumulate",
             "attention_qk_rope_and_pv": "bf16 MFMA, fp32 accumulate",
             "softmax": "fp32", "outputs": "bf16 (lse fp32)"},

@@ -11,13 +11,11 @@
 // Sweep: a work item is 64 pages (4,096 tokens) of one request, scored for all S queries by one
 // workgroup, whose four waves stream 16 of the pages each, so each page comes from HBM once;
 // the workgroups stride over the batch's items, numbered densely from the context lengths.
-// The contraction [S*32 heads x 128] x [128 x tokens] runs on MFMAs.  FP8 keys: on 32x32x64
-// FP8 MFMAs with the keys as stored and the bf16 query as two exact E4M3 parts under a
-// per-(head, k-step) power-of-two scale (two MFMAs per k-step); bf16 keys: on 32x32x16 bf16
-// MFMAs.  The per-token fp32 scale is applied after the ReLU (positive scales commute with it).
-// Lane l holds 64 contiguous key bytes of token l%32 (dims 64*(l/32) .. +64); the 128 dims are
-// assigned to MFMA k-slots in that order, and the query fragments read from LDS use the same
-// assignment.  With three or four queries the lanes load
+// The contraction [S*32 heads x 128] x [128 x tokens] runs on bf16 MFMA (32x32x16): FP8 keys
+// are converted to bf16 exactly, the per-token fp32 scale is applied after the ReLU (positive
+// scales commute with it).  Lane l holds 64 contiguous key bytes of token l%32 (dims
+// 64*(l/32) .. +64); the 128 dims are assigned to MFMA k-slots in that order, and the query
+// fragments read from LDS use the same assignment.  With three or four queries the lanes load
 // their key bytes straight into registers; with one or two the sweep is bound by the key
 // stream, and the key tiles come into LDS first, by direct loads of whole cache lines.  Scores
 // go to a per-(request, query) scratch row; their first radix digit (bits [30:19]) is counted
