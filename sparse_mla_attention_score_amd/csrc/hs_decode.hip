@@ -411,6 +411,27 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const unsigned char* p) {
   return u32x2{(uint32_t)v[0], (uint32_t)v[1]};
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Four floats (|x| < 448) -> their OCP E4M3 codes, rounded to nearest even, one per byte
+// (element e in byte e); *v gets the values the codes stand for.
+__device__ __forceinline__ uint32_t pack_e4m3x4(const float* x, float* v) {
+  i16x2 w = {0, 0};
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x[0], x[1], 1.0f, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x[2], x[3], 1.0f, true);
+  const uint32_t code = (uint32_t)__builtin_bit_cast(int, w);
+  const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)code, 1.0f, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)code, 1.0f, true);
+  v[0] = lo[0];
+  v[1] = lo[1];
+  v[2] = hi[0];
+  v[3] = hi[1];
+  return code;
+}
+
 // C += A B^T-style 16x16x128 product of E4M3 operands, B scaled by 2^(scale_b - 127) (one
 // E8M0 scale per column of B).  Lane l holds A[l%16][32(l/16) .. +32] and B[32(l/16) .. +32][l%16],
 // byte j of its eight dwords being element j; c[i] = C[4(l/16)+i][l%16].

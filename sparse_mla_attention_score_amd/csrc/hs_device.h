@@ -40,35 +40,6 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-
-typedef short i16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// Four floats (|x| < 448) -> their OCP E4M3 codes, rounded to nearest even, one per byte
-// (element e in byte e); *v gets the values the codes stand for.
-__device__ __forceinline__ uint32_t pack_e4m3x4(const float* x, float* v) {
-  i16x2 w = {0, 0};
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x[0], x[1], 1.0f, false);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x[2], x[3], 1.0f, true);
-  const uint32_t code = (uint32_t)__builtin_bit_cast(int, w);
-  const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)code, 1.0f, false);
-  const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)code, 1.0f, true);
-  v[0] = lo[0];
-  v[1] = lo[1];
-  v[2] = hi[0];
-  v[3] = hi[1];
-  return code;
-}
-
-// C += A(32x64) * B(64x32) of E4M3 operands, A scaled by 2^(scale_a - 127) (one E8M0 scale per
-// lane: its 32 K-values of one row; the two lanes of a row must pass the same).  Lane l holds
-// A[l%32][32(l/32) .. +32] and B[32(l/32) .. +32][l%32], byte j of its eight dwords being
-// element j; c[i] is C[8(i/4) + 4(l/32) + i%4][l%32].
-__device__ __forceinline__ f32x16 mfma_f8_32x32x64(const i32x8& a, const i32x8& b, int scale_a, f32x16 c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, 127);
-}
-
 // Byte permute of the 64-bit value {hi:lo}: selector byte k picks byte sel_k of it.
 __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);

@@ -113,7 +113,6 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
   __shared__ __align__(16) float lw[S][kIdxHeads];  // half the head weights (see finish)
   __shared__ int32_t lblk[kPagesPerItem];
   __shared__ __align__(16) unsigned char lq[S * kIdxHeads * kQRowBytes];
-  __shared__ int lqs[kFp8 ? S * kIdxHeads * 2 : 1];  // FP8 keys: E8M0 scale of each row's two k-steps
   __shared__ __align__(16) unsigned char lkeys[kLdsKeys ? kSweepWaves * kLRing * kSlot : 16];
   __shared__ int32_t litem[kSweepPrefix];              // first item of each request
   __shared__ int32_t llen[kSweepPrefix];               // context length of each request
@@ -189,57 +188,11 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
       }
       lblk[threadIdx.x] = blk;
     }
-    if constexpr (kFp8) {
-      // Q rows (query j, head h) as two E4M3 parts: q 2^E = hi + lo / 16 (bytes 0-127 hi, 128-255
-      // lo, in dim order), with one power of two E per row and k-step that puts the largest |q|
-      // of the step in [128, 256); hi keeps 4 significant bits and lo the next 4 of the
-      // remainder, so hi + lo / 16 carries bf16's 8 (the same split as the decode's query).
-      // K-step ks covers dims 32 ks .. +31 and 64 + 32 ks .. +31 (the MFMA's two lane halves).
-      for (int i = threadIdx.x; i < S * kIdxHeads * 2; i += kSweepThreads) {
-        const int row = i >> 1, ks = i & 1;
-        const uint16_t* qp = q_idx + ((int64_t)b * S * kIdxHeads + row) * kIdxDim;
-        float x[64];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const u32x4 wv = *reinterpret_cast<const u32x4*>(qp + 64 * hh + 32 * ks + 8 * v);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              x[32 * hh + 8 * v + 2 * e] = __uint_as_float(wv[e] << 16);
-              x[32 * hh + 8 * v + 2 * e + 1] = __uint_as_float(wv[e] & 0xFFFF0000u);
-            }
-          }
-        float m = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 64; ++e) m = fmaxf(m, fabsf(x[e]));
-        int E = 0;
-        if (m > 0.0f) E = 7 - ((int)((__float_as_uint(m) >> 23) & 255) - 127);
-        E = max(-120, min(E, 120));
-        const float sc = __builtin_ldexpf(1.0f, E);
-        unsigned char* qr = lq + row * kQRowBytes;
-#pragma unroll
-        for (int w4 = 0; w4 < 16; ++w4) {
-          float xs[4], hv[4], rr[4], lv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) xs[e] = x[4 * w4 + e] * sc;
-          const uint32_t hi = pack_e4m3x4(xs, hv);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) rr[e] = (xs[e] - hv[e]) * 16.0f;  // exact: |xs - hv| <= half a step
-          const uint32_t lo = pack_e4m3x4(rr, lv);
-          const int dim = 64 * (w4 >> 3) + 32 * ks + 4 * (w4 & 7);
-          *reinterpret_cast<uint32_t*>(qr + dim) = hi;
-          *reinterpret_cast<uint32_t*>(qr + 128 + dim) = lo;
-        }
-        lqs[i] = 127 - E;  // the lo part's scale is 2^-4 of it
-      }
-    } else {
-      // Q rows (query j, head h) of 128 bf16, 16-byte pieces
-      for (int i = threadIdx.x; i < S * kIdxHeads * 16; i += kSweepThreads) {
-        const int row = i >> 4, pc = i & 15;
-        *reinterpret_cast<u32x4*>(lq + row * kQRowBytes + 16 * pc) =
-            *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)b * S * kIdxHeads + row) * kIdxDim + 8 * pc);
-      }
+    // Q rows (query j, head h) of 128 bf16, 16-byte pieces
+    for (int i = threadIdx.x; i < S * kIdxHeads * 16; i += kSweepThreads) {
+      const int row = i >> 4, pc = i & 15;
+      *reinterpret_cast<u32x4*>(lq + row * kQRowBytes + 16 * pc) =
+          *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)b * S * kIdxHeads + row) * kIdxDim + 8 * pc);
     }
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -284,10 +237,7 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
     // LDS offsets of this lane's Q (and weight) reads.  They are made opaque again every tile:
     // otherwise the loop-invariant reads are hoisted out of the loop, and all of Q does not fit
     // the registers.
-    int q_off = col * kQRowBytes + (kFp8 ? 64 : 128) * half, w_off = half;
-    // FP8 keys: the scales of this lane's row for the two k-steps of query j (read from LDS at
-    // each use: held in registers they would cost the kernel its second wave per SIMD)
-    auto qsc = [&](int j, int ks) -> int { return lqs[(j * kIdxHeads + col) * 2 + ks]; };
+    int q_off = col * kQRowBytes + 128 * half, w_off = half;
 
     f32x16 acc[S];
     float part[S];
@@ -400,12 +350,9 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
         int t0k;
         tile_src(k, t0k);
         const int t = t0k + col;
-        // B operands of the two FP8 k-steps: the lane's token codes 32 ks .. 32 ks + 31 of its 64
-        i32x8 kf[2];
+        bf16x8 kb[8];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          kf[ks] = i32x8{(int)raw[2 * ks][0], (int)raw[2 * ks][1], (int)raw[2 * ks][2], (int)raw[2 * ks][3],
-                         (int)raw[2 * ks + 1][0], (int)raw[2 * ks + 1][1], (int)raw[2 * ks + 1][2], (int)raw[2 * ks + 1][3]};
+        for (int s8 = 0; s8 < 8; ++s8) kb[s8] = e4m3x8_to_bf16(raw[s8 / 2][(s8 % 2) * 2], raw[s8 / 2][(s8 % 2) * 2 + 1]);
         // the slot's reads have returned before it is refilled with tile k + kLRing (the last
         // iterations re-read the final tile, never scored)
         wait_lgkmcnt0();
@@ -414,15 +361,9 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
         for (int j = 0; j < S; ++j) {
           f32x16 a = {};
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const unsigned char* qa = lq + q_off + j * kIdxHeads * kQRowBytes + 32 * ks;
-            const u32x4 h0 = *reinterpret_cast<const u32x4*>(qa), h1 = *reinterpret_cast<const u32x4*>(qa + 16);
-            const u32x4 l0 = *reinterpret_cast<const u32x4*>(qa + 128), l1 = *reinterpret_cast<const u32x4*>(qa + 144);
-            a = mfma_f8_32x32x64(i32x8{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]},
-                                 kf[ks], qsc(j, ks), a);
-            a = mfma_f8_32x32x64(i32x8{(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]},
-                                 kf[ks], qsc(j, ks) - 4, a);
-          }
+          for (int s8 = 0; s8 < 8; ++s8)
+            a = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(lq + q_off + j * kIdxHeads * kQRowBytes + 16 * s8)),
+                             kb[s8], a);
           acc[j] = a;
           if (j > 0) finish(j - 1, t, scale);
         }
@@ -449,20 +390,9 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
           const int k = k0 + u;
           const int t = ring_t0[u] + col;
           asm volatile("" : "+v"(q_off), "+v"(w_off));
-          // FP8 keys: the B operands of two FP8 k-steps, the lane's codes 32 ks .. 32 ks + 31
-          // (taken before the refill below); bf16 keys: eight bf16 k-steps
-          i32x8 kf[2];
-          bf16x8 kb[kFp8 ? 1 : 8];
-          if constexpr (kFp8) {
+          bf16x8 kb[8];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-              kf[ks] = i32x8{(int)ring[u].v[2 * ks][0], (int)ring[u].v[2 * ks][1], (int)ring[u].v[2 * ks][2],
-                             (int)ring[u].v[2 * ks][3], (int)ring[u].v[2 * ks + 1][0], (int)ring[u].v[2 * ks + 1][1],
-                             (int)ring[u].v[2 * ks + 1][2], (int)ring[u].v[2 * ks + 1][3]};
-          } else {
-#pragma unroll
-            for (int s = 0; s < 8; ++s) kb[s] = key_operand<kFp8>(ring[u], s);
-          }
+          for (int s = 0; s < 8; ++s) kb[s] = key_operand<kFp8>(ring[u], s);
           // refill the slot with tile k + kRing (the last round re-reads the final tile, masked
           // by never being scored)
           const int kn = min(k + kRing, kTilesPerWave - 1);
@@ -471,27 +401,12 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
           load_key_codes<kFp8>(ring[u], src, o_next, half);
 #pragma unroll
           for (int j = 0; j < S; ++j) {
+            // A operand of k-step s for query j: Q[j][head = col][dims 64*half + 8*s .. +8]
             f32x16 a = {};
-            if constexpr (kFp8) {
-              // A operands of FP8 k-step ks: the hi and lo parts of Q[j][head = col][dims
-              // 64*half + 32*ks .. +32]
 #pragma unroll
-              for (int ks = 0; ks < 2; ++ks) {
-              const unsigned char* qa = lq + q_off + j * kIdxHeads * kQRowBytes + 32 * ks;
-              const u32x4 h0 = *reinterpret_cast<const u32x4*>(qa), h1 = *reinterpret_cast<const u32x4*>(qa + 16);
-              const u32x4 l0 = *reinterpret_cast<const u32x4*>(qa + 128), l1 = *reinterpret_cast<const u32x4*>(qa + 144);
-              a = mfma_f8_32x32x64(i32x8{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]},
-                                   kf[ks], qsc(j, ks), a);
-              a = mfma_f8_32x32x64(i32x8{(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]},
-                                   kf[ks], qsc(j, ks) - 4, a);
-              }
-            } else {
-              // A operand of k-step s for query j: Q[j][head = col][dims 64*half + 8*s .. +8]
-#pragma unroll
-              for (int s = 0; s < 8; ++s)
-                a = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(lq + q_off + j * kIdxHeads * kQRowBytes + 16 * s)),
-                                 kb[s], a);
-            }
+            for (int s = 0; s < 8; ++s)
+              a = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(lq + q_off + j * kIdxHeads * kQRowBytes + 16 * s)),
+                               kb[s], a);
             acc[j] = a;
             if (j > 0) finish(j - 1, t, ring[u].scale);
           }
