@@ -384,8 +384,8 @@ hs_status hs_decode_splits(const hs_ctx* ctx, int32_t B, int32_t S, int32_t* spl
  * its capacity are not timed and hs_kernel_times then returns HS_ERR_STATE (counts written).
  * Disabling destroys the pool and drops unread records.  Off by default. */
 typedef enum {
-  HS_KERNEL_INDEX_SCORE = 0,  /* indexer score sweep (+ first-digit histogram) */
-  HS_KERNEL_TOPK_SELECT = 1,  /* top-K select */
+  HS_KERNEL_INDEX_SCORE = 0,  /* indexer sweep listing candidates above the guesses */
+  HS_KERNEL_TOPK_SELECT = 1,  /* top-K select from the candidate lists */
   HS_KERNEL_RESOLVE = 2,      /* resolver: residency, hot hits, LRU victims, row ids */
   HS_KERNEL_MISS_COPY = 3,    /* host-to-device copy of the misses' rows */
   HS_KERNEL_DECODE = 4,       /* sparse MLA decode attention */
@@ -396,7 +396,9 @@ typedef enum {
   HS_KERNEL_LEASE = 9,        /* hot pages taking blocks from the free-block pool */
   HS_KERNEL_HOT_RELEASE = 10, /* requests' hot buffers made cold, blocks returned */
   HS_KERNEL_POOL_GIVE = 11,   /* blocks appended to the free-block pool */
-  HS_KERNEL_COUNT = 12
+  HS_KERNEL_INDEX_RESCORE = 12, /* indexer sweep storing scores (queries the lists cannot serve) */
+  HS_KERNEL_TOPK_RESCORED = 13, /* top-K select of those queries from their scores */
+  HS_KERNEL_COUNT = 14
 } hs_kernel_id;
 
 hs_status hs_kernel_timing(hs_ctx* ctx, int32_t enable);

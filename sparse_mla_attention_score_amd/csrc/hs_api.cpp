@@ -170,7 +170,6 @@ hs_status hs::compute_layout(const hs_config& c, Layout* L) {
   L->off_pool_ctr = take(2 * 8);
   L->off_err = take(4);
   L->off_scores = take(B * S * L->lmax * 4);
-  L->off_hist = take(B * S * kHistBins * 4);
   L->off_bitmap = take(B * S * L->bm_words * 4);
   L->off_miss_src = take(B * S * c.topk * 4);
   L->off_miss_dst = take(B * S * c.topk * 4);
@@ -179,6 +178,7 @@ hs_status hs::compute_layout(const hs_config& c, Layout* L) {
   L->off_part_ml = take(B * S * cap * kHeads * 2 * 4);
   L->n_seg = (int32_t)((c.max_pages_per_req + kPagesPerItem - 1) / kPagesPerItem * kSweepWaves);
   L->off_guess = take(B * S * 4);
+  L->off_rescore = take((B * S + 1) * 4);
   L->off_seg_count = take(B * S * L->n_seg * 4);
   L->off_cands = take(B * S * L->n_seg * kSegCap * 8);
   L->off_path_count = take(2 * 8);
@@ -369,7 +369,6 @@ hs_status hs_bind(hs_ctx* ctx, const hs_buffers* b) {
   ctx->ws.pool_ctr = reinterpret_cast<int64_t*>(w + L.off_pool_ctr);
   ctx->ws.err = reinterpret_cast<int32_t*>(w + L.off_err);
   ctx->ws.scores = reinterpret_cast<float*>(w + L.off_scores);
-  ctx->ws.hist = reinterpret_cast<uint32_t*>(w + L.off_hist);
   ctx->ws.bitmap = reinterpret_cast<uint32_t*>(w + L.off_bitmap);
   ctx->ws.miss_src = reinterpret_cast<int32_t*>(w + L.off_miss_src);
   ctx->ws.miss_dst = reinterpret_cast<int32_t*>(w + L.off_miss_dst);
@@ -377,6 +376,8 @@ hs_status hs_bind(hs_ctx* ctx, const hs_buffers* b) {
   ctx->ws.part_o = reinterpret_cast<float*>(w + L.off_part_o);
   ctx->ws.part_ml = reinterpret_cast<float*>(w + L.off_part_ml);
   ctx->ws.guess = reinterpret_cast<uint32_t*>(w + L.off_guess);
+  ctx->ws.rescore = reinterpret_cast<int32_t*>(w + L.off_rescore);
+  ctx->ws.n_rescore = ctx->ws.rescore + (int64_t)ctx->cfg.max_batch * ctx->cfg.max_queries;
   ctx->ws.seg_count = reinterpret_cast<uint32_t*>(w + L.off_seg_count);
   ctx->ws.cands = reinterpret_cast<uint64_t*>(w + L.off_cands);
   ctx->ws.path_count = reinterpret_cast<unsigned long long*>(w + L.off_path_count);

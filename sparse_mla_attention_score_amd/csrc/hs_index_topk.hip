@@ -89,27 +89,34 @@ constexpr int kQRowBytes = kIdxDim * 2 + 16;
 constexpr int kSweepPrefix = 1024;   // batches up to this size number their items densely
 constexpr int kSweepGridCap = 512;   // workgroups of a dense sweep: two per CU, all resident
 
-template <int S, bool kFp8>
-__global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    const int32_t* __restrict__ ctx_lens, const uint8_t* __restrict__ idx_pool,
-    const int32_t* __restrict__ idx_block_table, int64_t table_stride, int max_pages,
-    int64_t num_idx_blocks, int B,
-    float* __restrict__ scores, int64_t lmax, uint32_t* __restrict__ hist,
-    const uint32_t* __restrict__ guess, int guess_stride, uint32_t* __restrict__ seg_count,
-    uint64_t* __restrict__ cands, int n_seg, int32_t* __restrict__ err) {
+// kList: the steady-state sweep.  Queries with a guess list their tokens at or above it and
+// store no score; the others store every score.  Otherwise (the rescoring sweep): the flagged
+// queries (all of them when `rescore` is null) store every score.
+#define HS_SWEEP_PARAMS                                                                       \
+  const uint16_t *__restrict__ q_idx, const float *__restrict__ w,                              \
+      const int32_t *__restrict__ ctx_lens, const uint8_t *__restrict__ idx_pool,               \
+      const int32_t *__restrict__ idx_block_table, int64_t table_stride, int max_pages,         \
+      int64_t num_idx_blocks, int B, float *__restrict__ scores, int64_t lmax,                  \
+      const uint32_t *__restrict__ guess, int guess_stride,                                     \
+      const int32_t *__restrict__ rescore, int32_t *__restrict__ n_rescore,                     \
+      uint32_t *__restrict__ seg_count, uint64_t *__restrict__ cands, int n_seg,                \
+      int32_t *__restrict__ err
+#define HS_SWEEP_ARGS                                                                          \
+  q_idx, w, ctx_lens, idx_pool, idx_block_table, table_stride, max_pages, num_idx_blocks, B,   \
+      scores, lmax, guess, guess_stride, rescore, n_rescore, seg_count, cands, n_seg, err
+
+template <int S, bool kFp8, bool kList>
+__device__ __forceinline__ void index_sweep(HS_SWEEP_PARAMS) {
   constexpr int kBlkBytes = kFp8 ? kIdxFp8Block : kIdxBf16Block;
   constexpr int kRing = 2;  // tile slots per wave
   constexpr int kTilesPerWave = 2 * kPagesPerItem / 4;
   static_assert(kTilesPerWave % kRing == 0, "whole ring rounds");
   constexpr bool kWeightsInRegs = kFp8;
-  // With one or two queries (FP8 keys) the sweep is bound by the key stream, and key tiles go
-  // through LDS instead of registers (see the loop below); kLRing tiles per wave.
-  constexpr bool kLdsKeys = kFp8 && S <= 2;
+  // FP8 key tiles go through LDS instead of registers (see the loop below), kLRing tiles per
+  // wave.
+  constexpr bool kLdsKeys = kFp8;
   constexpr int kLRing = S == 1 ? 3 : 2;
   constexpr int kSlot = 32 * kIdxDim + 32 * 4;  // 32 tokens' codes, then their 32 scales
-  // 16-bit LDS counters, two bins per word: one workgroup sees at most 4,096 tokens.
-  __shared__ uint32_t lhist[S][kHistBins / 2];
   __shared__ __align__(16) float lw[S][kIdxHeads];  // half the head weights (see finish)
   __shared__ int32_t lblk[kPagesPerItem];
   __shared__ __align__(16) unsigned char lq[S * kIdxHeads * kQRowBytes];
@@ -124,6 +131,13 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
   // at most as many workgroups as stay resident, strides over them, so a batch of short and
   // long contexts launches no workgroup without work; beyond that, item w is (request w % B,
   // item w / B) and workgroups past a request's end exit at once.
+  // `n_rescore` counts the queries this call's list select flags: cleared by the steady-state
+  // sweep, which runs before that select; with none flagged the rescoring sweep has nothing to do
+  if constexpr (kList) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *n_rescore = 0;
+  } else {
+    if (rescore != nullptr && *n_rescore == 0) return;
+  }
   const bool packed = B <= kSweepPrefix;
   int total;
   if (packed) {
@@ -172,8 +186,17 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
     const int p_begin = item * kPagesPerItem;
     if (p_begin >= n_pages) continue;
     const int p_end = min(n_pages, p_begin + kPagesPerItem);
-
-    for (int i = threadIdx.x; i < S * kHistBins / 2; i += kSweepThreads) (&lhist[0][0])[i] = 0;
+    // the queries whose scores this item stores (the same in every thread); with kList the
+    // others list their candidates
+    bool sto[S];
+    bool any = kList;
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      sto[j] = kList ? guess[b * guess_stride + j] == kGuessOff
+                     : rescore == nullptr || rescore[b * guess_stride + j] != 0;
+      any = any || sto[j];
+    }
+    if (!any) continue;
     if (threadIdx.x < S * kIdxHeads)
       (&lw[0][0])[threadIdx.x] = 0.5f * w[b * S * kIdxHeads + threadIdx.x];
     if (threadIdx.x < kPagesPerItem) {
@@ -211,7 +234,7 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
     int cq[S];
 #pragma unroll
     for (int j = 0; j < S; ++j) {
-      gq[j] = guess[b * guess_stride + j];
+      gq[j] = kList ? guess[b * guess_stride + j] : kGuessOff;
       cq[j] = 0;
     }
     __syncthreads();
@@ -266,8 +289,8 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
       part[j] = p;
       if ((j & 1) || j == S - 1) {
         // Add the other half's 16 heads of the same token (lane l ^ 32).  The swap leaves the
-        // first query's total in lanes 0-31 and the second's in lanes 32-63, so one store and
-        // one histogram update serve both.
+        // first query's total in lanes 0-31 and the second's in lanes 32-63, so one score store
+        // and one list store serve both.
         const int jp = j & ~1, jq = j;
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[jp]), __float_as_uint(part[jq]),
                                                    false, false);
@@ -280,12 +303,11 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
         // lanes with nothing to store give an offset past the end (dropped by the hardware), so
         // every iteration issues the same number of vector-memory instructions and the waits for
         // the key ring count exactly the loads they need.  (Under a branch, the count differs
-        // between iterations and every wait has to drain all loads in flight.)  The histogram
-        // update adds zero for an invisible token.
-        const uint32_t soff = vis ? (uint32_t)(jj * lmax + t) * 4u : kOffEnd;
-        __builtin_amdgcn_raw_buffer_store_b32(bits, srs, soff, 0, 0);
-        const uint32_t bin = bits >> kHistShift;
-        atomicAdd(&lhist[jj][bin >> 1], vis ? 1u << (16 * (bin & 1)) : 0u);
+        // between iterations and every wait has to drain all loads in flight.)  First the score,
+        // if the query stores its scores.
+        const bool keep = vis && (half ? sto[jq] : sto[jp]);
+        __builtin_amdgcn_raw_buffer_store_b32(bits, srs, keep ? (uint32_t)(jj * lmax + t) * 4u : kOffEnd, 0, 0);
+        if constexpr (!kList) return;
         // list the token for the next select if its key reaches the query's guess: lanes 0-31
         // serve query jp, lanes 32-63 query jq; a lane's place is the number of listed lanes
         // below it in its half
@@ -324,8 +346,8 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
         }
         if (lane < 32) lds_load4(blk + 64 * kIdxDim + (k & 1) * 128 + 4 * lane, dst + 32 * kIdxDim);
       };
-      constexpr int kPerTile = 5, kStores = 2;
-      static_assert(S <= 2, "two stores per tile");
+      // per pair of queries: the score store, and with kList the list store
+      constexpr int kPerTile = 5, kStores = (kList ? 2 : 1) * ((S + 1) / 2);
       auto wait_tile = [&](int k) {
         // operations issued after tile k's loads: in the steady state the stores of the iteration
         // that issued them and kLRing - 1 whole iterations; at the start the later tiles of the
@@ -415,21 +437,27 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(
         }
       }
     }
-    if (lane == 0) {
+    if constexpr (kList) {
+      if (lane == 0) {
 #pragma unroll
-      for (int j = 0; j < S; ++j) seg_count[(int64_t)(b * S + j) * n_seg + seg] = (uint32_t)cq[j];
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < S * kHistBins / 2; i += kSweepThreads) {
-      const uint32_t v = (&lhist[0][0])[i];
-      if (v == 0) continue;
-      const int j = i / (kHistBins / 2), pair = i % (kHistBins / 2);
-      uint32_t* g = hist + (int64_t)(b * S + j) * kHistBins + 2 * pair;
-      if (v & 0xffffu) atomicAdd(g, v & 0xffffu);
-      if (v >> 16) atomicAdd(g + 1, v >> 16);
+        for (int j = 0; j < S; ++j) seg_count[(int64_t)(b * S + j) * n_seg + seg] = (uint32_t)cq[j];
+      }
     }
     __syncthreads();  // the item's shared state is free for the next one
   }
+}
+
+// The steady-state sweep: candidate lists of the queries with a guess.
+template <int S, bool kFp8>
+__global__ __launch_bounds__(kSweepThreads) void index_score_kernel(HS_SWEEP_PARAMS) {
+  index_sweep<S, kFp8, true>(HS_SWEEP_ARGS);
+}
+
+// The rescoring sweep: scores and first-digit histograms of the flagged queries (of every
+// query when `rescore` is null).
+template <int S, bool kFp8>
+__global__ __launch_bounds__(kSweepThreads) void index_rescore_kernel(HS_SWEEP_PARAMS) {
+  index_sweep<S, kFp8, false>(HS_SWEEP_ARGS);
 }
 
 constexpr int kSelThreads = 1024;
@@ -525,179 +553,243 @@ __device__ int find_threshold_bin(SelectShared& sh, int nbins, int need, int* ab
 // candidates in the dynamic LDS), else in the workspace.
 constexpr int kLdsBitmapMaxWords = 8192;
 
+// What a select launch serves.  kSelList: every query, from the sweep's candidate list; a query
+// the list cannot serve (no guess, an overflowed segment, fewer than K listed, or a threshold
+// bin too large for the chip) is flagged in `rescore` and left to the rescoring sweep and a
+// kSelRescored launch, which select the flagged queries from their scores.  kSelAll: every
+// query from its scores (a call without guesses, such as a prefill's).
+constexpr int kSelList = 0, kSelRescored = 1, kSelAll = 2;
+
 template <bool kLdsBitmap>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const int32_t* __restrict__ ctx_lens, int B, int S, int K, int max_ctx,
-    const float* __restrict__ scores, int64_t lmax, uint32_t* __restrict__ hist,
-    uint32_t* __restrict__ bitmap, int64_t bm_words, int32_t* __restrict__ topk_out,
+    const float* __restrict__ scores, int64_t lmax, uint32_t* __restrict__ bitmap, int64_t bm_words, int32_t* __restrict__ topk_out,
     int cand_cap, uint32_t* __restrict__ guess_all, int guess_stride,
     const uint32_t* __restrict__ seg_count,
-    const uint64_t* __restrict__ cands, int n_seg_max, unsigned long long* __restrict__ path_count,
+    const uint64_t* __restrict__ cands, int n_seg_max, int32_t* __restrict__ rescore,
+    int32_t* __restrict__ n_rescore, int mode, unsigned long long* __restrict__ path_count,
     int32_t* __restrict__ err) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ SelectShared sh;
+  __shared__ uint32_t lseg[kHistBins];  // list mode: the candidates each segment holds
   uint64_t* cand = reinterpret_cast<uint64_t*>(dyn);  // (key << 32) | ~token
 
   const int bj = blockIdx.x;
   const int b = bj / S, j = bj % S;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // rescoring flags and guesses persist per request slot, laid out [max_batch][max_queries]
+  int32_t* flag = rescore ? rescore + b * guess_stride + j : nullptr;  // null in kSelAll
+  if (mode == kSelRescored && (*n_rescore == 0 || *flag == 0)) return;
   const int Lb = ctx_lens[b];
   int32_t* out = topk_out + (int64_t)bj * K;
-  uint32_t* gh = hist + (int64_t)bj * kHistBins;
-  // the request slot's guesses persist across calls, laid out [max_batch][max_queries]
   uint32_t* guess = guess_all + b * guess_stride + j;
   const uint32_t g_used = *guess;  // the guess the sweep listed candidates from
   if (Lb < S || Lb > max_ctx) {
-    for (int i = tid; i < kHistBins; i += kSelThreads) gh[i] = 0;
     for (int i = tid; i < K; i += kSelThreads) out[i] = -1;
-    if (tid == 0) *guess = kGuessOff;
+    if (tid == 0) {
+      *guess = kGuessOff;
+      if (mode == kSelList) *flag = 0;
+    }
     return;
   }
   const int Lj = Lb - S + 1 + j;
-  if (Lj <= K) {  // everything is selected; keep the histogram zero for the next call
-    for (int i = tid; i < kHistBins; i += kSelThreads) gh[i] = 0;
+  if (Lj <= K) {  // everything is selected
     for (int i = tid; i < K; i += kSelThreads) out[i] = i < Lj ? i : -1;
-    if (tid == 0) *guess = kGuessOff;
+    if (tid == 0) {
+      *guess = kGuessOff;
+      if (mode == kSelList) *flag = 0;
+    }
     return;
   }
 
-  // The sweep's candidate list of this query (see the fast path below): the segments' counts
-  // are loaded now, with the histogram, on the chance that it is used.
   const int n_seg = (((Lb + kBlock - 1) / kBlock + kPagesPerItem - 1) / kPagesPerItem) * kSweepWaves;
   const int n_slots = n_seg * kSegCap;
-  const bool try_list = g_used != kGuessOff && n_seg <= min(n_seg_max, kHistBins);
-  const uint64_t* lst = cands + (int64_t)bj * n_seg_max * kSegCap;
-  constexpr int kSegPerThread = kHistBins / kSelThreads;
-  uint32_t segc[kSegPerThread];
-  if (try_list) {
-    const uint32_t* cnt_p = seg_count + (int64_t)bj * n_seg_max;
-#pragma unroll
-    for (int r = 0; r < kSegPerThread; ++r) {
-      const int i = tid + r * kSelThreads;
-      segc[r] = i < n_seg ? cnt_p[i] : 0u;
-    }
-  }
-  for (int i = tid; i < kHistBins; i += kSelThreads) {
-    sh.hist[i] = gh[i];
-    gh[i] = 0;
-  }
-  __syncthreads();
-  // the K-th largest score's bin, and the next call's guess: the lowest key of the bin that
-  // holds the n2-th largest score, so that a slowly moving threshold stays above it.  n2 is 8K,
-  // or a quarter of the list's slots if that is less, so that the segments (a wave's share of
-  // the listed tokens) do not overflow; no guess when that leaves no margin over K, or when
-  // there is no such bin.  (At 4K, a drifting query over a million tokens pushed its K-th
-  // score below the guess about one step in six.)
+  // The next call's guess sits at the lowest key of the bin holding the n2-th largest score, so
+  // that a slowly moving threshold stays above it.  n2 is 8K, or a quarter of the list's slots
+  // if that is less, so that the segments (a wave's share of the listed tokens) do not
+  // overflow; no guess when that leaves no margin over K, or when there is no such bin.  (At
+  // 4K, a drifting query over a million tokens pushed its K-th score below the guess about one
+  // step in six.)
   const int n2 = min(8 * K, n_slots / 4);
-  int above, beta, gbin;
-  find_threshold_bins2(sh, kHistBins, K, n2 > K ? n2 : 8 * K, &beta, &above, &gbin);
-  if (tid == 0) *guess = n2 > K && gbin > 0 ? (uint32_t)gbin << kHistShift : kGuessOff;
-  const int cnt_beta = beta >= 0 ? (int)sh.hist[beta] : 0;
-  const int need = K - above;  // tokens to take from bin beta
-  const float* sc = scores + (int64_t)bj * lmax;
   // bm_words covers whole 1,024-token chunks, so the last chunk's ballot words stay inside
   uint32_t* bm;
   if constexpr (kLdsBitmap) bm = reinterpret_cast<uint32_t*>(dyn + (size_t)cand_cap * sizeof(uint64_t));
   else bm = bitmap + (int64_t)bj * bm_words;
   const int n_chunks = (Lj + kSelThreads - 1) / kSelThreads;
+  int beta, above, gbin, cnt_beta;
+  bool fast = true;  // bin beta collected on chip, the tokens above it marked in the bitmap
+  const float* sc = scores + (int64_t)bj * lmax;
+  // in kSelList, a query without a guess stored its scores in the same sweep
+  const bool from_list = mode == kSelList && g_used != kGuessOff;
 
-  if (beta >= 0 && cnt_beta <= cand_cap) {
-    // ---- fast path: bin beta collected on chip, the tokens above it marked in the bitmap.
-    // From the sweep's candidate list when it is complete: every token of bin beta and above
-    // was listed if the guess is at most bin beta's lowest key and no wave's segment
-    // overflowed; the counts found must then equal the histogram's.  Otherwise, or if they
-    // do not, one pass over all the scores.
-    bool from_list = false;
-    if (try_list && g_used <= ((uint32_t)beta << kHistShift)) {
-      // segment counts into sh.hist (free until the refinement below)
-      int over = 0;
-#pragma unroll
-      for (int r = 0; r < kSegPerThread; ++r) {
-        const int i = tid + r * kSelThreads;
-        if (i < n_seg) sh.hist[i] = segc[r];
-        over |= segc[r] > (uint32_t)kSegCap ? 1 : 0;
+  if (from_list) {
+    // ---- from the candidate list.  The sweep listed every visible token whose key is at
+    // least the guess (a bin boundary), unless a wave's segment overflowed.  With at least K
+    // listed, the K-th largest key T is at least the guess, so every token with a key of T or
+    // more, and every key of T's bin, is in the list: the selection is made from it alone.
+    const uint64_t* lst = cands + (int64_t)bj * n_seg_max * kSegCap;
+    const uint32_t* cnt_p = seg_count + (int64_t)bj * n_seg_max;
+    const bool usable = n_seg <= min(n_seg_max, kHistBins);
+    int my_total = 0, over = 0;
+    if (usable)
+      for (int i = tid; i < n_seg; i += kSelThreads) {
+        const uint32_t c = cnt_p[i];
+        lseg[i] = c;
+        over |= c > (uint32_t)kSegCap ? 1 : 0;
+        my_total += (int)min(c, (uint32_t)kSegCap);
       }
-      const int n_words = (Lj + 31) / 32;
-      for (int i = tid; i < n_words; i += kSelThreads) bm[i] = 0u;
+    for (int i = tid; i < kHistBins; i += kSelThreads) sh.hist[i] = 0;
+    int total;
+    block_exclusive_scan<kSelThreads>(my_total, sh.scan, &total);
+    if (__syncthreads_or(over) || !usable || total < K) {
       if (tid == 0) {
-        sh.misc[2] = 0;
-        sh.misc[4] = 0;
+        *flag = 1;
+        atomicAdd(n_rescore, 1);
       }
-      if (!__syncthreads_or(over)) {  // (the barrier also orders the zeroing before the bits)
-        // Each wave reads whole segments (w, w + 16, ...), only their filled entries: lane l
-        // takes entries l, l + 64 and l + 128.  Nine segments' loads are issued together.
-        int my_above = 0;
-        auto take = [&](uint64_t v) {
-          const uint32_t key = (uint32_t)(v >> 32), t = ~(uint32_t)v;
-          if ((int)t >= Lj) return;
-          const int bin = (int)(key >> kHistShift);
-          if (bin > beta) {
-            atomicOr(&bm[t >> 5], 1u << (t & 31));
-            ++my_above;
-          } else if (bin == beta) {
-            const int pos = atomicAdd(&sh.misc[2], 1);
-            if (pos < cand_cap) cand[pos] = v;
-          }
-        };
-        // The loads are buffer loads: an empty entry's lane asks for an offset past the end,
-        // which returns zero without a memory access, so no load sits under a per-lane branch
-        // (where the compiler would issue it only when its value is used, one round trip
-        // each).  Segments are read kSegsAtOnce at a time, their first kFirstRows rows of 64
-        // entries together (rows past a segment's count skipped by a scalar branch); any
-        // further rows follow behind a scalar branch.  Contexts up to 256 K tokens (the LDS
-        // bitmap; at most 256 segments, around 48 entries each at 128 K): 9 segments of 3 rows.
-        // Longer ones (up to 1,028 segments, a few entries each at 1 M): 16 segments of 1 row.
-        constexpr int kRows = kSegCap / 64;
-        constexpr int kSegsAtOnce = kLdsBitmap ? 9 : 16, kFirstRows = kLdsBitmap ? kRows : 1;
-        static_assert(kSegCap % 64 == 0, "whole wave rows per segment");
-        const int n_waves = kSelThreads / 64;
-        const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint64_t*>(lst), (short)0, n_slots * (int)sizeof(uint64_t), kBufferRsrcWord3);
-        auto load_entry = [&](int sg, int idx, int c) -> uint64_t {
-          const uint32_t off = idx < c ? (uint32_t)(sg * kSegCap + idx) * (uint32_t)sizeof(uint64_t) : 0x80000000u;
-          const auto w = __builtin_amdgcn_raw_buffer_load_b64(lrs, off, 0, 0);
-          return ((uint64_t)(uint32_t)w[1] << 32) | (uint32_t)w[0];
-        };
-        for (int s0 = wave; s0 < n_seg; s0 += kSegsAtOnce * n_waves) {
-          uint64_t v[kSegsAtOnce][kFirstRows];
-          int c[kSegsAtOnce];  // the segment's count: the same in every lane
+      return;
+    }
+    // Each wave reads whole segments (w, w + 16, ...), only their filled entries: lane l takes
+    // entries l, l + 64 and l + 128.  The loads are buffer loads: an empty entry's lane asks
+    // for an offset past the end, which returns zero without a memory access, so no load sits
+    // under a per-lane branch (where the compiler would issue it only when its value is used,
+    // one round trip each).  Segments are read kSegsAtOnce at a time, their first kFirstRows
+    // rows of 64 entries together (rows past a segment's count skipped by a scalar branch);
+    // any further rows follow behind a scalar branch.  Contexts up to 256 K tokens (the LDS
+    // bitmap; at most 256 segments, around 48 entries each at 128 K): 9 segments of 3 rows.
+    // Longer ones (up to 1,028 segments, a few entries each at 1 M): 16 segments of 1 row.
+    constexpr int kRows = kSegCap / 64;
+    constexpr int kSegsAtOnce = kLdsBitmap ? 9 : 16, kFirstRows = kLdsBitmap ? kRows : 1;
+    static_assert(kSegCap % 64 == 0, "whole wave rows per segment");
+    const int n_waves = kSelThreads / 64;
+    const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint64_t*>(lst), (short)0, n_slots * (int)sizeof(uint64_t), kBufferRsrcWord3);
+    auto load_entry = [&](int sg, int idx, int c) -> uint64_t {
+      const uint32_t off = idx < c ? (uint32_t)(sg * kSegCap + idx) * (uint32_t)sizeof(uint64_t) : 0x80000000u;
+      const auto w = __builtin_amdgcn_raw_buffer_load_b64(lrs, off, 0, 0);
+      return ((uint64_t)(uint32_t)w[1] << 32) | (uint32_t)w[0];
+    };
+    auto for_each_listed = [&](auto&& take) {
+      for (int s0 = wave; s0 < n_seg; s0 += kSegsAtOnce * n_waves) {
+        uint64_t v[kSegsAtOnce][kFirstRows];
+        int c[kSegsAtOnce];  // the segment's count: the same in every lane
 #pragma unroll
-          for (int a = 0; a < kSegsAtOnce; ++a) {
-            const int sg = s0 + a * n_waves;
-            c[a] = __builtin_amdgcn_readfirstlane(sg < n_seg ? (int)sh.hist[sg] : 0);
+        for (int a = 0; a < kSegsAtOnce; ++a) {
+          const int sg = s0 + a * n_waves;
+          c[a] = __builtin_amdgcn_readfirstlane(sg < n_seg ? (int)lseg[sg] : 0);
 #pragma unroll
-            for (int r = 0; r < kFirstRows; ++r) {
-              // the first row is loaded unconditionally (a branch would make the compiler
-              // wait for it at the join); later rows only when the segment reaches them
-              v[a][r] = 0;
-              if (r == 0 || c[a] > 64 * r) v[a][r] = load_entry(sg, lane + 64 * r, c[a]);
-            }
-          }
-#pragma unroll
-          for (int a = 0; a < kSegsAtOnce; ++a)
-#pragma unroll
-            for (int r = 0; r < kFirstRows; ++r) {
-              if (c[a] <= 64 * r) continue;
-              asm volatile("" : "+v"(v[a][r]));  // every load above is issued before the first wait
-              if (lane + 64 * r < c[a]) take(v[a][r]);
-            }
-          for (int a = 0; a < kSegsAtOnce; ++a) {
-            if (c[a] <= 64 * kFirstRows) continue;
-            const int sg = s0 + a * n_waves;
-            for (int r = kFirstRows; r < kRows; ++r) {
-              if (c[a] <= 64 * r) break;
-              const uint64_t w = load_entry(sg, lane + 64 * r, c[a]);
-              if (lane + 64 * r < c[a]) take(w);
-            }
+          for (int r = 0; r < kFirstRows; ++r) {
+            // the first row is loaded unconditionally (a branch would make the compiler wait
+            // for it at the join); later rows only when the segment reaches them
+            v[a][r] = 0;
+            if (r == 0 || c[a] > 64 * r) v[a][r] = load_entry(sg, lane + 64 * r, c[a]);
           }
         }
-        if (my_above) atomicAdd(&sh.misc[4], my_above);
-        __syncthreads();
-        from_list = sh.misc[4] == above && sh.misc[2] == cnt_beta;
-        __syncthreads();
+#pragma unroll
+        for (int a = 0; a < kSegsAtOnce; ++a)
+#pragma unroll
+          for (int r = 0; r < kFirstRows; ++r) {
+            if (c[a] <= 64 * r) continue;
+            asm volatile("" : "+v"(v[a][r]));  // every load above is issued before the first wait
+            if (lane + 64 * r < c[a]) take(v[a][r]);
+          }
+        for (int a = 0; a < kSegsAtOnce; ++a) {
+          if (c[a] <= 64 * kFirstRows) continue;
+          const int sg = s0 + a * n_waves;
+          for (int r = kFirstRows; r < kRows; ++r) {
+            if (c[a] <= 64 * r) break;
+            const uint64_t w = load_entry(sg, lane + 64 * r, c[a]);
+            if (lane + 64 * r < c[a]) take(w);
+          }
+        }
+      }
+    };
+    // the listed keys' first-digit histogram
+    for_each_listed([&](uint64_t v) { atomicAdd(&sh.hist[(uint32_t)(v >> 32) >> kHistShift], 1u); });
+    __syncthreads();
+    find_threshold_bins2(sh, kHistBins, K, n2 > K ? n2 : 8 * K, &beta, &above, &gbin);
+    cnt_beta = beta >= 0 ? (int)sh.hist[beta] : 0;
+    if (beta < 0 || cnt_beta > cand_cap) {  // (beta >= 0 holds with K listed)
+      if (tid == 0) {
+        *flag = 1;
+        atomicAdd(n_rescore, 1);
+      }
+      return;
+    }
+    if (tid == 0) {
+      // The next guess.  With n2 or more listed, the n2-th largest key is listed too and the
+      // guess follows the rule above exactly.  With fewer, it lies below the list; the guess is
+      // lowered by as many bins as the missing count over the lowest listed bin's count
+      // suggests (one to eight bins; a list that still falls short of K is rescored, which
+      // sets the guess by the rule above).
+      uint32_t g = kGuessOff;
+      if (n2 > K) {
+        if (gbin >= 0) {
+          g = gbin > 0 ? (uint32_t)gbin << kHistShift : kGuessOff;
+        } else {
+          const int low = (int)(g_used >> kHistShift);
+          const int c_low = max((int)sh.hist[low], 1);
+          const int d = min(max((n2 - total + c_low - 1) / c_low, 1), 8);
+          g = low - d > 0 ? (uint32_t)(low - d) << kHistShift : kGuessOff;
+        }
+      }
+      *guess = g;
+      *flag = 0;
+      atomicAdd(&path_count[0], 1ull);
+    }
+    // the tokens above bin beta into the bitmap, bin beta on chip
+    const int n_words = (Lj + 31) / 32;
+    for (int i = tid; i < n_words; i += kSelThreads) bm[i] = 0u;
+    if (tid == 0) sh.misc[2] = 0;
+    __syncthreads();  // (also orders the zeroing before the bits)
+    for_each_listed([&](uint64_t v) {
+      const uint32_t key = (uint32_t)(v >> 32), t = ~(uint32_t)v;
+      const int bin = (int)(key >> kHistShift);
+      if (bin > beta) {
+        atomicOr(&bm[t >> 5], 1u << (t & 31));
+      } else if (bin == beta) {
+        const int pos = atomicAdd(&sh.misc[2], 1);
+        if (pos < cand_cap) cand[pos] = v;
+      }
+    });
+  } else {
+    // ---- from the scores: their first-digit histogram, counted on chip.  8 chunks per round,
+    // loaded together; the next round's loads are issued before this round is counted.
+    // Loads past the end read the last visible score again and are not counted.
+    for (int i = tid; i < kHistBins; i += kSelThreads) sh.hist[i] = 0;
+    __syncthreads();
+    {
+      constexpr int kPer = 8;
+      auto load_keys = [&](uint32_t (&k)[kPer], int c0) {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) k[e] = __float_as_uint(sc[min((c0 + e) * kSelThreads + tid, Lj - 1)]);
+      };
+      auto count_keys = [&](const uint32_t (&k)[kPer], int c0) {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e)
+          if ((c0 + e) * kSelThreads + tid < Lj) atomicAdd(&sh.hist[k[e] >> kHistShift], 1u);
+      };
+      uint32_t ka[kPer], kb[kPer];
+      load_keys(ka, 0);
+      for (int c0 = 0; c0 < n_chunks; c0 += 2 * kPer) {
+        load_keys(kb, c0 + kPer);
+        count_keys(ka, c0);
+        load_keys(ka, c0 + 2 * kPer);
+        count_keys(kb, c0 + kPer);
       }
     }
-    if (tid == 0) atomicAdd(&path_count[from_list ? 0 : 1], 1ull);
+    __syncthreads();
+    find_threshold_bins2(sh, kHistBins, K, n2 > K ? n2 : 8 * K, &beta, &above, &gbin);
+    if (tid == 0) {
+      *guess = n2 > K && gbin > 0 ? (uint32_t)gbin << kHistShift : kGuessOff;
+      if (mode == kSelList) *flag = 0;
+      atomicAdd(&path_count[1], 1ull);
+    }
+    cnt_beta = beta >= 0 ? (int)sh.hist[beta] : 0;
+    fast = beta >= 0 && cnt_beta <= cand_cap;
+  }
+  const int need = K - above;  // tokens to take from bin beta
+
+  if (fast) {
     if (!from_list) {
     // one pass over the scores; every bitmap word is written
     if (tid == 0) sh.misc[2] = 0;
@@ -796,7 +888,6 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
       if (rank < need_left) atomicOr(&bm[t >> 5], 1u << (t & 31));
     }
   } else {
-    if (tid == 0) atomicAdd(&path_count[1], 1ull);
     // ---- general path: refine the threshold over the remaining 19 bits, then an ordered
     // pass that takes the lowest-index ties.
     uint32_t prefix = (uint32_t)max(beta, 0);
@@ -974,7 +1065,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   if (tid == 0 && total != K) raise_error(err, HS_DEVERR_TOPK_COUNT);
 }
 
-// One sweep + select over B requests of S queries.  `idx_table` rows are `table_stride` apart
+// One index call over B requests of S queries.  `idx_table` rows are `table_stride` apart
 // (0: every request reads the same row, as the groups of one prefill do); the select keeps its
 // guesses in `guess` ([B][guess_stride]) and counts its paths in `paths`.
 struct IndexCall {
@@ -986,62 +1077,80 @@ struct IndexCall {
   int64_t table_stride;
   uint32_t* guess;
   int guess_stride;
+  int32_t* rescore;  // [B][guess_stride] rescoring flags; null: no guesses, every query rescored
+  int32_t* n_rescore;  // flags set in this call
   unsigned long long* paths;
   int32_t* topk_out;
 };
 
 template <int S, bool kFp8>
-hipError_t launch_scores(const hs_ctx* ctx, const IndexCall& a, hipStream_t stream) {
+hipError_t launch_sweep(const hs_ctx* ctx, const IndexCall& a, bool list, hipStream_t stream) {
   const hs_config& c = ctx->cfg;
   const int items = (c.max_pages_per_req + kPagesPerItem - 1) / kPagesPerItem;
   int64_t n_wg = (int64_t)a.B * items;
   if (a.B <= kSweepPrefix && n_wg > kSweepGridCap) n_wg = kSweepGridCap;
-  dim3 grid((unsigned)n_wg), block(kSweepThreads);
-  hs_timer_mark(ctx, HS_KERNEL_INDEX_SCORE, true, stream);
-  hipLaunchKernelGGL((index_score_kernel<S, kFp8>), grid, block, 0, stream,
-                     static_cast<const uint16_t*>(a.q_idx), a.w, a.ctx_lens,
-                     static_cast<const uint8_t*>(ctx->buf.idx_pool), a.idx_table, a.table_stride,
-                     c.max_pages_per_req, (int64_t)c.num_idx_blocks, a.B, ctx->ws.scores,
-                     ctx->lay.lmax, ctx->ws.hist, a.guess, a.guess_stride, ctx->ws.seg_count,
-                     ctx->ws.cands, ctx->lay.n_seg, ctx->ws.err);
-  hs_timer_mark(ctx, HS_KERNEL_INDEX_SCORE, false, stream);
+  const dim3 grid((unsigned)n_wg), block(kSweepThreads);
+  const int id = list ? HS_KERNEL_INDEX_SCORE : HS_KERNEL_INDEX_RESCORE;
+  const auto kernel = list ? index_score_kernel<S, kFp8> : index_rescore_kernel<S, kFp8>;
+  hs_timer_mark(ctx, id, true, stream);
+  hipLaunchKernelGGL(kernel, grid, block, 0, stream, static_cast<const uint16_t*>(a.q_idx), a.w,
+                     a.ctx_lens, static_cast<const uint8_t*>(ctx->buf.idx_pool), a.idx_table,
+                     a.table_stride, c.max_pages_per_req, (int64_t)c.num_idx_blocks, a.B,
+                     ctx->ws.scores, ctx->lay.lmax, a.guess, a.guess_stride,
+                     a.rescore, a.n_rescore, ctx->ws.seg_count, ctx->ws.cands, ctx->lay.n_seg,
+                     ctx->ws.err);
+  hs_timer_mark(ctx, id, false, stream);
   return hipGetLastError();
 }
 
-hipError_t launch_index_call(const hs_ctx* ctx, const IndexCall& a, hipStream_t stream) {
+hipError_t launch_sweep_for(const hs_ctx* ctx, const IndexCall& a, bool list, hipStream_t stream) {
   const bool fp8 = ctx->cfg.idx_dtype == HS_FP8_E4M3;
-  hipError_t e;
   switch (a.S * 2 + (fp8 ? 1 : 0)) {
-    case 2: e = launch_scores<1, false>(ctx, a, stream); break;
-    case 3: e = launch_scores<1, true>(ctx, a, stream); break;
-    case 4: e = launch_scores<2, false>(ctx, a, stream); break;
-    case 5: e = launch_scores<2, true>(ctx, a, stream); break;
-    case 6: e = launch_scores<3, false>(ctx, a, stream); break;
-    case 7: e = launch_scores<3, true>(ctx, a, stream); break;
-    case 8: e = launch_scores<4, false>(ctx, a, stream); break;
-    case 9: e = launch_scores<4, true>(ctx, a, stream); break;
+    case 2: return launch_sweep<1, false>(ctx, a, list, stream);
+    case 3: return launch_sweep<1, true>(ctx, a, list, stream);
+    case 4: return launch_sweep<2, false>(ctx, a, list, stream);
+    case 5: return launch_sweep<2, true>(ctx, a, list, stream);
+    case 6: return launch_sweep<3, false>(ctx, a, list, stream);
+    case 7: return launch_sweep<3, true>(ctx, a, list, stream);
+    case 8: return launch_sweep<4, false>(ctx, a, list, stream);
+    case 9: return launch_sweep<4, true>(ctx, a, list, stream);
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess) return e;
+}
+
+hipError_t launch_select(const hs_ctx* ctx, const IndexCall& a, int mode, hipStream_t stream) {
   const int cap = hs_select_cand_cap(ctx->cfg);
   const bool lds_bitmap = ctx->lay.bm_words <= kLdsBitmapMaxWords;
   const size_t dyn = (size_t)cap * sizeof(uint64_t) + (lds_bitmap ? (size_t)ctx->lay.bm_words * 4 : 0);
   const dim3 grid((unsigned)(a.B * a.S));
-  hs_timer_mark(ctx, HS_KERNEL_TOPK_SELECT, true, stream);
-  if (lds_bitmap)
-    hipLaunchKernelGGL(topk_select_kernel<true>, grid, dim3(kSelThreads), dyn, stream, a.ctx_lens,
-                       a.B, a.S, ctx->cfg.topk, ctx->cfg.max_pages_per_req * kBlock,
-                       ctx->ws.scores, ctx->lay.lmax, ctx->ws.hist, ctx->ws.bitmap,
-                       (int64_t)ctx->lay.bm_words, a.topk_out, cap, a.guess, a.guess_stride,
-                       ctx->ws.seg_count, ctx->ws.cands, ctx->lay.n_seg, a.paths, ctx->ws.err);
-  else
-    hipLaunchKernelGGL(topk_select_kernel<false>, grid, dim3(kSelThreads), dyn, stream, a.ctx_lens,
-                       a.B, a.S, ctx->cfg.topk, ctx->cfg.max_pages_per_req * kBlock,
-                       ctx->ws.scores, ctx->lay.lmax, ctx->ws.hist, ctx->ws.bitmap,
-                       (int64_t)ctx->lay.bm_words, a.topk_out, cap, a.guess, a.guess_stride,
-                       ctx->ws.seg_count, ctx->ws.cands, ctx->lay.n_seg, a.paths, ctx->ws.err);
-  hs_timer_mark(ctx, HS_KERNEL_TOPK_SELECT, false, stream);
+  const int id = mode == kSelRescored ? HS_KERNEL_TOPK_RESCORED : HS_KERNEL_TOPK_SELECT;
+  const auto kernel = lds_bitmap ? topk_select_kernel<true> : topk_select_kernel<false>;
+  hs_timer_mark(ctx, id, true, stream);
+  hipLaunchKernelGGL(kernel, grid, dim3(kSelThreads), dyn, stream, a.ctx_lens, a.B, a.S,
+                     ctx->cfg.topk, ctx->cfg.max_pages_per_req * kBlock, ctx->ws.scores,
+                     ctx->lay.lmax, ctx->ws.bitmap, (int64_t)ctx->lay.bm_words,
+                     a.topk_out, cap, a.guess, a.guess_stride, ctx->ws.seg_count, ctx->ws.cands,
+                     ctx->lay.n_seg, a.rescore, a.n_rescore, mode, a.paths, ctx->ws.err);
+  hs_timer_mark(ctx, id, false, stream);
   return hipGetLastError();
+}
+
+// One index call.  With guesses: the steady-state sweep lists candidates, the select serves
+// every query it can from the lists and flags the rest, the rescoring sweep scores the flagged
+// queries and the last select serves them.  Without (a prefill's groups): every query is
+// scored and selected from its scores.
+hipError_t launch_index_call(const hs_ctx* ctx, const IndexCall& a, hipStream_t stream) {
+  hipError_t e;
+  if (a.rescore) {
+    e = launch_sweep_for(ctx, a, true, stream);
+    if (e == hipSuccess) e = launch_select(ctx, a, kSelList, stream);
+    if (e == hipSuccess) e = launch_sweep_for(ctx, a, false, stream);
+    if (e == hipSuccess) e = launch_select(ctx, a, kSelRescored, stream);
+  } else {
+    e = launch_sweep_for(ctx, a, false, stream);
+    if (e == hipSuccess) e = launch_select(ctx, a, kSelAll, stream);
+  }
+  return e;
 }
 
 // A prefill chunk as decode-shaped groups: queries [c0, c0 + n) of the P new tokens that end an
@@ -1085,7 +1194,8 @@ hipError_t hs_launch_index_topk(const hs_ctx* ctx, const void* q_idx, const floa
                                 const int32_t* ctx_lens, int B, int S, int32_t* topk_out,
                                 hipStream_t stream) {
   const IndexCall a{q_idx, w, ctx_lens, B, S, ctx->buf.idx_block_table, ctx->cfg.max_pages_per_req,
-                    ctx->ws.guess, ctx->cfg.max_queries, ctx->ws.path_count, topk_out};
+                    ctx->ws.guess, ctx->cfg.max_queries, ctx->ws.rescore, ctx->ws.n_rescore,
+                    ctx->ws.path_count, topk_out};
   return launch_index_call(ctx, a, stream);
 }
 
@@ -1112,7 +1222,8 @@ hipError_t hs_launch_prefill_index_topk(const hs_ctx* ctx, int b, const void* q_
     const unsigned char* qb = static_cast<const unsigned char*>(q_idx) + (size_t)c0 * q_bytes;
     if (full) {
       const IndexCall a{qb, w + (int64_t)c0 * kIdxHeads, ctx->ws.pf_lens, full, S, table, 0,
-                        ctx->ws.pf_guess, S, ctx->ws.pf_paths, topk_out + (int64_t)c0 * c.topk};
+                        ctx->ws.pf_guess, S, nullptr, nullptr, ctx->ws.pf_paths,
+                        topk_out + (int64_t)c0 * c.topk};
       e = launch_index_call(ctx, a, stream);
       if (e != hipSuccess) return e;
     }
@@ -1120,7 +1231,7 @@ hipError_t hs_launch_prefill_index_topk(const hs_ctx* ctx, int b, const void* q_
       const int i0 = c0 + full * S;
       const IndexCall a{qb + (size_t)full * S * q_bytes, w + (int64_t)i0 * kIdxHeads,
                         ctx->ws.pf_lens + full, 1, rem, table, 0, ctx->ws.pf_guess + full * S, S,
-                        ctx->ws.pf_paths, topk_out + (int64_t)i0 * c.topk};
+                        nullptr, nullptr, ctx->ws.pf_paths, topk_out + (int64_t)i0 * c.topk};
       e = launch_index_call(ctx, a, stream);
       if (e != hipSuccess) return e;
     }

@@ -61,7 +61,6 @@ struct Workspace {
   int64_t* pool_ctr;     // [2]                pool front and back, monotonic (entry = ring[x % cap])
   int32_t* err;          // [1]                sticky device error word (HS_DEVERR_*)
   float* scores;         // [Bmax][Smax][Lmax] indexer scores of one call
-  uint32_t* hist;        // [Bmax][Smax][kHistBins] first-digit histogram (kept zero between calls)
   uint32_t* bitmap;      // [Bmax][Smax][bm_words] selected-token bitmap
   int32_t* miss_src;     // [Bmax][Smax*K] host row of each miss of the last resolve
   int32_t* miss_dst;     // [Bmax][Smax*K] device row (hot slot) it is copied to
@@ -69,6 +68,8 @@ struct Workspace {
   float* part_o;         // [Bmax*Smax*splits_cap][64][512] split-K partial outputs
   float* part_ml;        // [Bmax*Smax*splits_cap][64][2] split-K (max, sum) in log2 units
   uint32_t* guess;       // [Bmax][Smax]       score key from which the sweep lists candidates
+  int32_t* rescore;      // [Bmax][Smax]       queries the candidate lists could not serve this call
+  int32_t* n_rescore;    // [1]                how many of them (follows `rescore`)
   uint32_t* seg_count;   // [Bmax][Smax][n_seg] candidates each sweep wave found (> kSegCap: overflow)
   uint64_t* cands;       // [Bmax][Smax][n_seg][kSegCap] (key << 32) | ~token
   unsigned long long* path_count;  // [2] selections made from the candidate list / the scores
@@ -82,8 +83,8 @@ struct Workspace {
 
 struct Layout {
   size_t off_slot_token, off_slot_stamp, off_lru_order, off_tok2slot, off_req_step, off_req_used,
-      off_win_start, off_pool_ring, off_pool_ctr, off_err, off_scores, off_hist, off_bitmap, off_miss_src, off_miss_dst, off_miss_cnt,
-      off_part_o, off_part_ml, off_guess, off_seg_count, off_cands, off_path_count, off_zero_row,
+      off_win_start, off_pool_ring, off_pool_ctr, off_err, off_scores, off_bitmap, off_miss_src, off_miss_dst, off_miss_cnt,
+      off_part_o, off_part_ml, off_guess, off_rescore, off_seg_count, off_cands, off_path_count, off_zero_row,
       off_pf_lens, off_pf_guess, off_pf_paths, off_pf_rows, total;
   int32_t hot_rows;
   int64_t lmax;       // max_pages_per_req * 64

@@ -601,7 +601,7 @@ __global__ __launch_bounds__(64) void pool_append_kernel(
 __global__ void hot_reset_kernel(int32_t* slot_token, int32_t* slot_stamp, int32_t* lru_order,
                                  int64_t n_slots, int H, int32_t* tok2slot, int64_t n_tok,
                                  int32_t* req_step, int32_t* req_used, int32_t* win_start,
-                                 int max_batch, uint32_t* hist, int64_t n_hist, uint32_t* guess,
+                                 int max_batch, uint32_t* guess,
                                  int n_guess, unsigned long long* path_count, int32_t* hot_blocks,
                                  int64_t n_hot_blocks, int64_t* pool_ctr, int64_t n_all,
                                  int32_t* err) {
@@ -614,7 +614,6 @@ __global__ void hot_reset_kernel(int32_t* slot_token, int32_t* slot_stamp, int32
       lru_order[i] = (int32_t)(i % H);
       lru_order[n_slots + i] = (int32_t)(i % H);
     }
-    if (i < n_hist) hist[i] = 0;
     if (i < n_guess) guess[i] = kGuessOff;
     if (i < 2) path_count[i] = 0;
     if (i < max_batch) {
@@ -731,11 +730,9 @@ hipError_t hs_launch_hot_reset(const hs_ctx* ctx, hipStream_t stream) {
   const hs_config& c = ctx->cfg;
   const int64_t n_slots = (int64_t)c.max_batch * ctx->lay.hot_rows;
   const int64_t n_tok = (int64_t)c.max_batch * ctx->lay.lmax;
-  const int64_t n_hist = (int64_t)c.max_batch * c.max_queries * kHistBins;
   const int64_t n_hot_blocks = c.hot_leasing ? (int64_t)c.max_batch * (ctx->lay.hot_rows / kBlock) : 0;
   int64_t n = n_tok;
   if (n_slots > n) n = n_slots;
-  if (n_hist > n) n = n_hist;
   if (n_hot_blocks > n) n = n_hot_blocks;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
@@ -743,7 +740,7 @@ hipError_t hs_launch_hot_reset(const hs_ctx* ctx, hipStream_t stream) {
   hipLaunchKernelGGL(hot_reset_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      ctx->ws.slot_token, ctx->ws.slot_stamp, ctx->ws.lru_order, n_slots,
                      ctx->lay.hot_rows, ctx->ws.tok2slot, n_tok, ctx->ws.req_step, ctx->ws.req_used,
-                     ctx->ws.win_start, c.max_batch, ctx->ws.hist, n_hist, ctx->ws.guess,
+                     ctx->ws.win_start, c.max_batch, ctx->ws.guess,
                      c.max_batch * c.max_queries, ctx->ws.path_count, ctx->buf.hot_blocks,
                      n_hot_blocks, c.hot_leasing ? ctx->ws.pool_ctr : nullptr, n, ctx->ws.err);
   hs_timer_mark(ctx, HS_KERNEL_HOT_RESET, false, stream);

@@ -29,7 +29,8 @@ HS_DEVERR_BAD_REQUEST = 0x200
 
 # hs_kernel_id
 KERNEL_NAMES = ["index_score", "topk_select", "resolve", "miss_copy", "decode", "decode_merge",
-                "hot_reset", "materialize", "release", "lease", "hot_release", "pool_give"]
+                "hot_reset", "materialize", "release", "lease", "hot_release", "pool_give",
+                "index_rescore", "topk_rescored"]
 HS_KERNEL_COUNT = len(KERNEL_NAMES)
 
 EXPORTED = ["hs_create", "hs_destroy", "hs_workspace_bytes", "hs_host_pool_bytes",
