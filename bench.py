@@ -311,7 +311,7 @@ def main() -> int:
                       "peak": PCIE_PEAK_GBPS, "frac": round(copy_gbps / PCIE_PEAK_GBPS, 4)},
         "kernels_us": kernels_us,
         "kernel_launches": kernel_launches,
-        "roofline": {"kernel": "index_score_kernel (indexer score sweep)",
+        "roofline": {"kernel": "index_score_kernel (indexer sweep, steady state: every key scored, candidates listed)",
                      "bound": "hbm", "achieved": round(sweep_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(sweep_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,

@@ -183,9 +183,12 @@ hs_status hs_hot_reset(hs_ctx* ctx, void* stream);
  *             index, written in ascending token order and padded with -1.
  * The score formula is not printed on the pages; this is the reading the library takes.
  * Between calls the library keeps, per request slot and query, a guess of where the next
- * call's selection threshold lies (from this call's score histogram); the sweep then also
- * lists the tokens scoring above the guess, and the select reads that short list instead of
- * every score whenever the histogram proves it complete.  The result is the same either way;
+ * call's selection threshold lies (set from this call's scores or candidates).  A query with a
+ * guess has its sweep list only the tokens scoring at or above it, and its select works from
+ * that list alone when the list provably holds the answer (no segment overflowed and at
+ * least K tokens listed); otherwise the query is rescored (a second sweep stores its scores)
+ * and selected from all its scores.  The result is the same either way; the call launches
+ * four kernels (two of which find nothing to do when every list serves), all on `stream`.
  * hs_hot_reset and hs_hot_release clear the guesses.
  */
 hs_status hisparse_index_topk(hs_ctx* ctx, const void* q_idx, const float* w,

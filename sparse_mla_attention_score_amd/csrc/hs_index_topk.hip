@@ -15,19 +15,24 @@
 // are converted to bf16 exactly, the per-token fp32 scale is applied after the ReLU (positive
 // scales commute with it).  Lane l holds 64 contiguous key bytes of token l%32 (dims
 // 64*(l/32) .. +64); the 128 dims are assigned to MFMA k-slots in that order, and the query
-// fragments read from LDS use the same assignment.  With three or four queries the lanes load
-// their key bytes straight into registers; with one or two the sweep is bound by the key
-// stream, and the key tiles come into LDS first, by direct loads of whole cache lines.  Scores
-// go to a per-(request, query) scratch row; their first radix digit (bits [30:19]) is counted
-// in LDS and added to a global histogram.
+// fragments read from LDS use the same assignment.  FP8 key tiles come into LDS first, by
+// direct loads of whole cache lines; bf16 keys go straight into registers.
 //
-// Select: one workgroup per (request, query).  The histogram gives the threshold bin; one
-// pass over the scores (two rounds of loads in flight) marks the tokens above it in a bitmap
-// (wave ballots; in LDS up to 256 K tokens, else in the workspace) and collects the bin's
-// tokens on chip, where a radix select over the key's remaining 19 bits and a token order
-// among equal keys pick the rest.  If the bin is too large for the chip, the same
-// refinement runs over the scores in memory, with an index-ordered pass for exact ties.  The
-// bitmap is then emitted in order.
+// A query with a guess (a score key left by the previous call) only lists its tokens whose
+// key reaches the guess, into per-wave segments of a candidate list; a query without one
+// stores all its scores.  No score of a guessed query is stored and nothing is counted.
+//
+// Select: one workgroup per (request, query).  From the list: with no segment overflowed and
+// at least K entries, the K-th largest key is at or above the guess, so the list holds the
+// whole answer.  A first pass counts the listed keys' first radix digit (bits [30:19]) in LDS
+// (and stashes the entries on chip when they fit); the histogram gives the threshold bin; a
+// second pass marks the entries above it in a token bitmap (in LDS up to 256 K tokens, else
+// in the workspace) and collects the bin's entries on chip, where a radix select over the
+// key's remaining 19 bits and a token order among equal keys pick the rest.  The bitmap is
+// then emitted in order.  From the scores: the same, with both passes over the stored scores,
+// and, if the bin is too large for the chip, the refinement over the scores in memory with an
+// index-ordered pass for exact ties.  A query whose list cannot serve is flagged; a rescoring
+// sweep stores the flagged queries' scores and a second select serves them from the scores.
 #include "hs_device.h"
 #include "hs_internal.h"
 
@@ -81,7 +86,7 @@ __device__ __forceinline__ bf16x8 key_operand(const KeyTile<kFp8>& kt, int s) {
 // banks).  Per tile, the key operands are converted once; then each query runs a chain of 8
 // MFMAs while the previous query's weighted ReLU sum (VALU) runs beside it, the last query's
 // sum overlapping the next tile's first chain.  The slot a tile came from is refilled right
-// after its conversion, so two tiles stay in flight behind the one being scored.  With FP8
+// after its reads, so one or two tiles stay in flight behind the one being scored.  With FP8
 // keys the 16 head weights each lane needs per query stay in registers; bf16 tiles are twice
 // as large and read the weights from LDS instead.  All of it fits two waves per SIMD.
 constexpr int kSweepThreads = 256;
@@ -270,7 +275,7 @@ __device__ __forceinline__ void index_sweep(HS_SWEEP_PARAMS) {
       part[j] = 0.0f;
     }
     // Weighted ReLU sum of query j over the lane's 16 heads, then (after the second query of a
-    // pair, or a lone last query) the store and histogram update of token t.
+    // pair, or a lone last query) the score store and the list entry of token t.
     // w * max(c, 0) == (w / 2) * (c + |c|): both factors are exact power-of-two rescalings, so
     // the products round identically; c + |c| needs no NaN canonicalising.
     auto finish = [&](int j, int t, float sc) {
@@ -453,8 +458,7 @@ __global__ __launch_bounds__(kSweepThreads) void index_score_kernel(HS_SWEEP_PAR
   index_sweep<S, kFp8, true>(HS_SWEEP_ARGS);
 }
 
-// The rescoring sweep: scores and first-digit histograms of the flagged queries (of every
-// query when `rescore` is null).
+// The rescoring sweep: scores of the flagged queries (of every query when `rescore` is null).
 template <int S, bool kFp8>
 __global__ __launch_bounds__(kSweepThreads) void index_rescore_kernel(HS_SWEEP_PARAMS) {
   index_sweep<S, kFp8, false>(HS_SWEEP_ARGS);
@@ -552,6 +556,9 @@ __device__ int find_threshold_bin(SelectShared& sh, int nbins, int need, int* ab
 // The token bitmap of the selection lives in LDS when it fits (kLdsBitmap; it follows the
 // candidates in the dynamic LDS), else in the workspace.
 constexpr int kLdsBitmapMaxWords = 8192;
+// Candidate-list entries the select stashes on chip: 12 K beside the LDS bitmap (a list of a
+// guess at the 8 K-th largest score plus its bin's other entries, typically), 15 K without.
+constexpr int stash_cap(bool lds_bitmap) { return lds_bitmap ? 12288 : 15360; }
 
 // What a select launch serves.  kSelList: every query, from the sweep's candidate list; a query
 // the list cannot serve (no guess, an overflowed segment, fewer than K listed, or a threshold
@@ -571,8 +578,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     int32_t* __restrict__ err) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ SelectShared sh;
-  __shared__ uint32_t lseg[kHistBins];  // list mode: the candidates each segment holds
-  uint64_t* cand = reinterpret_cast<uint64_t*>(dyn);  // (key << 32) | ~token
+  __shared__ uint16_t lseg[kHistBins];  // list mode: the candidates each segment holds
+  constexpr int kStashCap = stash_cap(kLdsBitmap);
+  // Dynamic LDS: the candidates of the threshold bin, (key << 32) | ~token, in a region that
+  // first stashes the whole candidate list (list mode), then the LDS bitmap if there is one.
+  uint64_t* cand = reinterpret_cast<uint64_t*>(dyn);
+  uint64_t* stash = cand;
+  const int region = max(cand_cap, kStashCap);
 
   const int bj = blockIdx.x;
   const int b = bj / S, j = bj % S;
@@ -613,7 +625,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   const int n2 = min(8 * K, n_slots / 4);
   // bm_words covers whole 1,024-token chunks, so the last chunk's ballot words stay inside
   uint32_t* bm;
-  if constexpr (kLdsBitmap) bm = reinterpret_cast<uint32_t*>(dyn + (size_t)cand_cap * sizeof(uint64_t));
+  if constexpr (kLdsBitmap) bm = reinterpret_cast<uint32_t*>(dyn + (size_t)region * sizeof(uint64_t));
   else bm = bitmap + (int64_t)bj * bm_words;
   const int n_chunks = (Lj + kSelThreads - 1) / kSelThreads;
   int beta, above, gbin, cnt_beta;
@@ -634,11 +646,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     if (usable)
       for (int i = tid; i < n_seg; i += kSelThreads) {
         const uint32_t c = cnt_p[i];
-        lseg[i] = c;
+        lseg[i] = (uint16_t)min(c, (uint32_t)kSegCap);
         over |= c > (uint32_t)kSegCap ? 1 : 0;
         my_total += (int)min(c, (uint32_t)kSegCap);
       }
     for (int i = tid; i < kHistBins; i += kSelThreads) sh.hist[i] = 0;
+    if (tid == 0) sh.misc[6] = 0;
     int total;
     block_exclusive_scan<kSelThreads>(my_total, sh.scan, &total);
     if (__syncthreads_or(over) || !usable || total < K) {
@@ -668,14 +681,20 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
       const auto w = __builtin_amdgcn_raw_buffer_load_b64(lrs, off, 0, 0);
       return ((uint64_t)(uint32_t)w[1] << 32) | (uint32_t)w[0];
     };
+    // take(entry, slot): every listed entry once, with a distinct slot in [0, total) (each
+    // wave reserves its round's slots with one LDS atomic)
     auto for_each_listed = [&](auto&& take) {
       for (int s0 = wave; s0 < n_seg; s0 += kSegsAtOnce * n_waves) {
         uint64_t v[kSegsAtOnce][kFirstRows];
         int c[kSegsAtOnce];  // the segment's count: the same in every lane
+        int pre[kSegsAtOnce];
+        int round_n = 0;
 #pragma unroll
         for (int a = 0; a < kSegsAtOnce; ++a) {
           const int sg = s0 + a * n_waves;
           c[a] = __builtin_amdgcn_readfirstlane(sg < n_seg ? (int)lseg[sg] : 0);
+          pre[a] = round_n;
+          round_n += c[a];
 #pragma unroll
           for (int r = 0; r < kFirstRows; ++r) {
             // the first row is loaded unconditionally (a branch would make the compiler wait
@@ -684,13 +703,16 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
             if (r == 0 || c[a] > 64 * r) v[a][r] = load_entry(sg, lane + 64 * r, c[a]);
           }
         }
+        int base = 0;
+        if (lane == 0 && round_n > 0) base = atomicAdd(&sh.misc[6], round_n);
+        base = __builtin_amdgcn_readfirstlane(base);
 #pragma unroll
         for (int a = 0; a < kSegsAtOnce; ++a)
 #pragma unroll
           for (int r = 0; r < kFirstRows; ++r) {
             if (c[a] <= 64 * r) continue;
             asm volatile("" : "+v"(v[a][r]));  // every load above is issued before the first wait
-            if (lane + 64 * r < c[a]) take(v[a][r]);
+            if (lane + 64 * r < c[a]) take(v[a][r], base + pre[a] + lane + 64 * r);
           }
         for (int a = 0; a < kSegsAtOnce; ++a) {
           if (c[a] <= 64 * kFirstRows) continue;
@@ -698,13 +720,18 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
           for (int r = kFirstRows; r < kRows; ++r) {
             if (c[a] <= 64 * r) break;
             const uint64_t w = load_entry(sg, lane + 64 * r, c[a]);
-            if (lane + 64 * r < c[a]) take(w);
+            if (lane + 64 * r < c[a]) take(w, base + pre[a] + lane + 64 * r);
           }
         }
       }
     };
-    // the listed keys' first-digit histogram
-    for_each_listed([&](uint64_t v) { atomicAdd(&sh.hist[(uint32_t)(v >> 32) >> kHistShift], 1u); });
+    // The listed keys' first-digit histogram; the entries are stashed on chip when they fit,
+    // for the second pass below.
+    const bool stashed = total <= kStashCap;
+    for_each_listed([&](uint64_t v, int slot) {
+      atomicAdd(&sh.hist[(uint32_t)(v >> 32) >> kHistShift], 1u);
+      if (stashed) stash[slot] = v;
+    });
     __syncthreads();
     find_threshold_bins2(sh, kHistBins, K, n2 > K ? n2 : 8 * K, &beta, &above, &gbin);
     cnt_beta = beta >= 0 ? (int)sh.hist[beta] : 0;
@@ -737,11 +764,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
       atomicAdd(&path_count[0], 1ull);
     }
     // the tokens above bin beta into the bitmap, bin beta on chip
-    const int n_words = (Lj + 31) / 32;
-    for (int i = tid; i < n_words; i += kSelThreads) bm[i] = 0u;
-    if (tid == 0) sh.misc[2] = 0;
-    __syncthreads();  // (also orders the zeroing before the bits)
-    for_each_listed([&](uint64_t v) {
+    auto classify = [&](uint64_t v) {
       const uint32_t key = (uint32_t)(v >> 32), t = ~(uint32_t)v;
       const int bin = (int)(key >> kHistShift);
       if (bin > beta) {
@@ -750,7 +773,30 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
         const int pos = atomicAdd(&sh.misc[2], 1);
         if (pos < cand_cap) cand[pos] = v;
       }
-    });
+    };
+    const int n_words = (Lj + 31) / 32;
+    if (stashed) {
+      // every stashed entry goes to registers before the candidates, which share its memory,
+      // are written
+      constexpr int kPer = kStashCap / kSelThreads;
+      uint64_t e[kPer];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * kSelThreads;
+        e[k] = i < total ? stash[i] : 0;
+      }
+      for (int i = tid; i < n_words; i += kSelThreads) bm[i] = 0u;
+      if (tid == 0) sh.misc[2] = 0;
+      __syncthreads();  // (also orders the zeroing before the bits)
+#pragma unroll
+      for (int k = 0; k < kPer; ++k)
+        if (tid + k * kSelThreads < total) classify(e[k]);
+    } else {
+      for (int i = tid; i < n_words; i += kSelThreads) bm[i] = 0u;
+      if (tid == 0) sh.misc[2] = 0;
+      __syncthreads();  // (also orders the zeroing before the bits)
+      for_each_listed([&](uint64_t v, int) { classify(v); });
+    }
   } else {
     // ---- from the scores: their first-digit histogram, counted on chip.  8 chunks per round,
     // loaded together; the next round's loads are issued before this round is counted.
@@ -1121,7 +1167,9 @@ hipError_t launch_sweep_for(const hs_ctx* ctx, const IndexCall& a, bool list, hi
 hipError_t launch_select(const hs_ctx* ctx, const IndexCall& a, int mode, hipStream_t stream) {
   const int cap = hs_select_cand_cap(ctx->cfg);
   const bool lds_bitmap = ctx->lay.bm_words <= kLdsBitmapMaxWords;
-  const size_t dyn = (size_t)cap * sizeof(uint64_t) + (lds_bitmap ? (size_t)ctx->lay.bm_words * 4 : 0);
+  const int stash = stash_cap(lds_bitmap);
+  const size_t dyn = (size_t)(cap > stash ? cap : stash) * sizeof(uint64_t) +
+                     (lds_bitmap ? (size_t)ctx->lay.bm_words * 4 : 0);
   const dim3 grid((unsigned)(a.B * a.S));
   const int id = mode == kSelRescored ? HS_KERNEL_TOPK_RESCORED : HS_KERNEL_TOPK_SELECT;
   const auto kernel = lds_bitmap ? topk_select_kernel<true> : topk_select_kernel<false>;
@@ -1171,16 +1219,21 @@ __global__ void prefill_setup_kernel(int32_t* __restrict__ lens, uint32_t* __res
 
 using namespace hs;
 
-// Dynamic-LDS limit of the select: the largest candidate list plus the largest LDS bitmap.  The
-// attribute is process-wide, so it is always set to this one maximum, whatever the context's
+// Dynamic-LDS limit of the select: the candidate region (which first stashes the candidate
+// list) plus, for the instance that has one, the largest LDS bitmap.  The attribute is
+// process-wide, so it is always set to this one maximum, whatever the context's
 // own cap: a context created later never lowers it under a live one.
 hipError_t hs_select_set_attributes() {
-  const int lds = kDefaultCandCap * (int)sizeof(uint64_t) + kLdsBitmapMaxWords * 4;
+  auto region = [](bool lds_bitmap) {
+    return kDefaultCandCap > stash_cap(lds_bitmap) ? kDefaultCandCap : stash_cap(lds_bitmap);
+  };
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_select_kernel<true>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     region(true) * (int)sizeof(uint64_t) + kLdsBitmapMaxWords * 4);
   if (e == hipSuccess)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_select_kernel<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            region(false) * (int)sizeof(uint64_t));
   return e;
 }
 
