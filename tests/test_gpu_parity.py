@@ -160,6 +160,42 @@ def test_select_falls_back_when_the_guess_misses():
     gw.close()
 
 
+def test_select_rescores_only_the_queries_whose_list_misses():
+    # At step 2 only request 1's head weights drop by x0.25, so only its two queries' lists
+    # fall short of K: they are flagged, rescored (the rescoring sweep skips the other
+    # requests) and selected from their scores, while the other requests' queries are served
+    # by their lists in the same call.  Every call's top-K is checked against the oracle.
+    wl = synth.toy(seed=11, batch=3, queries=2, ctx=(9000, 12000, 7000), topk=256, steps=4)
+    gw = GpuWorkload(wl)
+    base = gw.w_np.copy()
+    paths = []
+    for step in range(4):
+        w = base.copy()
+        if step >= 2:
+            w[1] *= 0.25
+        gw.w_np = w
+        gw.w = torch.from_numpy(w).to(gw.dev)
+        qidx, _, ctx_lens = gw.inputs(step)
+        print(f"[partial rescore] step {step}", flush=True)
+        tk = gw.gpu_topk(qidx, ctx_lens).cpu().numpy()
+        for b in range(wl.batch):
+            _, sc = gw.oracle_topk(b, qidx, int(ctx_lens[b]))
+            for j in range(wl.queries):
+                check_topk(tk[b, j], sc[j], wl.topk)
+        paths.append(gw.ctx.select_paths())
+    per_call = wl.batch * wl.queries
+    from_list = [paths[i][0] - (paths[i - 1][0] if i else 0) for i in range(4)]
+    from_scores = [paths[i][1] - (paths[i - 1][1] if i else 0) for i in range(4)]
+    print(f"per call: from the list {from_list}, from the scores {from_scores}")
+    assert all(from_list[i] + from_scores[i] == per_call for i in range(4))
+    assert from_scores[0] == per_call  # no guesses yet
+    # request 1's two queries from their scores, the other requests' from their lists
+    assert from_scores[2] >= 2 and from_list[2] >= per_call - 3
+    assert from_list[3] >= per_call - 1  # request 1 has a guess again
+    assert gw.ctx.device_error() == 0
+    gw.close()
+
+
 def test_config1_bf16_8k():
     wl = synth.config(1)
     gw = GpuWorkload(wl)
