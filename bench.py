@@ -345,7 +345,7 @@ def bench_prefill(torch, dev, P: int) -> dict:
     wl = synth.toy(seed=synth.SEED_BASE + 6, batch=1, queries=4, ctx=(P,), topk=K, steps=1,
                    residency=[(synth.RES_FULL, 1.0)])
     lay = synth.make_layout(wl)
-    max_batch = 64                               # chunks of 64 x 4 prompt tokens
+    max_batch = 256                              # chunks of 256 x 4 prompt tokens
     pad = ((0, max_batch - 1), (0, 0))
     cfg = hsb.make_config(topk=K, n_layers=1, max_batch=max_batch, max_queries=4,
                           max_pages_per_req=wl.max_pages, num_gpu_blocks=lay.num_gpu_blocks,
@@ -409,7 +409,7 @@ def bench_prefill(torch, dev, P: int) -> dict:
                           "frac": round(att_flops / (ms_att * 1e-3) / (BF16_DENSE_TFLOPS * 1e12), 4)},
             "kernels_us_total_launches": kt,
             "note": "indexer + top-K of every prompt token, then one layer of sparse MLA on the "
-                    "decode kernel; run as groups of 4 tokens, 256 tokens per chunk"}
+                    "decode kernel; run as groups of 4 tokens, 1,024 tokens per chunk"}
 
 
 def measure_stream_read(torch, dev) -> float:
