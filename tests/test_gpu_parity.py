@@ -88,6 +88,25 @@ def test_toy_indexshare_four_layers_mixed_residency():
     gw.close()
 
 
+@pytest.mark.parametrize("idx_dtype", [1, 0], ids=["fp8_keys", "bf16_keys"])
+def test_three_queries_lists_and_rescoring(idx_dtype):
+    # S = 3: one pair of queries and a lone third share each tile (a score store and a list
+    # store per pair and per lone query), with FP8 key tiles through the LDS ring or bf16 keys
+    # in registers.  Step 0 selects from the scores, later steps from the candidate lists; the
+    # 2,000-token request leaves no margin for a guess and is selected from its scores in every
+    # step.
+    wl = synth.toy(seed=12, batch=3, queries=3, ctx=(5000, 2000, 9000), topk=256, steps=4,
+                   idx_dtype=idx_dtype)
+    gw = GpuWorkload(wl)
+    run_isolated(gw, 4)
+    from_list, from_scores = gw.ctx.select_paths()
+    print(f"selections from the candidate list {from_list}, from all scores {from_scores}")
+    assert from_list + from_scores == 4 * wl.batch * wl.queries
+    assert from_scores >= 4 * wl.queries  # request 1 in every call, and the first call
+    assert from_list >= 2 * 2 * wl.queries  # requests 0 and 2 from the second call on
+    gw.close()
+
+
 def test_topk2048_ragged_and_short_contexts():
     # several 64-row tiles, a ragged tail, and one context shorter than K (selects everything)
     wl = synth.toy(seed=5, batch=3, queries=1, ctx=(10000, 1500, 6100), topk=2048, steps=2)
