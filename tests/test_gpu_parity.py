@@ -88,14 +88,15 @@ def test_toy_indexshare_four_layers_mixed_residency():
     gw.close()
 
 
-@pytest.mark.parametrize("idx_dtype", [1, 0], ids=["fp8_keys", "bf16_keys"])
-def test_three_queries_lists_and_rescoring(idx_dtype):
+@pytest.mark.parametrize("queries,idx_dtype", [(3, 1), (3, 0), (4, 0)],
+                         ids=["s3_fp8_keys", "s3_bf16_keys", "s4_bf16_keys"])
+def test_lists_and_scores_in_one_call(queries, idx_dtype):
     # S = 3: one pair of queries and a lone third share each tile (a score store and a list
-    # store per pair and per lone query), with FP8 key tiles through the LDS ring or bf16 keys
-    # in registers.  Step 0 selects from the scores, later steps from the candidate lists; the
-    # 2,000-token request leaves no margin for a guess and is selected from its scores in every
-    # step.
-    wl = synth.toy(seed=12, batch=3, queries=3, ctx=(5000, 2000, 9000), topk=256, steps=4,
+    # store per pair and per lone query); FP8 key tiles go through the LDS ring, bf16 keys
+    # through registers.  Step 0 selects from the scores, later steps from the candidate lists;
+    # the 2,000-token request leaves no margin for a guess and is selected from its scores in
+    # every step.
+    wl = synth.toy(seed=12, batch=3, queries=queries, ctx=(5000, 2000, 9000), topk=256, steps=4,
                    idx_dtype=idx_dtype)
     gw = GpuWorkload(wl)
     run_isolated(gw, 4)
