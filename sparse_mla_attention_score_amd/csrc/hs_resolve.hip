@@ -143,7 +143,9 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
   if (tid < 8) cnt[tid] = 0;
   for (int i = tid; i < H; i += kResThreads) flag[i] = 0;
   int nU;
-  auto read_out = [&](auto word_at) {
+  // wpre (when given): each word's first place in U, so that a token's place is its word's
+  // plus the set bits below it in the word
+  auto read_out = [&](auto word_at, int32_t* wpre) {
     const int per = (n_words + kResThreads - 1) / kResThreads;
     const int w0 = min(n_words, tid * per), w1 = min(n_words, w0 + per);
     int c = 0;
@@ -152,6 +154,7 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     int pos = block_exclusive_scan<kResThreads>(c, scan, &tot);
     for (int wd = w0; wd < w1; ++wd) {
       uint32_t v = word_at(wd);
+      if (wpre) wpre[wd] = pos;
       while (v) {
         const int bit = __ffs(v) - 1;
         v &= v - 1;
@@ -172,6 +175,10 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
   // the end (as the top-K call emits it), the list is already the sorted union, and the bitmap
   // is skipped.  Any other list takes the bitmap below.
   bool direct = false;
+  // upos: the place in U of each of the thread's list entries, when it is known before step 5
+  // (else step 5 finds it by binary search)
+  int32_t upos[kPerU];
+  bool have_pos = false;
   if (S == 1) {
 #pragma unroll
     for (int e = 0; e < kPerU; ++e) {
@@ -201,21 +208,35 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
     }
   }
   if (direct) {
-    // U holds the list
+    // U holds the list: entry i is at place i
+#pragma unroll
+    for (int e = 0; e < kPerU; ++e) upos[e] = tid + e * kResThreads;
+    have_pos = true;
   } else if (n_words <= 2 * union_cap) {
     uint32_t* lb = reinterpret_cast<uint32_t*>(msrc);
     for (int i = tid; i < n_words; i += kResThreads) lb[i] = 0u;
     __syncthreads();
     mark(lb);
     __syncthreads();
-    read_out([&](int wd) { return lb[wd]; });
+    // with the bitmap in msrc alone, the words' first places fit in cls (free until step 2)
+    int32_t* wpre = n_words <= union_cap ? cls : nullptr;
+    read_out([&](int wd) { return lb[wd]; }, wpre);
+    if (wpre) {
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < kPerU; ++e) {
+        const int32_t t = tkv[e];
+        upos[e] = t >= 0 && t < Lb ? wpre[t >> 5] + __popc(lb[t >> 5] & ((1u << (t & 31)) - 1u)) : 0;
+      }
+      have_pos = true;
+    }
   } else {
     uint32_t* ub = ubits + (int64_t)b * ubits_stride;
     for (int i = tid; i < n_words; i += kResThreads) ub[i] = 0u;
     __syncthreads();  // the zeroing stores have completed before any bit is set
     mark(ub);
     __syncthreads();  // the atomics were performed in L2; the words are read back at agent scope
-    read_out([&](int wd) { return load_agent(&ub[wd]); });
+    read_out([&](int wd) { return load_agent(&ub[wd]); }, nullptr);
   }
   __syncthreads();
 
@@ -355,16 +376,16 @@ __global__ __launch_bounds__(kResThreads) void resolve_kernel(
   if (tid == 0) miss_cnt[b] = n_assign;
   __syncthreads();
 
-  // ---- 5. row ids, positionally: each entry's place in U by binary search (the thread's
-  // searches advance together, one LDS round trip per halving step)
+  // ---- 5. row ids, positionally: each entry's place in U, known from step 1 or found by
+  // binary search (the thread's searches advance together, one LDS round trip per halving step)
   {
     int lo[kPerU], hi[kPerU];
 #pragma unroll
     for (int e = 0; e < kPerU; ++e) {
-      lo[e] = 0;
-      hi[e] = tkv[e] >= 0 && tkv[e] < Lb ? nU : 0;
+      lo[e] = have_pos ? upos[e] : 0;
+      hi[e] = have_pos ? upos[e] : tkv[e] >= 0 && tkv[e] < Lb ? nU : 0;
     }
-    for (int it = 0; (1 << it) <= nU; ++it) {
+    for (int it = 0; !have_pos && (1 << it) <= nU; ++it) {
 #pragma unroll
       for (int e = 0; e < kPerU; ++e) {
         if (lo[e] < hi[e]) {
