@@ -216,6 +216,53 @@ def test_select_rescores_only_the_queries_whose_list_misses():
     gw.close()
 
 
+@pytest.mark.parametrize("queries,ctx", [(4, (300000, 600000)), (2, (200000, 300000))],
+                         ids=["s4_300k_600k", "s2_200k_300k"])
+def test_resolver_union_paths_long_contexts(queries, ctx):
+    # The resolver builds a request's union of its S lists through a token bitmap: with the
+    # bitmap in one LDS array (contexts up to 32 tokens per union slot) each entry's place in the
+    # union is read off the bitmap; with a longer context the bitmap spans two LDS arrays (up to
+    # 64 tokens per slot), and beyond that it lives in workspace memory, and the places are found
+    # by binary search.  K = 2,048 gives 8,192 slots at S = 4 and 4,096 at S = 2, so each
+    # request here takes one of the two longer paths.  The lists are synthetic: each step draws
+    # 2,600 tokens per request, keeping 80 % of the last step's, and each query takes 2,048 of
+    # them, so the queries share most tokens and the hot buffer sees hits, misses and evictions.
+    S, K = queries, 2048
+    wl = synth.toy(seed=13, batch=2, queries=S, ctx=ctx, topk=K, steps=3)
+    gw = GpuWorkload(wl)
+    rng = np.random.default_rng(1300 + S)
+    base = [None] * wl.batch
+    for step in range(3):
+        _, _, ctx_lens = gw.inputs(step)
+        tk = np.empty((wl.batch, S, K), np.int32)
+        for b in range(wl.batch):
+            span = int(ctx_lens[b]) - S + 1  # every query sees these tokens
+            if base[b] is None:
+                base[b] = rng.choice(span, 2600, replace=False)
+            else:
+                keep = rng.choice(base[b], 2080, replace=False)
+                fresh = np.setdiff1d(rng.choice(span, 1200, replace=False), keep)[:520]
+                base[b] = np.concatenate([keep, fresh])
+            for j in range(S):
+                tk[b, j] = np.sort(rng.choice(base[b], K, replace=False))
+        print(f"[resolver paths S={S}] step {step} contexts {ctx_lens.tolist()}", flush=True)
+        rows_dev, stats_dev = gw.gpu_resolve(torch.from_numpy(tk).to(gw.dev), ctx_lens)
+        rows, stats = rows_dev.cpu().numpy(), stats_dev.cpu().numpy()
+        for b in range(wl.batch):
+            rows_ref, _, st_ref = gw.oracle_resolve(b, tk[b])
+            assert np.array_equal(rows[b], rows_ref), f"row ids differ, request {b} step {step}"
+            assert tuple(int(x) for x in stats[b]) == st_ref, f"stats {stats[b]} vs {st_ref}"
+            check_content(gw, b, rows[b].ravel(), tk[b].ravel())
+        st_tok, st_stamp, t2s, _ = gw.ctx.hot_state()
+        for b in range(wl.batch):
+            o = gw.states[b]
+            assert np.array_equal(st_tok[b], o.slot_token), f"slot_token request {b}"
+            assert np.array_equal(st_stamp[b], o.slot_stamp), f"slot_stamp request {b}"
+            assert np.array_equal(t2s[b], o.tok2slot), f"tok2slot request {b}"
+        assert gw.ctx.device_error() == 0
+    gw.close()
+
+
 def test_config1_bf16_8k():
     wl = synth.config(1)
     gw = GpuWorkload(wl)
